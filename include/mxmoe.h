@@ -1,0 +1,204 @@
+/*
+ * mxmoe.h — C ABI of the MXFP4 mixture-of-experts layer for AMD MI355X (gfx950).
+ *
+ * The layer is the GPT-OSS expert block whose weights are stored in OCP
+ * MXFP4: e2m1 values packed two per uint8 with one e8m0 power-of-two scale
+ * per 32-value block (KerasFormers "mxfp4" page, intro and "Primitives").
+ * gate_up_proj is laid out (E, 2I, H) and down_proj (E, H, I), each as
+ * uint8 blocks (rows, K/32, 16) plus uint8 scales (rows, K/32), with
+ * full-precision biases (same page, "As GPT-OSS's native format").  Rows 2i
+ * and 2i+1 of gate_up are gate_i and up_i (interleaved).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, row-major and densely packed in the shapes stated.  The
+ *     library keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; no call synchronises the host.
+ *   - All arguments are validated on the host before anything is launched.
+ *     On any error the call returns a non-zero status, launches nothing and
+ *     leaves every output untouched.  MXMOE_ERR_HIP means a HIP call failed
+ *     after validation; the outputs are then undefined.
+ *   - The library allocates no device memory: scratch space comes from the
+ *     caller's workspace, sized by the matching *_workspace_bytes call.
+ *   - Calls on distinct streams with distinct outputs and workspaces may run
+ *     concurrently; two calls sharing a workspace must be ordered.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXMOE_OK = 0,
+  MXMOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MXMOE_ERR_ALIGN = 2,       /* a pointer is not 16-byte aligned */
+  MXMOE_ERR_SHAPE = 3,       /* a size is out of range, including a contracting dim % 32 != 0 */
+  MXMOE_ERR_DTYPE = 4,       /* unknown dtype code, or a combination not offered */
+  MXMOE_ERR_WORKSPACE = 5,   /* workspace smaller than the *_workspace_bytes figure */
+  MXMOE_ERR_UNSUPPORTED = 6, /* a valid request outside what this library implements */
+  MXMOE_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
+  MXMOE_ERR_VALUE = 8        /* a non-size argument is out of range (e.g. an FP8 scale <= 0) */
+} mxmoe_status_t;
+
+typedef enum {
+  MXMOE_F32 = 0,  /* IEEE binary32 */
+  MXMOE_BF16 = 1  /* bfloat16 (raw 16-bit patterns) */
+} mxmoe_dtype_t;
+
+/* Limits of the layer entry points. */
+#define MXMOE_MAX_EXPERTS 256
+#define MXMOE_MAX_TOPK 8
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* mxmoe_status_string(int32_t status);
+
+/* Interface version, bumped on any ABI change (currently 1). */
+int32_t mxmoe_version(void);
+
+/*
+ * mxfp4_unpack — dequantise MXFP4 to float ("Primitives": each nibble goes
+ * through the FP4 codebook {0, 0.5, 1, 1.5, 2, 3, 4, 6} with bit 3 the sign,
+ * times 2^(e8m0 - 127)).
+ *
+ *   blocks : (rows, k/32, 16) uint8.  Element 32*b + 2*j + n of a row is
+ *            nibble n of byte j of block b, n = 0 being the low nibble.
+ *   scales : (rows, k/32) uint8 e8m0.  Byte 255 decodes to NaN.
+ *   out    : (rows, k) in out_dtype (MXMOE_BF16 or MXMOE_F32).
+ *
+ * The result is exact: every code times a power of two is representable,
+ * except that results beyond the format's range become +-Inf and results
+ * below it are kept as subnormals; nibble 8 gives -0.0.
+ * Errors: k <= 0 or k % 32 != 0, rows < 0 -> MXMOE_ERR_SHAPE (the
+ * "As a quantize_model scheme" section: a clear error when the contracting
+ * dimension is not a multiple of 32).  rows == 0 is a no-op.
+ */
+mxmoe_status_t mxfp4_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t rows, int64_t k,
+                            void* out, int32_t out_dtype, void* stream);
+
+/*
+ * mxfp4_pack — quantise real values to MXFP4 ("Primitives": the e8m0 block
+ * scale is floor(log2(amax)) - 2 and each value is rounded to the nearest
+ * FP4 grid point).
+ *
+ *   w      : (rows, k) in w_dtype (MXMOE_BF16 or MXMOE_F32).
+ *   blocks : (rows, k/32, 16) uint8 output; scales : (rows, k/32) output.
+ *
+ * Per 32-value block: e = floor(log2(amax)) - 2 from the exact binary
+ * exponent, clamped to [-127, 127] (an all-zero block gets e = -127); the
+ * scale byte is e + 127; w / 2^e is rounded to the nearest FP4 magnitude
+ * with ties to the even code, saturating at 6, and keeps the sign bit of w
+ * (-0.0 and negatives that round to zero give nibble 8).  NaN or Inf inputs
+ * give unspecified bytes.  Errors as for mxfp4_unpack.
+ */
+mxmoe_status_t mxfp4_pack(const void* w, int32_t w_dtype, int64_t rows, int64_t k,
+                          uint8_t* blocks, uint8_t* scales, void* stream);
+
+/* One MoE layer's parameters, all device pointers (see the file header). */
+typedef struct {
+  int32_t E;            /* experts, 1..MXMOE_MAX_EXPERTS */
+  int32_t H;            /* hidden size, multiple of 32 */
+  int32_t I;            /* intermediate size, multiple of 32 */
+  int32_t top_k;        /* experts per token, 1..min(E, MXMOE_MAX_TOPK) */
+  int32_t param_dtype;  /* dtype of biases and router: MXMOE_BF16 or MXMOE_F32 */
+  int32_t reserved0;
+  const uint8_t* gate_up_blocks; /* (E, 2I, H/32, 16) */
+  const uint8_t* gate_up_scales; /* (E, 2I, H/32) */
+  const void* gate_up_bias;      /* (E, 2I) param_dtype; added before the SwiGLU */
+  const uint8_t* down_blocks;    /* (E, H, I/32, 16) */
+  const uint8_t* down_scales;    /* (E, H, I/32) */
+  const void* down_bias;         /* (E, H) param_dtype; part of each expert's output */
+  const void* router_w;          /* (E, H) param_dtype, never quantised */
+  const void* router_b;          /* (E,)   param_dtype */
+} mxmoe_layer_t;
+
+/* Per-call options of the forward. */
+typedef struct {
+  int32_t act_dtype;  /* dtype of x and out: MXMOE_BF16 or MXMOE_F32 */
+  int32_t fp8_act;    /* 1: W-MXFP4 A-FP8 mode (needs act_dtype MXMOE_BF16) */
+  float x_scale;      /* FP8 mode: static per-tensor scale of x (> 0, finite) */
+  float h_scale;      /* FP8 mode: static per-tensor scale of the SwiGLU output */
+  int32_t* topk_idx_out; /* optional device (T, top_k) int32: chosen experts */
+  float* topk_w_out;     /* optional device (T, top_k) fp32: their weights */
+} mxmoe_fwd_opts_t;
+
+/*
+ * Workspace size in bytes for moe_mxfp4_forward with these arguments
+ * (0 if the arguments are invalid).
+ */
+size_t moe_mxfp4_workspace_bytes(const mxmoe_layer_t* layer, int64_t T, const mxmoe_fwd_opts_t* opts);
+
+/*
+ * moe_mxfp4_forward — the routed MoE layer (upstream GptOssExperts forward,
+ * gpt-oss-15.5b-23E-nf4-GPU page, "Notes"; only the top-k experts of each
+ * token are evaluated, KerasFormers "mxfp4" page, "As GPT-OSS's native
+ * format").
+ *
+ *   x   : (T, H) act_dtype.   out : (T, H) act_dtype.   T >= 0 (0 = no-op).
+ *
+ * Per token t: logits = W_r x_t + b_r with fp32 accumulation from the
+ * unquantised x; the top_k largest logits (ties to the lower expert id),
+ * ordered by logit; w = softmax over those top_k logits in fp32.  For each
+ * chosen expert e: G = W_gu[e] x + b_gu[e] (fp32 accumulation over decoded
+ * MXFP4 weights), gate = min(G[2i], 7), up = clamp(G[2i+1], -7, 7),
+ * h_i = (up + 1) * gate * sigmoid(1.702 * gate), rounded to act_dtype (or
+ * quantised to FP8 with h_scale), Y = W_d[e] h + b_d[e]; then
+ * out_t = sum_j w_j * Y_j summed in the order j = 0..top_k-1.
+ *
+ * FP8 mode (fp8_act = 1): x and h are quantised to float8_e4m3fn as
+ * code = sat448(rne(fp32(v) * (1 / scale))), 1/scale computed once in fp32,
+ * and both GEMMs run on scaled MXFP4 x FP8 matrix instructions with fp32
+ * accumulation; the router still reads the unquantised x.
+ *
+ * The result is deterministic: identical inputs give identical bits.
+ */
+mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* layer, const void* x, int64_t T, void* out,
+                                 const mxmoe_fwd_opts_t* opts, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * moe_mxfp4_route — only the routing steps of the forward: router logits,
+ * top-k, softmax over the k, and the grouping of the T*top_k (token, slot)
+ * pairs by expert.
+ *
+ *   idx_out     : (T, top_k) int32       w_out      : (T, top_k) fp32
+ *   counts_out  : (E,) int32 tokens per expert
+ *   offsets_out : (E+1,) int32 exclusive prefix sum of counts
+ *   sorted_out  : (T*top_k,) int32 flat slot ids t*top_k + j grouped by
+ *                 expert, ascending slot id within an expert
+ *   pos_out     : (T*top_k,) int32 row of each flat slot in sorted_out
+ * Any of the five outputs may be NULL.  opts->act_dtype gives x's dtype;
+ * the FP8 fields are ignored.  Workspace as for moe_mxfp4_forward.
+ */
+mxmoe_status_t moe_mxfp4_route(const mxmoe_layer_t* layer, const void* x, int64_t T,
+                               const mxmoe_fwd_opts_t* opts, int32_t* idx_out, float* w_out,
+                               int32_t* counts_out, int32_t* offsets_out, int32_t* sorted_out,
+                               int32_t* pos_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_mxfp4_calibrate_fp8 — static per-tensor FP8 scales from a calibration
+ * batch (min/max observer, symmetric: the FP8 script comment on the
+ * gpt-oss-120b-mxfp4-fp8attn-v2 page; per-tensor activation scheme on the
+ * amd/gpt-oss-20b-MoE-Quant-W-MXFP4-A-FP8-KV-FP8 page).
+ *
+ *   x_calib    : (T, H) bf16 calibration activations, T >= 1.
+ *   scales_out : device float[2] = { amax(x)/448, amax(h)/448 } in fp32,
+ *                h being the bf16-rounded SwiGLU output of every routed
+ *                (token, expert) pair of the batch in the bf16 path.
+ * Workspace: moe_mxfp4_workspace_bytes with act_dtype MXMOE_BF16, fp8_act 0.
+ */
+mxmoe_status_t moe_mxfp4_calibrate_fp8(const mxmoe_layer_t* layer, const void* x_calib, int64_t T,
+                                       float* scales_out, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXMOE_H */

@@ -1,0 +1,19 @@
+"""MXFP4 mixture-of-experts layer for AMD MI355X (gfx950).
+
+The computation lives in libmxmoe.so (hand-written HIP, C ABI in
+include/mxmoe.h); this package only loads it and marshals torch tensors.
+"""
+from .binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    MoEWeights,
+    MxmoeError,
+    alloc_workspace,
+    load_library,
+    moe_mxfp4_calibrate_fp8,
+    moe_mxfp4_forward,
+    moe_mxfp4_route,
+    mxfp4_pack,
+    mxfp4_unpack,
+    workspace_bytes,
+)

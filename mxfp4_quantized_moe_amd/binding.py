@@ -1,0 +1,279 @@
+"""Python binding of libmxmoe.so: argument marshalling only.
+
+Every step of the layer runs in the HIP library; this module turns torch
+tensors into device pointers, sizes and the current HIP stream, calls the
+C ABI declared in include/mxmoe.h and raises on a non-zero status.  There is
+no fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
+
+MXMOE_F32 = 0
+MXMOE_BF16 = 1
+
+STATUS_NAMES = {
+    0: "MXMOE_OK",
+    1: "MXMOE_ERR_NULL",
+    2: "MXMOE_ERR_ALIGN",
+    3: "MXMOE_ERR_SHAPE",
+    4: "MXMOE_ERR_DTYPE",
+    5: "MXMOE_ERR_WORKSPACE",
+    6: "MXMOE_ERR_UNSUPPORTED",
+    7: "MXMOE_ERR_HIP",
+    8: "MXMOE_ERR_VALUE",
+}
+
+EXPORTED = (
+    "mxmoe_status_string",
+    "mxmoe_version",
+    "mxfp4_unpack",
+    "mxfp4_pack",
+    "moe_mxfp4_workspace_bytes",
+    "moe_mxfp4_forward",
+    "moe_mxfp4_route",
+    "moe_mxfp4_calibrate_fp8",
+)
+
+
+class MxmoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [
+        ("E", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("I", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("param_dtype", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("gate_up_blocks", ctypes.c_void_p),
+        ("gate_up_scales", ctypes.c_void_p),
+        ("gate_up_bias", ctypes.c_void_p),
+        ("down_blocks", ctypes.c_void_p),
+        ("down_scales", ctypes.c_void_p),
+        ("down_bias", ctypes.c_void_p),
+        ("router_w", ctypes.c_void_p),
+        ("router_b", ctypes.c_void_p),
+    ]
+
+
+class FwdOpts(ctypes.Structure):
+    _fields_ = [
+        ("act_dtype", ctypes.c_int32),
+        ("fp8_act", ctypes.c_int32),
+        ("x_scale", ctypes.c_float),
+        ("h_scale", ctypes.c_float),
+        ("topk_idx_out", ctypes.c_void_p),
+        ("topk_w_out", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmxmoe.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing: build it with `python -m mxfp4_quantized_moe_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.mxmoe_status_string.restype = ctypes.c_char_p
+    lib.mxmoe_status_string.argtypes = [i32]
+    lib.mxmoe_version.restype = i32
+    lib.mxmoe_version.argtypes = []
+    lib.mxfp4_unpack.restype = i32
+    lib.mxfp4_unpack.argtypes = [vp, vp, i64, i64, vp, i32, vp]
+    lib.mxfp4_pack.restype = i32
+    lib.mxfp4_pack.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    lib.moe_mxfp4_workspace_bytes.restype = sz
+    lib.moe_mxfp4_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i64, ctypes.POINTER(FwdOpts)]
+    lib.moe_mxfp4_forward.restype = i32
+    lib.moe_mxfp4_forward.argtypes = [ctypes.POINTER(Layer), vp, i64, vp, ctypes.POINTER(FwdOpts), vp, sz, vp]
+    lib.moe_mxfp4_route.restype = i32
+    lib.moe_mxfp4_route.argtypes = [ctypes.POINTER(Layer), vp, i64, ctypes.POINTER(FwdOpts),
+                                    vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_mxfp4_calibrate_fp8.restype = i32
+    lib.moe_mxfp4_calibrate_fp8.argtypes = [ctypes.POINTER(Layer), vp, i64, vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().mxmoe_status_string(status).decode()
+        raise MxmoeError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return MXMOE_BF16
+    if dt == torch.float32:
+        return MXMOE_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+# ---------------------------------------------------------------- codec
+
+
+def mxfp4_unpack(blocks: torch.Tensor, scales: torch.Tensor, dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """(..., nb, 16) uint8 blocks + (..., nb) uint8 scales -> (..., nb*32)."""
+    nb = blocks.shape[-2]
+    lead = tuple(blocks.shape[:-2])
+    rows = 1
+    for d in lead:
+        rows *= d
+    if out is None:
+        out = torch.empty(lead + (nb * 32,), dtype=dtype, device=blocks.device)
+    _check(load_library().mxfp4_unpack(_ptr(blocks), _ptr(scales), rows, nb * 32, _ptr(out),
+                                       _dtype_code(out.dtype), _stream(blocks.device)))
+    return out
+
+
+def mxfp4_pack(w: torch.Tensor):
+    """(..., K) bf16/fp32 -> (blocks (..., K/32, 16) uint8, scales (..., K/32) uint8)."""
+    K = w.shape[-1]
+    lead = tuple(w.shape[:-1])
+    rows = 1
+    for d in lead:
+        rows *= d
+    blocks = torch.empty(lead + (max(K // 32, 0), 16), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(lead + (max(K // 32, 0),), dtype=torch.uint8, device=w.device)
+    _check(load_library().mxfp4_pack(_ptr(w), _dtype_code(w.dtype), rows, K, _ptr(blocks), _ptr(scales),
+                                     _stream(w.device)))
+    return blocks, scales
+
+
+# ----------------------------------------------------------------- layer
+
+
+@dataclass
+class MoEWeights:
+    """Device tensors of one MXFP4 MoE layer (see include/mxmoe.h)."""
+
+    gate_up_blocks: torch.Tensor  # (E, 2I, H/32, 16) uint8
+    gate_up_scales: torch.Tensor  # (E, 2I, H/32) uint8
+    gate_up_bias: torch.Tensor  # (E, 2I)
+    down_blocks: torch.Tensor  # (E, H, I/32, 16) uint8
+    down_scales: torch.Tensor  # (E, H, I/32) uint8
+    down_bias: torch.Tensor  # (E, H)
+    router_w: torch.Tensor  # (E, H)
+    router_b: torch.Tensor  # (E,)
+    top_k: int
+
+    @property
+    def E(self) -> int:
+        return int(self.gate_up_blocks.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.router_w.shape[1])
+
+    @property
+    def I(self) -> int:
+        return int(self.down_blocks.shape[2]) * 32
+
+    def descriptor(self) -> Layer:
+        return Layer(
+            E=self.E, H=self.H, I=self.I, top_k=self.top_k, param_dtype=_dtype_code(self.router_w.dtype), reserved0=0,
+            gate_up_blocks=_ptr(self.gate_up_blocks), gate_up_scales=_ptr(self.gate_up_scales),
+            gate_up_bias=_ptr(self.gate_up_bias), down_blocks=_ptr(self.down_blocks),
+            down_scales=_ptr(self.down_scales), down_bias=_ptr(self.down_bias), router_w=_ptr(self.router_w),
+            router_b=_ptr(self.router_b))
+
+
+def _opts(act_dtype: torch.dtype, fp8: bool, x_scale: float, h_scale: float, idx_out=None, w_out=None) -> FwdOpts:
+    return FwdOpts(act_dtype=_dtype_code(act_dtype), fp8_act=1 if fp8 else 0, x_scale=x_scale, h_scale=h_scale,
+                   topk_idx_out=_ptr(idx_out), topk_w_out=_ptr(w_out))
+
+
+def workspace_bytes(layer: MoEWeights, T: int, act_dtype: torch.dtype, fp8: bool = False) -> int:
+    d = layer.descriptor()
+    o = _opts(act_dtype, fp8, 1.0, 1.0)
+    n = load_library().moe_mxfp4_workspace_bytes(ctypes.byref(d), T, ctypes.byref(o))
+    if n == 0 and T > 0:
+        raise MxmoeError(3, "invalid layer or token count")
+    return int(n)
+
+
+def alloc_workspace(layer: MoEWeights, T: int, act_dtype: torch.dtype, fp8: bool = False) -> torch.Tensor:
+    n = workspace_bytes(layer, T, act_dtype, fp8)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=layer.router_w.device)
+
+
+def moe_mxfp4_forward(layer: MoEWeights, x: torch.Tensor, fp8: bool = False, x_scale: float = 1.0,
+                      h_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, topk_idx_out: Optional[torch.Tensor] = None,
+                      topk_w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The routed MXFP4 MoE layer on x (T, H); returns out (T, H)."""
+    T = int(x.shape[0])
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(layer, T, x.dtype, fp8)
+    d = layer.descriptor()
+    o = _opts(x.dtype, fp8, x_scale, h_scale, topk_idx_out, topk_w_out)
+    _check(load_library().moe_mxfp4_forward(ctypes.byref(d), _ptr(x), T, _ptr(out), ctypes.byref(o),
+                                            _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+def moe_mxfp4_route(layer: MoEWeights, x: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Routing only: returns (idx, w, counts, offsets, sorted_slots, slot_pos)."""
+    T = int(x.shape[0])
+    k, E = layer.top_k, layer.E
+    dev = x.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    sorted_slots = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    pos = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(layer, T, x.dtype)
+    d = layer.descriptor()
+    o = _opts(x.dtype, False, 1.0, 1.0)
+    _check(load_library().moe_mxfp4_route(ctypes.byref(d), _ptr(x), T, ctypes.byref(o), _ptr(idx), _ptr(w),
+                                          _ptr(counts), _ptr(offsets), _ptr(sorted_slots), _ptr(pos),
+                                          _ptr(workspace), workspace.numel(), _stream(dev)))
+    return idx, w, counts, offsets, sorted_slots, pos
+
+
+def moe_mxfp4_calibrate_fp8(layer: MoEWeights, x_calib: torch.Tensor,
+                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Static FP8 scales (s_x, s_h) from a bf16 calibration batch, as a device float[2]."""
+    T = int(x_calib.shape[0])
+    scales = torch.empty((4,), dtype=torch.float32, device=x_calib.device)
+    if workspace is None:
+        workspace = alloc_workspace(layer, T, torch.bfloat16)
+    d = layer.descriptor()
+    _check(load_library().moe_mxfp4_calibrate_fp8(ctypes.byref(d), _ptr(x_calib), T, _ptr(scales),
+                                                  _ptr(workspace), workspace.numel(), _stream(x_calib.device)))
+    return scales[:2]

@@ -1,0 +1,321 @@
+// C ABI of the MXFP4 MoE layer: host-side validation, workspace layout and
+// dispatch onto the gfx950 kernels.  Nothing here allocates device memory
+// or synchronises the host; every check runs before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/mxmoe.h"
+#include "launch.h"
+
+namespace {
+
+using namespace mxmoe;
+
+constexpr int64_t kMaxSlots = int64_t(1) << 26;  // T * top_k limit (grid sizes stay in range)
+constexpr int64_t kMaxDim = int64_t(1) << 20;    // H, I, pack/unpack k
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Workspace {
+  size_t idx, wts, counts, offsets, active, tile_off, sorted, pos, calib, xq, h, y, total;
+};
+
+// Byte offsets of the forward's scratch buffers inside the caller's workspace.
+Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8) {
+  Workspace w{};
+  const size_t slots = size_t(T) * size_t(k);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  w.idx = take(slots * 4);
+  w.wts = take(slots * 4);
+  w.counts = take(size_t(E) * 4);
+  w.offsets = take(size_t(E + 1) * 4);
+  w.active = take(size_t(E + 1) * 4);
+  w.tile_off = take(size_t(E + 1) * 4);
+  w.sorted = take(slots * 4);
+  w.pos = take(slots * 4);
+  w.calib = take(16);
+  w.xq = take(fp8 ? size_t(T) * size_t(H) : 0);
+  const size_t hb = fp8 ? 1 : (act_dtype == MXMOE_BF16 ? 2 : 4);
+  w.h = take(slots * size_t(I) * hb);
+  w.y = take(slots * size_t(H) * 4);
+  w.total = o;
+  return w;
+}
+
+mxmoe_status_t check_layer(const mxmoe_layer_t* L) {
+  if (!L) return MXMOE_ERR_NULL;
+  if (L->E < 1 || L->E > MXMOE_MAX_EXPERTS) return MXMOE_ERR_SHAPE;
+  if (L->H <= 0 || L->I <= 0 || L->H > kMaxDim || L->I > kMaxDim) return MXMOE_ERR_SHAPE;
+  if (L->H % 32 != 0 || L->I % 32 != 0) return MXMOE_ERR_SHAPE;
+  if (L->top_k < 1 || L->top_k > MXMOE_MAX_TOPK || L->top_k > L->E) return MXMOE_ERR_SHAPE;
+  if (L->param_dtype != MXMOE_F32 && L->param_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
+  const void* ptrs[] = {L->gate_up_blocks, L->gate_up_scales, L->gate_up_bias, L->down_blocks,
+                        L->down_scales,    L->down_bias,      L->router_w,     L->router_b};
+  for (const void* p : ptrs)
+    if (!p) return MXMOE_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MXMOE_ERR_ALIGN;
+  return MXMOE_OK;
+}
+
+mxmoe_status_t check_opts(const mxmoe_layer_t* L, const mxmoe_fwd_opts_t* o, bool use_fp8) {
+  if (!o) return MXMOE_ERR_NULL;
+  if (o->act_dtype != MXMOE_F32 && o->act_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
+  if (o->act_dtype != L->param_dtype) return MXMOE_ERR_DTYPE;  // one dtype for x, router and biases
+  if (use_fp8) {
+    if (o->fp8_act != 0 && o->fp8_act != 1) return MXMOE_ERR_VALUE;
+    if (o->fp8_act) {
+      if (o->act_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
+      if (!(std::isfinite(o->x_scale) && o->x_scale > 0.f)) return MXMOE_ERR_VALUE;
+      if (!(std::isfinite(o->h_scale) && o->h_scale > 0.f)) return MXMOE_ERR_VALUE;
+      if (!std::isfinite(1.0f / o->x_scale) || !std::isfinite(1.0f / o->h_scale)) return MXMOE_ERR_VALUE;
+    }
+  }
+  if (o->topk_idx_out && !aligned16(o->topk_idx_out)) return MXMOE_ERR_ALIGN;
+  if (o->topk_w_out && !aligned16(o->topk_w_out)) return MXMOE_ERR_ALIGN;
+  return MXMOE_OK;
+}
+
+mxmoe_status_t check_tokens(const mxmoe_layer_t* L, int64_t T) {
+  if (T < 0) return MXMOE_ERR_SHAPE;
+  if (T * int64_t(L->top_k) > kMaxSlots) return MXMOE_ERR_SHAPE;
+  return MXMOE_OK;
+}
+
+mxmoe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MXMOE_OK : MXMOE_ERR_HIP; }
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
+}
+
+// Router + grouping into the workspace; optional copies for the caller.
+hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act_dtype, const Workspace& w,
+                       void* ws, int32_t* idx_out, float* w_out, int32_t* counts_out, int32_t* offsets_out,
+                       int32_t* sorted_buf, int32_t* pos_buf, hipStream_t s) {
+  RouteArgs ra{};
+  ra.x = x;
+  ra.w_r = L->router_w;
+  ra.b_r = L->router_b;
+  ra.act_bf16 = act_dtype == MXMOE_BF16;
+  ra.T = int(T);
+  ra.H = L->H;
+  ra.E = L->E;
+  ra.top_k = L->top_k;
+  ra.idx = at<int32_t>(ws, w.idx);
+  ra.wts = at<float>(ws, w.wts);
+  ra.idx_out = idx_out;
+  ra.wts_out = w_out;
+  hipError_t e = launch_route(ra, s);
+  if (e != hipSuccess) return e;
+  PermuteArgs pa{};
+  pa.idx = ra.idx;
+  pa.n_slots = int(T * L->top_k);
+  pa.E = L->E;
+  pa.counts = at<int32_t>(ws, w.counts);
+  pa.offsets = at<int32_t>(ws, w.offsets);
+  pa.sorted = sorted_buf ? sorted_buf : at<int32_t>(ws, w.sorted);
+  pa.pos = pos_buf ? pos_buf : at<int32_t>(ws, w.pos);
+  pa.active = at<int32_t>(ws, w.active);
+  pa.tile_off = at<int32_t>(ws, w.tile_off);
+  pa.counts_out = counts_out;
+  pa.offsets_out = offsets_out;
+  return launch_permute(pa, s);
+}
+
+GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t T, int act, int phase) {
+  GemmArgs g{};
+  g.act = act;
+  g.phase = phase;
+  g.bias_bf16 = L->param_dtype == MXMOE_BF16;
+  g.top_k = L->top_k;
+  g.E = L->E;
+  g.sorted = at<int32_t>(ws, w.sorted);
+  g.offsets = at<int32_t>(ws, w.offsets);
+  g.active = at<int32_t>(ws, w.active);
+  g.tile_off = at<int32_t>(ws, w.tile_off);
+  const int64_t slots = T * L->top_k;
+  g.n_slots = int(slots);
+  g.max_active = int(slots < L->E ? slots : L->E);
+  g.max_tiles = int((slots + kPrefillTokens - 1) / kPrefillTokens + g.max_active);
+  g.acc_scale = 1.0f;
+  g.out_inv_scale = 1.0f;
+  if (phase == 0) {
+    g.wblk = L->gate_up_blocks;
+    g.wsc = L->gate_up_scales;
+    g.bias = L->gate_up_bias;
+    g.R = 2 * L->I;
+    g.nb = L->H / 32;
+    g.out = at<void>(ws, w.h);
+  } else {
+    g.wblk = L->down_blocks;
+    g.wsc = L->down_scales;
+    g.bias = L->down_bias;
+    g.R = L->H;
+    g.nb = L->I / 32;
+    g.bsrc = at<void>(ws, w.h);
+    g.out = at<void>(ws, w.y);
+  }
+  return g;
+}
+
+// Decode-shaped kernels while experts see few tokens on average; the
+// LDS-staged MFMA tiles beyond that.
+bool use_prefill(const mxmoe_layer_t* L, int64_t T, int act) {
+  if (act == ACT_F32) return false;
+  const int64_t slots = T * L->top_k;
+  const int64_t active = slots < L->E ? slots : L->E;
+  return slots > 16 * active;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxmoe_status_string(int32_t s) {
+  switch (s) {
+    case MXMOE_OK: return "ok";
+    case MXMOE_ERR_NULL: return "a required pointer is NULL";
+    case MXMOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MXMOE_ERR_SHAPE: return "a size is out of range (the contracting dimension must be a multiple of 32)";
+    case MXMOE_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case MXMOE_ERR_WORKSPACE: return "workspace too small";
+    case MXMOE_ERR_UNSUPPORTED: return "request not supported by this library";
+    case MXMOE_ERR_HIP: return "HIP runtime error";
+    case MXMOE_ERR_VALUE: return "an argument value is out of range";
+    default: return "unknown status";
+  }
+}
+
+int32_t mxmoe_version(void) { return 1; }
+
+mxmoe_status_t mxfp4_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t rows, int64_t k, void* out,
+                            int32_t out_dtype, void* stream) {
+  if (rows < 0 || k <= 0 || k % 32 != 0 || k > kMaxDim) return MXMOE_ERR_SHAPE;
+  if (out_dtype != MXMOE_F32 && out_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
+  if (rows == 0) return MXMOE_OK;
+  if (!blocks || !scales || !out) return MXMOE_ERR_NULL;
+  if (!aligned16(blocks) || !aligned16(scales) || !aligned16(out)) return MXMOE_ERR_ALIGN;
+  const int64_t nblocks = rows * (k / 32);
+  if (nblocks / (k / 32) != rows || nblocks > (int64_t(1) << 40)) return MXMOE_ERR_SHAPE;
+  return hip_status(launch_unpack(blocks, scales, nblocks, out, out_dtype == MXMOE_BF16,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+mxmoe_status_t mxfp4_pack(const void* w, int32_t w_dtype, int64_t rows, int64_t k, uint8_t* blocks,
+                          uint8_t* scales, void* stream) {
+  if (rows < 0 || k <= 0 || k % 32 != 0 || k > kMaxDim) return MXMOE_ERR_SHAPE;
+  if (w_dtype != MXMOE_F32 && w_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
+  if (rows == 0) return MXMOE_OK;
+  if (!w || !blocks || !scales) return MXMOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(blocks) || !aligned16(scales)) return MXMOE_ERR_ALIGN;
+  const int64_t nblocks = rows * (k / 32);
+  if (nblocks / (k / 32) != rows || nblocks > (int64_t(1) << 40)) return MXMOE_ERR_SHAPE;
+  return hip_status(launch_pack(w, w_dtype == MXMOE_BF16, nblocks, blocks, scales, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_mxfp4_workspace_bytes(const mxmoe_layer_t* L, int64_t T, const mxmoe_fwd_opts_t* o) {
+  if (check_layer(L) != MXMOE_OK || !o || check_tokens(L, T) != MXMOE_OK) return 0;
+  if (o->act_dtype != MXMOE_F32 && o->act_dtype != MXMOE_BF16) return 0;
+  return layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, o->fp8_act == 1).total;
+}
+
+mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t T, void* out,
+                                 const mxmoe_fwd_opts_t* o, void* ws, size_t ws_bytes, void* stream) {
+  mxmoe_status_t st = check_layer(L);
+  if (st != MXMOE_OK) return st;
+  if ((st = check_opts(L, o, true)) != MXMOE_OK) return st;
+  if ((st = check_tokens(L, T)) != MXMOE_OK) return st;
+  if (T == 0) return MXMOE_OK;
+  if (!x || !out || !ws) return MXMOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return MXMOE_ERR_ALIGN;
+  const bool fp8 = o->fp8_act == 1;
+  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, fp8);
+  if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
+                             nullptr, s);
+  if (e != hipSuccess) return MXMOE_ERR_HIP;
+  const int act = fp8 ? ACT_FP8 : (o->act_dtype == MXMOE_BF16 ? ACT_BF16 : ACT_F32);
+  const float inv_x = fp8 ? 1.0f / o->x_scale : 1.0f;
+  const float inv_h = fp8 ? 1.0f / o->h_scale : 1.0f;
+  if (fp8) {
+    e = launch_quant_fp8(static_cast<const uint16_t*>(x), T * L->H, inv_x, at<uint8_t>(ws, w.xq), s);
+    if (e != hipSuccess) return MXMOE_ERR_HIP;
+  }
+  const bool prefill = use_prefill(L, T, act);
+  GemmArgs g0 = gemm_args(L, w, ws, T, act, 0);
+  g0.bsrc = fp8 ? at<void>(ws, w.xq) : x;
+  if (fp8) {
+    g0.acc_scale = o->x_scale;
+    g0.out_inv_scale = inv_h;
+  }
+  if ((e = launch_moe_gemm(g0, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  GemmArgs g1 = gemm_args(L, w, ws, T, act, 1);
+  if (fp8) g1.acc_scale = o->h_scale;
+  if ((e = launch_moe_gemm(g1, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  CombineArgs ca{};
+  ca.Y = at<float>(ws, w.y);
+  ca.pos = at<int32_t>(ws, w.pos);
+  ca.wts = at<float>(ws, w.wts);
+  ca.out = out;
+  ca.out_bf16 = o->act_dtype == MXMOE_BF16;
+  ca.T = int(T);
+  ca.H = L->H;
+  ca.top_k = L->top_k;
+  return hip_status(launch_combine(ca, s));
+}
+
+mxmoe_status_t moe_mxfp4_route(const mxmoe_layer_t* L, const void* x, int64_t T, const mxmoe_fwd_opts_t* o,
+                               int32_t* idx_out, float* w_out, int32_t* counts_out, int32_t* offsets_out,
+                               int32_t* sorted_out, int32_t* pos_out, void* ws, size_t ws_bytes, void* stream) {
+  mxmoe_status_t st = check_layer(L);
+  if (st != MXMOE_OK) return st;
+  if ((st = check_opts(L, o, false)) != MXMOE_OK) return st;
+  if ((st = check_tokens(L, T)) != MXMOE_OK) return st;
+  if (T == 0) return MXMOE_OK;
+  if (!x || !ws) return MXMOE_ERR_NULL;
+  const void* outs[] = {x, ws, idx_out, w_out, counts_out, offsets_out, sorted_out, pos_out};
+  for (const void* p : outs)
+    if (p && !aligned16(p)) return MXMOE_ERR_ALIGN;
+  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, o->fp8_act == 1);
+  if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
+  return hip_status(run_routing(L, x, T, o->act_dtype, w, ws, idx_out, w_out, counts_out, offsets_out, sorted_out,
+                                pos_out, static_cast<hipStream_t>(stream)));
+}
+
+mxmoe_status_t moe_mxfp4_calibrate_fp8(const mxmoe_layer_t* L, const void* x, int64_t T, float* scales_out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  mxmoe_status_t st = check_layer(L);
+  if (st != MXMOE_OK) return st;
+  if (L->param_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
+  if ((st = check_tokens(L, T)) != MXMOE_OK) return st;
+  if (T < 1) return MXMOE_ERR_SHAPE;
+  if (!x || !scales_out || !ws) return MXMOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(scales_out) || !aligned16(ws)) return MXMOE_ERR_ALIGN;
+  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, MXMOE_BF16, false);
+  if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_routing(L, x, T, MXMOE_BF16, w, ws, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  if (e != hipSuccess) return MXMOE_ERR_HIP;
+  GemmArgs g0 = gemm_args(L, w, ws, T, ACT_BF16, 0);
+  g0.bsrc = x;
+  if (launch_moe_gemm(g0, use_prefill(L, T, ACT_BF16), s) != hipSuccess) return MXMOE_ERR_HIP;
+  uint32_t* slots = at<uint32_t>(ws, w.calib);
+  if (launch_calib_init(slots, s) != hipSuccess) return MXMOE_ERR_HIP;
+  if (launch_amax_bf16(static_cast<const uint16_t*>(x), T * L->H, slots, s) != hipSuccess) return MXMOE_ERR_HIP;
+  if (launch_amax_bf16(at<uint16_t>(ws, w.h), T * L->top_k * L->I, slots + 1, s) != hipSuccess) return MXMOE_ERR_HIP;
+  return hip_status(launch_calib_finish(slots, scales_out, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// MXFP4 unpack (dequantise) and pack (quantise) kernels for gfx950.
+//
+// Format (KerasFormers "mxfp4" page, intro and "Primitives"): a row of K
+// values is K/32 blocks of 16 bytes, element 32*b + 2*j + n being nibble n
+// (low first) of byte j of block b, e2m1 with bit 3 the sign, times
+// 2^(e8m0 - 127) from the block's scale byte.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxmoe {
+
+// ---------------------------------------------------------------- unpack
+//
+// HBM-bound: 17 bytes in, 64 (bf16) or 128 (fp32) bytes out per block.  Each
+// thread owns one 16-byte block: one 128-bit load, one scale byte, sixteen
+// packed hardware conversions (exact for every byte and scale, including
+// s = 0 -> 2^-127, s = 255 -> NaN and overflow -> Inf), and four or eight
+// 128-bit stores.  Consecutive lanes own consecutive blocks, so the loads
+// and the wave's stores each cover one contiguous span.
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void unpack_kernel(const u32x4_t* __restrict__ blocks,
+                                                     const uint8_t* __restrict__ scales,
+                                                     void* __restrict__ out, int64_t nblocks) {
+  int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= nblocks) return;
+  const u32x4_t w = __builtin_nontemporal_load(blocks + i);
+  const float sc = e8m0_as_scale_operand(scales[i]);
+  if constexpr (OUT_BF16) {
+    u32x4_t* o = static_cast<u32x4_t*>(out) + i * 4;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      u32x4_t r;
+      r[0] = fp4x2_to_bf16x2<0>(w[d], sc);
+      r[1] = fp4x2_to_bf16x2<1>(w[d], sc);
+      r[2] = fp4x2_to_bf16x2<2>(w[d], sc);
+      r[3] = fp4x2_to_bf16x2<3>(w[d], sc);
+      __builtin_nontemporal_store(r, o + d);
+    }
+  } else {
+    f32x4_t* o = static_cast<f32x4_t*>(out) + i * 8;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f32x2_t a = fp4x2_to_f32x2<0>(w[d], sc);
+      const f32x2_t b = fp4x2_to_f32x2<1>(w[d], sc);
+      const f32x2_t c = fp4x2_to_f32x2<2>(w[d], sc);
+      const f32x2_t e = fp4x2_to_f32x2<3>(w[d], sc);
+      __builtin_nontemporal_store(f32x4_t{a[0], a[1], b[0], b[1]}, o + 2 * d);
+      __builtin_nontemporal_store(f32x4_t{c[0], c[1], e[0], e[1]}, o + 2 * d + 1);
+    }
+  }
+}
+
+hipError_t launch_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t nblocks, void* out, bool out_bf16,
+                         hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;
+  int64_t grid = (nblocks + 255) / 256;
+  if (out_bf16)
+    unpack_kernel<true><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(reinterpret_cast<const u32x4_t*>(blocks), scales,
+                                                                       out, nblocks);
+  else
+    unpack_kernel<false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(reinterpret_cast<const u32x4_t*>(blocks), scales,
+                                                                        out, nblocks);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ pack
+//
+// One thread per 32-value block ("Primitives": quantize).  The block
+// exponent e = floor(log2(amax)) - 2 is read from the float's exponent
+// field (subnormal amax via the leading-zero count), clamped to
+// [-127, 127]; v = w * 2^-e is exact, and its magnitude maps to the FP4 code
+// index by counting the rounding thresholds it passes.  The thresholds are
+// the midpoints between neighbouring grid values; '>' at a midpoint whose
+// lower neighbour has an even index and '>=' where the upper one does give
+// round-half-to-even on the code.
+
+__device__ __forceinline__ uint32_t fp4_index_of_magnitude(float a) {
+  return uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+         uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+}
+
+__device__ __forceinline__ int floor_log2_abs(float amax) {
+  uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
+  int ef = int(u >> 23);
+  if (ef > 0) return ef - 127;
+  // subnormal: value = m * 2^-149 with m = u (nonzero)
+  return (31 - __clz(u)) - 149;
+}
+
+template <bool IN_BF16>
+__global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ w, uint8_t* __restrict__ blocks,
+                                                   uint8_t* __restrict__ scales, int64_t nblocks) {
+  int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= nblocks) return;
+  float v[32];
+  if constexpr (IN_BF16) {
+    const uint4* p = static_cast<const uint4*>(w) + i * 4;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint4 q = p[d];
+      uint32_t qs[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[d * 8 + t * 2] = __uint_as_float(qs[t] << 16);
+        v[d * 8 + t * 2 + 1] = __uint_as_float(qs[t] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* p = static_cast<const float4*>(w) + i * 8;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      float4 q = p[d];
+      v[d * 4 + 0] = q.x;
+      v[d * 4 + 1] = q.y;
+      v[d * 4 + 2] = q.z;
+      v[d * 4 + 3] = q.w;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 32; ++t) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[t]));
+  int e = amax > 0.0f ? floor_log2_abs(amax) - 2 : -127;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  uint32_t words[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    float a = __builtin_amdgcn_ldexpf(__builtin_fabsf(v[t]), -e);
+    uint32_t nib = fp4_index_of_magnitude(a) | ((__float_as_uint(v[t]) >> 28) & 8u);
+    words[t / 8] |= nib << (4 * (t % 8));
+  }
+  reinterpret_cast<uint4*>(blocks)[i] = make_uint4(words[0], words[1], words[2], words[3]);
+  scales[i] = uint8_t(e + 127);
+}
+
+hipError_t launch_pack(const void* w, bool in_bf16, int64_t nblocks, uint8_t* blocks, uint8_t* scales,
+                       hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;
+  int64_t grid = (nblocks + 255) / 256;
+  if (in_bf16)
+    pack_kernel<true><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(w, blocks, scales, nblocks);
+  else
+    pack_kernel<false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(w, blocks, scales, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

@@ -1,0 +1,97 @@
+// Device-side helpers shared by the gfx950 kernels of the MXFP4 MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Largest top_k the kernels handle (the ABI limit).
+constexpr int MAX_TOPK_DEV = 8;
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Two floats -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// An e8m0 scale byte as the float whose exponent field is that byte; the
+// scaled conversions read only the exponent, so byte 0 means 2^-127 and
+// byte 255 means NaN.
+__device__ __forceinline__ float e8m0_as_scale_operand(uint32_t s) { return __uint_as_float(s << 23); }
+
+// float8_e4m3fn code of v (round to nearest even), saturating to +-448 first:
+// the hardware conversion itself turns overflow into NaN.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  v = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false)) & 0xFFu;
+}
+
+// Four floats -> four e4m3 codes packed little-endian in a dword.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  c = __builtin_fminf(__builtin_fmaxf(c, -448.0f), 448.0f);
+  d = __builtin_fminf(__builtin_fmaxf(d, -448.0f), 448.0f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return uint32_t(r);
+}
+
+// ------------------------------------------------------------ FP4 decode
+
+// Nibbles of byte `sel` of `w` -> two bf16 values code * 2^(s-127), packed.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
+}
+
+// Eight nibbles (one dword, low nibble first) -> eight bf16 for an MFMA operand.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t w, float scale) {
+  u32x4_t v;
+  v[0] = fp4x2_to_bf16x2<0>(w, scale);
+  v[1] = fp4x2_to_bf16x2<1>(w, scale);
+  v[2] = fp4x2_to_bf16x2<2>(w, scale);
+  v[3] = fp4x2_to_bf16x2<3>(w, scale);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// ----------------------------------------------------------------- misc
+
+__device__ __forceinline__ float clamped_swiglu(float gate, float up) {
+  // gate <= 7, up in [-7, 7], h = (up + 1) * gate * sigmoid(1.702 * gate)
+  float g = __builtin_fminf(gate, 7.0f);
+  float u = __builtin_fminf(__builtin_fmaxf(up, -7.0f), 7.0f);
+  float sig = 1.0f / (1.0f + __expf(-1.702f * g));
+  return (u + 1.0f) * g * sig;
+}
+
+__device__ __forceinline__ float load_param(const void* p, int64_t i, int is_bf16) {
+  return is_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+
+}  // namespace mxmoe

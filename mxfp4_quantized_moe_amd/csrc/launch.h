@@ -1,0 +1,90 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+// Arithmetic of the expert GEMMs: fp32 or bf16 activations on decoded
+// weights, or FP8 activations on the scaled MXFP4 x FP8 instructions.
+enum Act : int { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2 };
+
+// Token-tile height of the prefill grouped GEMM (tokens per workgroup tile).
+constexpr int kPrefillTokens = 64;
+// Rows of a prefill workgroup stripe (4 waves x 64 rows).
+constexpr int kPrefillRows = 256;
+
+hipError_t launch_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t nblocks, void* out, bool out_bf16,
+                         hipStream_t stream);
+hipError_t launch_pack(const void* w, bool in_bf16, int64_t nblocks, uint8_t* blocks, uint8_t* scales,
+                       hipStream_t stream);
+
+struct RouteArgs {
+  const void* x;        // (T, H) act dtype
+  const void* w_r;      // (E, H) same dtype
+  const void* b_r;      // (E,)
+  int act_bf16;         // 1 = bf16 x and router, 0 = fp32
+  int T, H, E, top_k;
+  int32_t* idx;         // (T, k) workspace
+  float* wts;           // (T, k) workspace
+  int32_t* idx_out;     // optional copies
+  float* wts_out;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+struct PermuteArgs {
+  const int32_t* idx;   // (T*k)
+  int n_slots, E;
+  int32_t* counts;      // (E)
+  int32_t* offsets;     // (E+1)
+  int32_t* sorted;      // (T*k)
+  int32_t* pos;         // (T*k)
+  int32_t* active;      // (E + 1): active[0] = count, active[1..] = expert ids ascending
+  int32_t* tile_off;    // (E+1): prefix of ceil(count / kPrefillTokens)
+  int32_t* counts_out;  // optional copies
+  int32_t* offsets_out;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+
+// FP8 static quantisation of a (rows, cols) bf16 tensor to e4m3 codes.
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8_t* q, hipStream_t stream);
+
+struct GemmArgs {
+  int act;                    // Act: 0 f32, 1 bf16, 2 fp8
+  int phase;                  // 0 = gate_up + SwiGLU -> h, 1 = down -> Y
+  const uint8_t* wblk;        // (E, R, nb, 16)
+  const uint8_t* wsc;         // (E, R, nb)
+  const void* bias;           // (E, R)
+  int bias_bf16;
+  int R, nb, top_k, E;
+  const void* bsrc;           // phase 0: x (T, K) act storage; phase 1: h (T*k, K) act storage
+  const int32_t* sorted;      // (T*k) flat slot ids in expert order
+  const int32_t* offsets;     // (E+1)
+  const int32_t* active;      // (E+1)
+  const int32_t* tile_off;    // (E+1)
+  void* out;                  // phase 0: h (T*k, R/2) act storage; phase 1: Y (T*k, R) fp32
+  float acc_scale;            // fp8: the static scale of the B operand; else 1
+  float out_inv_scale;        // phase 0 fp8: 1 / h_scale
+  int max_active;             // grid bound: min(E, T*k)
+  int max_tiles;              // grid bound of the prefill tile list
+  int n_slots;                // T*k
+};
+hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream);
+
+struct CombineArgs {
+  const float* Y;        // (T*k, H) fp32 in sorted order
+  const int32_t* pos;    // (T*k)
+  const float* wts;      // (T, k)
+  void* out;             // (T, H) act dtype
+  int out_bf16;
+  int T, H, top_k;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// amax of bf16 tensors into two uint32 slots, then scales = amax / 448.
+hipError_t launch_calib_init(uint32_t* slots, hipStream_t stream);
+hipError_t launch_amax_bf16(const uint16_t* v, int64_t n, uint32_t* slot, hipStream_t stream);
+hipError_t launch_calib_finish(const uint32_t* slots, float* scales_out, hipStream_t stream);
+
+}  // namespace mxmoe

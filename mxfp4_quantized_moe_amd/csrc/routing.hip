@@ -1,0 +1,413 @@
+// Routing kernels of the MXFP4 MoE layer for gfx950: router GEMM with fused
+// top-k + softmax, the token->expert grouping (histogram, scan, stable
+// permutation by wavefront ballots), FP8 static quantisation of x and the
+// calibration reductions.
+//
+// The router is the upstream GptOssExperts one (gpt-oss-15.5b-23E-nf4-GPU
+// page, "Notes"): logits = W_r x + b_r from the unquantised activations (the
+// router is excluded from quantisation on the gpt-oss-120b-mxfp4-fp8attn-v2
+// and amd/gpt-oss-20b-MoE-Quant-W-MXFP4-A-FP8-KV-FP8 pages), the top-k
+// logits, then a softmax over those k.
+#include <climits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxmoe {
+
+// ------------------------------------------------------------------ router
+//
+// One workgroup (4 waves) per 16 tokens.  The logits^T tile (E x 16) is an
+// MFMA product with A = W_r rows (experts) and B = x rows (tokens); the 4
+// waves split the contracting dimension into interleaved 128-wide chunks and
+// their partial sums are added in a fixed order in LDS, so the logits are
+// deterministic.  Inside a chunk, lane group g (lanes 16g..16g+15) of the
+// MFMA covers K = 128c + 32g + [0, 32): the same permutation of K is applied
+// to both operands, which leaves the dot products unchanged.
+
+constexpr int kRouteTokens = 16;
+constexpr int kMaxRowTiles = 16;  // E <= 256
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+  extern __shared__ float part[];  // [4][16][E]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int E = a.E, H = a.H;
+  const int t0 = blockIdx.x * kRouteTokens;
+  const int tok = t0 + r16;
+  const bool tok_ok = tok < a.T;
+  const int nrt = (E + 15) >> 4;
+  const int nchunks = (H + 127) >> 7;
+
+  f32x4_t acc[kMaxRowTiles];
+#pragma unroll
+  for (int rt = 0; rt < kMaxRowTiles; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = wave; c < nchunks; c += 4) {
+    const int kb = 128 * c + 32 * g;  // start of this lane group's 32 K values
+    const bool k_ok = kb < H;
+    if constexpr (BF16) {
+      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + int64_t(tok) * H + kb;
+      const uint16_t* wr = static_cast<const uint16_t*>(a.w_r);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint4 bq = make_uint4(0, 0, 0, 0);
+        if (tok_ok && k_ok) bq = *reinterpret_cast<const uint4*>(xr + 8 * s);
+        bf16x8_t b = __builtin_bit_cast(bf16x8_t, bq);
+#pragma unroll
+        for (int rt = 0; rt < kMaxRowTiles; ++rt) {
+          if (rt < nrt) {
+            const int e = rt * 16 + r16;
+            uint4 aq = make_uint4(0, 0, 0, 0);
+            if (e < E && k_ok) aq = *reinterpret_cast<const uint4*>(wr + int64_t(e) * H + kb + 8 * s);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aq), b, acc[rt], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+      const float* xr = static_cast<const float*>(a.x) + int64_t(tok) * H + kb;
+      const float* wr = static_cast<const float*>(a.w_r);
+#pragma unroll
+      for (int s4 = 0; s4 < 8; ++s4) {
+        float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tok_ok && k_ok) bq = *reinterpret_cast<const float4*>(xr + 4 * s4);
+#pragma unroll
+        for (int rt = 0; rt < kMaxRowTiles; ++rt) {
+          if (rt < nrt) {
+            const int e = rt * 16 + r16;
+            float4 aq = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < E && k_ok) aq = *reinterpret_cast<const float4*>(wr + int64_t(e) * H + kb + 4 * s4);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.x, bq.x, acc[rt], 0, 0, 0);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.y, bq.y, acc[rt], 0, 0, 0);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.z, bq.z, acc[rt], 0, 0, 0);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.w, bq.w, acc[rt], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // partial logits: accumulator element i of row tile rt is expert
+  // rt*16 + 4g + i for token r16
+  float* mine = part + (wave * kRouteTokens + r16) * E;
+#pragma unroll
+  for (int rt = 0; rt < kMaxRowTiles; ++rt) {
+    if (rt < nrt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = rt * 16 + 4 * g + i;
+        if (e < E) mine[e] = acc[rt][i];
+      }
+    }
+  }
+  __syncthreads();
+  const int tile = kRouteTokens * E;
+  for (int j = threadIdx.x; j < tile; j += 256) {
+    const int e = j % E;
+    float s = part[j];
+    s += part[tile + j];
+    s += part[2 * tile + j];
+    s += part[3 * tile + j];
+    part[j] = s + load_param(a.b_r, e, a.act_bf16);
+  }
+  __syncthreads();
+
+  // top-k + softmax: wave w handles tokens 4w .. 4w+3 of the tile
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tl = wave * 4 + tt;
+    const int t = t0 + tl;
+    if (t >= a.T) break;
+    const float* lg = part + tl * E;
+    float v[4];
+    unsigned picked = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      float x = e < E ? lg[e] : -INFINITY;
+      v[j] = (x != x) ? -INFINITY : x;  // a NaN logit ranks lowest
+    }
+    float sel_v[MAX_TOPK_DEV];
+    int sel_i[MAX_TOPK_DEV];
+#pragma unroll
+    for (int kk = 0; kk < MAX_TOPK_DEV; ++kk) {
+      sel_v[kk] = -INFINITY;
+      sel_i[kk] = 0;
+      if (kk < a.top_k) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = lane + 64 * j;
+          if (e < E && !((picked >> j) & 1u)) {
+            if (v[j] > bv || (v[j] == bv && e < bi)) {
+              bv = v[j];
+              bi = e;
+            }
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const float ov = __shfl_xor(bv, off);
+          const int oi = __shfl_xor(bi, off);
+          if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        sel_v[kk] = bv;
+        sel_i[kk] = bi;
+        if ((bi & 63) == lane) picked |= 1u << (bi >> 6);
+      }
+    }
+    const float m = sel_v[0];
+    float den = 0.f;
+    float ex[MAX_TOPK_DEV];
+#pragma unroll
+    for (int kk = 0; kk < MAX_TOPK_DEV; ++kk) {
+      ex[kk] = kk < a.top_k ? expf(sel_v[kk] - m) : 0.f;
+      den += ex[kk];
+    }
+#pragma unroll
+    for (int kk = 0; kk < MAX_TOPK_DEV; ++kk) {
+      if (kk < a.top_k && lane == kk) {
+        const float w = ex[kk] / den;
+        const int64_t o = int64_t(t) * a.top_k + kk;
+        a.idx[o] = sel_i[kk];
+        a.wts[o] = w;
+        if (a.idx_out) a.idx_out[o] = sel_i[kk];
+        if (a.wts_out) a.wts_out[o] = w;
+      }
+    }
+  }
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const unsigned grid = unsigned((a.T + kRouteTokens - 1) / kRouteTokens);
+  const size_t lds = size_t(4) * kRouteTokens * a.E * sizeof(float);
+  if (a.act_bf16)
+    route_kernel<true><<<dim3(grid), dim3(256), lds, stream>>>(a);
+  else
+    route_kernel<false><<<dim3(grid), dim3(256), lds, stream>>>(a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- permutation
+//
+// One workgroup of 16 waves.  (1) histogram of expert ids with LDS atomics
+// (integer counts, order-free); (2) exclusive scan, active-expert list and
+// prefill tile offsets by wave 0; (3) stable ranking in chunks of 1024 slots:
+// inside a wave the lanes holding the same expert find each other with eight
+// ballots over the id bits (rank = popcount of lower peers), across the 16
+// waves of a chunk per-(wave, expert) counts are scanned in wave order, and
+// a running base per expert carries over between chunks.  The result orders
+// the slots by (expert, flat slot id), the same grouping a stable sort gives.
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / 64;
+
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  *total = __shfl(x, 63);
+  return x - v;
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) {
+  __shared__ int cnt[256];
+  __shared__ int off[257];
+  __shared__ int run_base[256];
+  __shared__ int chunk_total[256];
+  __shared__ int wcnt[kPermWaves][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, N = a.n_slots;
+
+  for (int e = tid; e < 256; e += kPermThreads) {
+    cnt[e] = 0;
+    run_base[e] = 0;
+  }
+  __syncthreads();
+  for (int s = tid; s < N; s += kPermThreads) {
+    int e = a.idx[s];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // each lane scans 4 consecutive experts
+    int c[4], t[4], tsum = 0, csum = 0, act = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      c[j] = e < E ? cnt[e] : 0;
+      t[j] = (c[j] + kPrefillTokens - 1) / kPrefillTokens;
+      csum += c[j];
+      tsum += t[j];
+      act += c[j] > 0;
+    }
+    int ctot, ttot, atot;
+    int cbase = wave_excl_scan(csum, lane, &ctot);
+    int tbase = wave_excl_scan(tsum, lane, &ttot);
+    int abase = wave_excl_scan(act, lane, &atot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      if (e < E) {
+        off[e] = cbase;
+        a.offsets[e] = cbase;
+        a.counts[e] = c[j];
+        a.tile_off[e] = tbase;
+        if (a.counts_out) a.counts_out[e] = c[j];
+        if (a.offsets_out) a.offsets_out[e] = cbase;
+        if (c[j] > 0) a.active[1 + abase++] = e;
+      }
+      cbase += c[j];
+      tbase += t[j];
+    }
+    if (lane == 0) {
+      off[E] = ctot;
+      a.offsets[E] = ctot;
+      a.tile_off[E] = ttot;
+      a.active[0] = atot;
+      if (a.offsets_out) a.offsets_out[E] = ctot;
+    }
+  }
+  __syncthreads();
+
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < N; base += kPermThreads) {
+    for (int j = tid; j < kPermWaves * 256; j += kPermThreads) (&wcnt[0][0])[j] = 0;
+    __syncthreads();
+    const int s = base + tid;
+    const bool valid = s < N;
+    int key = 0;
+    if (valid) {
+      key = a.idx[s];
+      key = key < 0 ? 0 : (key >= E ? E - 1 : key);
+    }
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) wcnt[wave][key] = __popcll(peers);
+    __syncthreads();
+    for (int e = tid; e < E; e += kPermThreads) {
+      int r = 0;
+      for (int w = 0; w < kPermWaves; ++w) {
+        const int c = wcnt[w][e];
+        wcnt[w][e] = r;
+        r += c;
+      }
+      chunk_total[e] = r;
+    }
+    __syncthreads();
+    if (valid) {
+      const int p = off[key] + run_base[key] + wcnt[wave][key] + rank;
+      a.sorted[p] = s;
+      a.pos[s] = p;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kPermThreads) run_base[e] += chunk_total[e];
+    __syncthreads();
+  }
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
+  permute_kernel<<<dim3(1), dim3(kPermThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------- FP8 quant
+//
+// code = sat448(rne_e4m3(fp32(x) * inv_scale)), inv_scale = 1 / s computed
+// once in fp32 on the host (FP8 static per-tensor scheme).  8 values per
+// thread: one 16-byte load, one 8-byte store.
+
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint4* __restrict__ x, int64_t n8, float inv,
+                                                        uint2* __restrict__ q) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 v = x[i];
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __uint_as_float(w[j] << 16) * inv;
+    f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u) * inv;
+  }
+  q[i] = make_uint2(pack_e4m3x4(f[0], f[1], f[2], f[3]), pack_e4m3x4(f[4], f[5], f[6], f[7]));
+}
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8_t* q, hipStream_t stream) {
+  const int64_t n8 = n / 8;  // n is a multiple of 32
+  if (n8 == 0) return hipSuccess;
+  quant_fp8_kernel<<<dim3(unsigned((n8 + 255) / 256)), dim3(256), 0, stream>>>(
+      reinterpret_cast<const uint4*>(x), n8, inv_scale, reinterpret_cast<uint2*>(q));
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- calibration
+//
+// amax over bf16 tensors: |v| as an unsigned bit pattern orders like the
+// value, so an integer atomic max gives the exact, order-free maximum.
+
+__global__ void calib_init_kernel(uint32_t* slots) {
+  if (threadIdx.x < 2) slots[threadIdx.x] = 0u;
+}
+
+__global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict__ v, int64_t n8, uint32_t* slot) {
+  uint32_t m = 0;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n8; i += int64_t(gridDim.x) * 256) {
+    const uint4 q = v[i];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+      lo = lo > 0x7F80u ? 0u : lo;  // NaN does not count
+      hi = hi > 0x7F80u ? 0u : hi;
+      m = m > lo ? m : lo;
+      m = m > hi ? m : hi;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(m, off);
+    m = m > o ? m : o;
+  }
+  if ((threadIdx.x & 63) == 0) atomicMax(slot, m);
+}
+
+__global__ void calib_finish_kernel(const uint32_t* slots, float* out) {
+  if (threadIdx.x < 2) out[threadIdx.x] = __uint_as_float(slots[threadIdx.x] << 16) / 448.0f;
+}
+
+hipError_t launch_calib_init(uint32_t* slots, hipStream_t stream) {
+  calib_init_kernel<<<1, 64, 0, stream>>>(slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16(const uint16_t* v, int64_t n, uint32_t* slot, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  int64_t grid = (n8 + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  amax_bf16_kernel<<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(reinterpret_cast<const uint4*>(v), n8, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_calib_finish(const uint32_t* slots, float* scales_out, hipStream_t stream) {
+  calib_finish_kernel<<<1, 64, 0, stream>>>(slots, scales_out);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

@@ -1,0 +1,166 @@
+"""The C ABI without a GPU: the library loads, exports what include/mxmoe.h
+declares, and rejects bad arguments on the host before any launch.
+
+Every call here fails validation (or is a documented no-op) so nothing is
+launched; fake device pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_quantized_moe_amd as mx
+from mxfp4_quantized_moe_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+OK, NULL, ALIGN, SHAPE, DTYPE, WS, UNSUP, HIP, VALUE = range(9)
+P = 0x10000  # a 16-byte aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmxmoe.so is not built: run `python -m mxfp4_quantized_moe_amd.build`")
+    return mx.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.mxmoe_version() == 1
+    for s in range(9):
+        assert lib.mxmoe_status_string(s)
+
+
+def test_unpack_pack_validation(lib):
+    s = None
+    assert lib.mxfp4_unpack(P, P, 4, 48, P, 1, s) == SHAPE  # k % 32 != 0 ("a clear error")
+    assert lib.mxfp4_unpack(P, P, 4, 0, P, 1, s) == SHAPE
+    assert lib.mxfp4_unpack(P, P, -1, 64, P, 1, s) == SHAPE
+    assert lib.mxfp4_unpack(P, P, 4, 64, P, 7, s) == DTYPE
+    assert lib.mxfp4_unpack(None, P, 4, 64, P, 1, s) == NULL
+    assert lib.mxfp4_unpack(P, P, 4, 64, P + 8, 1, s) == ALIGN
+    assert lib.mxfp4_unpack(P, P, 0, 64, P, 1, s) == OK  # no rows: no-op, nothing launched
+    assert lib.mxfp4_pack(P, 0, 4, 33, P, P, s) == SHAPE
+    assert lib.mxfp4_pack(P, 2, 4, 64, P, P, s) == DTYPE
+    assert lib.mxfp4_pack(P, 0, 4, 64, None, P, s) == NULL
+    assert lib.mxfp4_pack(P + 4, 0, 4, 64, P, P, s) == ALIGN
+    assert lib.mxfp4_pack(P, 1, 0, 64, P, P, s) == OK
+
+
+def _layer(**kw):
+    d = dict(E=4, H=64, I=64, top_k=2, param_dtype=1, reserved0=0, gate_up_blocks=P, gate_up_scales=P,
+             gate_up_bias=P, down_blocks=P, down_scales=P, down_bias=P, router_w=P, router_b=P)
+    d.update(kw)
+    return B.Layer(**d)
+
+
+def _opts(**kw):
+    d = dict(act_dtype=1, fp8_act=0, x_scale=1.0, h_scale=1.0, topk_idx_out=None, topk_w_out=None)
+    d.update(kw)
+    return B.FwdOpts(**d)
+
+
+def _fwd(lib, layer, T=8, opts=None, x=P, out=P, ws=P, ws_bytes=1 << 30):
+    opts = opts or _opts()
+    return lib.moe_mxfp4_forward(ctypes.byref(layer), x, T, out, ctypes.byref(opts), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=48), SHAPE),            # contracting dim of gate_up not a multiple of 32
+    (dict(I=80), SHAPE),            # contracting dim of down not a multiple of 32
+    (dict(E=0), SHAPE),
+    (dict(E=257), SHAPE),
+    (dict(top_k=0), SHAPE),
+    (dict(top_k=5), SHAPE),         # > E
+    (dict(E=16, top_k=9), SHAPE),   # > 8
+    (dict(param_dtype=3), DTYPE),
+    (dict(gate_up_blocks=None), NULL),
+    (dict(router_b=None), NULL),
+    (dict(down_scales=P + 1), ALIGN),
+])
+def test_forward_layer_validation(lib, kw, code):
+    assert _fwd(lib, _layer(**kw)) == code
+
+
+def test_forward_opts_validation(lib):
+    L = _layer()
+    assert _fwd(lib, L, opts=_opts(act_dtype=5)) == DTYPE
+    assert _fwd(lib, L, opts=_opts(act_dtype=0)) == DTYPE  # x fp32 with bf16 params
+    assert _fwd(lib, _layer(param_dtype=0), opts=_opts(act_dtype=0, fp8_act=1)) == DTYPE  # FP8 needs bf16
+    assert _fwd(lib, L, opts=_opts(fp8_act=1, x_scale=0.0)) == VALUE
+    assert _fwd(lib, L, opts=_opts(fp8_act=1, h_scale=float("nan"))) == VALUE
+    assert _fwd(lib, L, opts=_opts(fp8_act=1, x_scale=-1.0)) == VALUE
+    assert _fwd(lib, L, opts=_opts(fp8_act=2)) == VALUE
+    assert _fwd(lib, L, opts=_opts(topk_idx_out=P + 4)) == ALIGN
+    assert lib.moe_mxfp4_forward(ctypes.byref(L), P, 8, P, None, P, 1 << 30, None) == NULL
+
+
+def test_forward_token_and_workspace_validation(lib):
+    L = _layer()
+    assert _fwd(lib, L, T=-1) == SHAPE
+    assert _fwd(lib, L, T=0, x=None, out=None, ws=None) == OK  # empty batch: no-op
+    assert _fwd(lib, L, x=None) == NULL
+    assert _fwd(lib, L, out=P + 2) == ALIGN
+    need = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 8, ctypes.byref(_opts()))
+    assert need > 0
+    assert _fwd(lib, L, ws_bytes=need - 1) == WS
+    assert _fwd(lib, L, T=(1 << 26)) == SHAPE  # T * top_k beyond the slot limit
+    # the FP8 mode needs room for the quantised x
+    need8 = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 8, ctypes.byref(_opts(fp8_act=1)))
+    assert need8 > need - 8 * 64 * 2 * 1
+    assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(_layer(H=40)), 8, ctypes.byref(_opts())) == 0
+
+
+def test_workspace_bytes_grows_with_tokens(lib):
+    L = _layer(E=32, H=2880, I=2880, top_k=4)
+    o = _opts()
+    a = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 64, ctypes.byref(o))
+    b = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 4096, ctypes.byref(o))
+    assert 0 < a < b
+    # dominated by the per-slot intermediate h (bf16) and Y (fp32)
+    assert b >= 4096 * 4 * (2880 * 2 + 2880 * 4)
+
+
+def test_route_and_calibrate_validation(lib):
+    L = _layer()
+    o = _opts()
+    r = lib.moe_mxfp4_route(ctypes.byref(_layer(H=36)), P, 8, ctypes.byref(o), P, P, P, P, P, P, P, 1 << 30, None)
+    assert r == SHAPE
+    r = lib.moe_mxfp4_route(ctypes.byref(L), P, 8, ctypes.byref(o), P + 4, P, P, P, P, P, P, 1 << 30, None)
+    assert r == ALIGN
+    r = lib.moe_mxfp4_route(ctypes.byref(L), P, 8, ctypes.byref(o), P, P, P, P, P, P, P, 16, None)
+    assert r == WS
+    assert lib.moe_mxfp4_route(ctypes.byref(L), P, 0, ctypes.byref(o), None, None, None, None, None, None, None, 0,
+                               None) == OK
+    assert lib.moe_mxfp4_calibrate_fp8(ctypes.byref(_layer(param_dtype=0)), P, 8, P, P, 1 << 30, None) == DTYPE
+    assert lib.moe_mxfp4_calibrate_fp8(ctypes.byref(L), P, 0, P, P, 1 << 30, None) == SHAPE
+    assert lib.moe_mxfp4_calibrate_fp8(ctypes.byref(L), P, 8, None, P, 1 << 30, None) == NULL
+
+
+def test_binding_raises_on_bad_status(lib):
+    with pytest.raises(mx.MxmoeError) as ei:
+        B._check(SHAPE)
+    assert ei.value.status == SHAPE and "multiple of 32" in str(ei.value)
+
+
+def test_binding_has_no_cpu_fallback(tmp_path):
+    # loading a missing library raises instead of computing anything elsewhere
+    saved = B._lib
+    try:
+        B._lib = None
+        with pytest.raises(OSError):
+            B.load_library(str(tmp_path / "nope.so"))
+    finally:
+        B._lib = saved

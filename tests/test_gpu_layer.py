@@ -1,0 +1,213 @@
+"""GPU parity of routing and of the whole MoE layer against the oracle.
+
+Bars: routing index sets and the expert grouping are bit-exact (outside
+rounding-level near-ties, reported); the layer output satisfies
+max|d| <= 1e-2 * max|ref| for bf16/fp32 activations and <= 3e-2 * max|ref|
+in the FP8-activation mode, ref being the oracle's unrounded float64
+output.  The fp32 path is also held to 1e-4, the size of its own fp32
+accumulation error over K <= 2880 (decoded weights and fp32 inputs are
+exact, so only summation rounding remains).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.gpu_util import compare_routing, device, max_rel_err, note, sub_case
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-2, "fp8": 3e-2}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def run_gpu(case, dev, x_scale=1.0, h_scale=1.0, want_route=True):
+    import torch
+    import mxfp4_quantized_moe_amd as mx
+
+    wts = W.layer_to_torch(case.layer, dev)
+    x = W.array_to_torch(case.x, dev)
+    T, k = case.T, case.layer.top_k
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = mx.moe_mxfp4_forward(wts, x, fp8=case.fp8, x_scale=x_scale, h_scale=h_scale, topk_idx_out=idx,
+                               topk_w_out=w)
+    torch.cuda.synchronize()
+    res = dict(out=W.torch_to_array(out), idx=W.torch_to_array(idx), w=W.torch_to_array(w))
+    if want_route:
+        r = mx.moe_mxfp4_route(wts, x)
+        torch.cuda.synchronize()
+        res["route"] = [W.torch_to_array(t) for t in r]
+    return res, wts, x
+
+
+def as_f64(a, act):
+    return O.bf16_from_bits(a) if act == "bf16" else a.astype(np.float64)
+
+
+def check_perm(case, route):
+    idx, w, counts, offsets, sorted_slots, pos = route
+    c, o, s, p = O.permute(idx, case.layer.E)
+    assert np.array_equal(counts, c) and np.array_equal(offsets, o)
+    assert np.array_equal(sorted_slots, s) and np.array_equal(pos, p)
+
+
+def check_layer(case, res, sample=None, x_scale=None, h_scale=None, tol=None):
+    k = case.layer.top_k
+    n_exempt, override = compare_routing(case, res["idx"], res["w"])
+    if sample is None:
+        sample = np.arange(case.T)
+    sc = sub_case(case, sample)
+    ov = (override[0][sample], override[1][sample])
+    ref = O.moe_forward(sc.layer, sc.x, case.act_dtype, fp8=case.fp8, x_scale=x_scale, h_scale=h_scale,
+                        route_override=ov)
+    got = as_f64(res["out"][sample], case.act_dtype)
+    assert np.all(np.isfinite(as_f64(res["out"], case.act_dtype)))
+    err = max_rel_err(got, ref)
+    kind = "fp8" if case.fp8 else case.act_dtype
+    bar = tol if tol is not None else TOL[kind]
+    note(f"{case.name}: max|d|/max|ref| = {err:.3e} (bar {bar}), exempt tokens {n_exempt}")
+    assert err <= bar
+    return err
+
+
+# ------------------------------------------------------------ the five workloads
+
+
+def test_tiny_f32(dev):
+    case = W.tiny()
+    note(case.name)
+    res, _, _ = run_gpu(case, dev)
+    check_perm(case, res["route"])
+    check_layer(case, res, tol=1e-4)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_decode_20b(dev, T):
+    case = W.decode_20b(T=T)
+    note(case.name)
+    res, _, _ = run_gpu(case, dev)
+    check_perm(case, res["route"])
+    check_layer(case, res)
+
+
+def test_prefill_120b_full_size(dev):
+    """T=4096 at the 120b shape: routing and grouping for every token, the
+    layer output on 12 tokens spread over the batch (the oracle computes
+    them one by one; tokens are independent)."""
+    case = W.prefill_120b()
+    note(case.name)
+    res, _, _ = run_gpu(case, dev)
+    check_perm(case, res["route"])
+    counts = res["route"][2]
+    assert counts.max() > 3 * counts.mean()  # the router bias skews expert load
+    sample = np.linspace(0, case.T - 1, 12).astype(int)
+    check_layer(case, res, sample=sample)
+
+
+def test_fp8_20b_full_size(dev):
+    """W-MXFP4 A-FP8 at T=2048: static scales from the 256-token calibration
+    batch (the oracle's values, fed to both sides), output on 12 tokens."""
+    case = W.fp8_20b()
+    s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+    note(f"{case.name} s_x={s_x} s_h={s_h}")
+    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False)
+    sample = np.linspace(0, case.T - 1, 12).astype(int)
+    check_layer(case, res, sample=sample, x_scale=s_x, h_scale=s_h)
+
+
+def test_fp8_calibration_scales(dev):
+    import torch
+    import mxfp4_quantized_moe_amd as mx
+
+    case = W.fp8_20b()
+    s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+    note("fp8 calibration")
+    wts = W.layer_to_torch(case.layer, dev)
+    sc = mx.moe_mxfp4_calibrate_fp8(wts, W.array_to_torch(case.x_calib, dev))
+    torch.cuda.synchronize()
+    g = W.torch_to_array(sc)
+    assert np.float32(g[0]) == np.float32(s_x)  # amax of bf16 inputs is exact
+    assert abs(g[1] - s_h) <= 1e-2 * s_h  # h differs by accumulation order only
+
+
+# --------------------------------------------------------------- sweeps / edges
+
+
+@pytest.mark.parametrize("seed,E,H,I,k,T,act", [
+    (10, 8, 64, 64, 2, 33, "bf16"),      # ragged T, decode-shaped kernels
+    (11, 5, 96, 160, 3, 7, "bf16"),      # K/32 = 3 and 5: partial 128-K chunks
+    (12, 3, 128, 96, 3, 5, "f32"),       # top_k = E
+    (13, 1, 64, 32, 1, 9, "bf16"),       # a single expert
+    (14, 16, 256, 128, 8, 40, "bf16"),   # top_k = 8
+    (15, 4, 64, 96, 2, 300, "bf16"),     # prefill kernels, R = 192 < one 256-row stripe
+    (16, 6, 160, 352, 2, 777, "bf16"),   # prefill: ragged token tiles, K/32 = 5 and 11
+    (17, 2, 32, 32, 1, 200, "bf16"),     # smallest dims through prefill
+    (18, 4, 64, 64, 2, 130, "f32"),      # fp32 with more than 64 tokens per expert
+])
+def test_small_shapes(dev, seed, E, H, I, k, T, act):
+    case = W.small_case(seed, E, H, I, k, T, act_dtype=act)
+    note(case.name)
+    res, _, _ = run_gpu(case, dev)
+    check_perm(case, res["route"])
+    check_layer(case, res, tol=1e-4 if act == "f32" else None)
+
+
+@pytest.mark.parametrize("seed,E,H,I,k,T", [
+    (20, 4, 64, 64, 2, 16),     # decode-shaped
+    (21, 4, 96, 160, 2, 400),   # prefill-shaped with partial chunks
+])
+def test_small_fp8(dev, seed, E, H, I, k, T):
+    case = W.small_case(seed, E, H, I, k, T, act_dtype="bf16", fp8=True)
+    s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+    note(f"{case.name} fp8")
+    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False)
+    check_layer(case, res, x_scale=s_x, h_scale=s_h)
+
+
+def test_empty_batch_is_noop(dev):
+    import torch
+    import mxfp4_quantized_moe_amd as mx
+
+    case = W.small_case(30, 4, 64, 64, 2, 1)
+    wts = W.layer_to_torch(case.layer, dev)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    out = mx.moe_mxfp4_forward(wts, x)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_deterministic_bits(dev):
+    """Two forwards on the same inputs give identical bits (no float atomics)."""
+    import torch
+    import mxfp4_quantized_moe_amd as mx
+
+    for case in (W.decode_20b(T=64), W.small_case(40, 8, 128, 96, 2, 500)):
+        note(f"determinism {case.name}")
+        wts = W.layer_to_torch(case.layer, dev)
+        x = W.array_to_torch(case.x, dev)
+        a = mx.moe_mxfp4_forward(wts, x).clone()
+        b = mx.moe_mxfp4_forward(wts, x).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_prefixes_agree(dev):
+    """T=1 and T=8 decode batches are prefixes of T=64; per-token results may
+    only differ by the kernel path's rounding, not by routing."""
+    import torch
+    import mxfp4_quantized_moe_amd as mx
+
+    c64 = W.decode_20b(T=64)
+    wts = W.layer_to_torch(c64.layer, dev)
+    x = W.array_to_torch(c64.x, dev)
+    o64 = mx.moe_mxfp4_forward(wts, x)
+    o8 = mx.moe_mxfp4_forward(wts, x[:8].contiguous())
+    torch.cuda.synchronize()
+    a = O.bf16_from_bits(W.torch_to_array(o64[:8]))
+    b = O.bf16_from_bits(W.torch_to_array(o8))
+    assert np.max(np.abs(a - b)) <= 1e-2 * np.max(np.abs(a))

@@ -200,3 +200,47 @@ def random_weights(seed: int, rows: int, k: int, std: float = 1.0, dtype: str = 
     """A dense weight matrix to be packed (pack parity cases)."""
     rng = np.random.default_rng(seed)
     return _real(rng, (rows, k), std, dtype)
+
+
+# ---------------------------------------------------------------------------
+# Device upload (bit-for-bit copies, no arithmetic).
+# ---------------------------------------------------------------------------
+
+
+def _t(a: np.ndarray, device):
+    import torch
+
+    if a.dtype == np.uint16:  # raw bf16 bits
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def layer_to_torch(layer: MoELayer, device):
+    """The layer's arrays as device tensors, in the binding's MoEWeights."""
+    from mxfp4_quantized_moe_amd import MoEWeights
+
+    return MoEWeights(
+        gate_up_blocks=_t(layer.gate_up_blocks, device),
+        gate_up_scales=_t(layer.gate_up_scales, device),
+        gate_up_bias=_t(layer.gate_up_bias, device),
+        down_blocks=_t(layer.down_blocks, device),
+        down_scales=_t(layer.down_scales, device),
+        down_bias=_t(layer.down_bias, device),
+        router_w=_t(layer.router_w, device),
+        router_b=_t(layer.router_b, device),
+        top_k=layer.top_k,
+    )
+
+
+def array_to_torch(a: np.ndarray, device):
+    return _t(a, device)
+
+
+def torch_to_array(t) -> np.ndarray:
+    """Device tensor -> numpy (bf16 as raw uint16 bits)."""
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
