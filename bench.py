@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""MXFP4 MoE layer benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one moe_mxfp4_forward call (router + top-k/softmax, expert
+grouping, gate_up grouped GEMM with fused SwiGLU, down grouped GEMM,
+combine; plus the FP8 quantisation of x in FP8 mode) over one batch whose
+inputs already sit in HBM.  W untimed steps, then K timed steps between
+two device synchronisations; value = tokens / second of the timed steps.
+Weights are cycled over enough identical copies that a step does not find
+its experts in the 256 MB Infinity Cache left by the previous ones.
+
+The per-stage durations come from HIP events the library records on its
+stream inside the timed steps; the dominant kernel's average duration
+gives the roofline fraction against MI355X's published peaks.  The CPU
+baseline is the float64 oracle timed on a bounded slice of the same
+workload on the host cores (a reported baseline, not the target).
+
+Workloads (synthetic, seeded; see workloads/):
+  prefill_120b_t4096   gpt-oss-120b MoE layer, E=128, top-4, H=I=2880, T=4096, bf16 (default)
+  decode_20b_t{1,8,64} gpt-oss-20b MoE layer, E=32, top-4, H=I=2880, bf16
+  fp8_20b_t2048        W-MXFP4 A-FP8, gpt-oss-20b shape, T=2048
+  tiny                 E=4, top-2, H=I=64, T=8, fp32
+  unpack_20b           mxfp4_unpack of the 20b expert tensors to bf16 (GB/s)
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 MoE layer tokens/s; % HBM roofline (decode), % MFMA peak (prefill)"
+PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp8_TFLOPs": 5000.0, "fp32_TFLOPs": 157.3}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["mxfp4_quantized_moe_amd/csrc/moe_gemm.hip", "mxfp4_quantized_moe_amd/csrc/codec.hip",
+                  "mxfp4_quantized_moe_amd/csrc/device_common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------ HIP events
+
+class HipEvents:
+    """hipEvent_t handles from libamdhip64 (the stream-ordered timers the
+    library records around its stages)."""
+
+    _hip = None
+
+    def __init__(self, n: int):
+        if HipEvents._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvents._hip = hip
+        self.hip = HipEvents._hip
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = h
+        self.n = n
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+# ------------------------------------------------------------ workloads
+
+def make_case(name: str):
+    import workloads as W
+
+    if name == "prefill_120b_t4096":
+        return W.prefill_120b()
+    if name.startswith("decode_20b_t"):
+        return W.decode_20b(T=int(name.rsplit("t", 1)[1]))
+    if name == "fp8_20b_t2048":
+        return W.fp8_20b()
+    if name == "tiny":
+        return W.tiny()
+    raise SystemExit(f"unknown workload {name}")
+
+
+def layer_bytes(layer) -> int:
+    return sum(a.nbytes for a in (layer.gate_up_blocks, layer.gate_up_scales, layer.gate_up_bias, layer.down_blocks,
+                                  layer.down_scales, layer.down_bias))
+
+
+def expert_gemm_bytes(case, phase: int, n_active: int) -> int:
+    """Algorithmic HBM bytes of one grouped-GEMM launch: the routed experts'
+    packed weights, scales and biases once, the activations in and out once."""
+    L = case.layer
+    H, I, k, T = L.H, L.I, L.top_k, case.T
+    pb = 2 if L.param_dtype == "bf16" else 4
+    ab = 1 if case.fp8 else (2 if case.act_dtype == "bf16" else 4)
+    if phase == 0:
+        w = 2 * I * (H // 32) * 17 + 2 * I * pb
+        return n_active * w + T * H * ab + T * k * I * ab
+    w = H * (I // 32) * 17 + H * pb
+    return n_active * w + T * k * I * ab + T * k * H * 4
+
+
+def expert_gemm_flops(case, phase: int) -> int:
+    L = case.layer
+    slots = case.T * L.top_k
+    return 2 * slots * (2 * L.I) * L.H if phase == 0 else 2 * slots * L.H * L.I
+
+
+def cpu_baseline(case, budget_s: float):
+    """The oracle as it stands on a bounded token slice of the workload."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        cores = int(info[0]["num_threads"]) if info else os.cpu_count()
+        blas = info[0].get("internal_api", "blas") if info else "unknown"
+    except Exception:
+        cores, blas = os.cpu_count(), "unknown"
+    scales = {}
+    if case.fp8:
+        s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+        scales = dict(fp8=True, x_scale=s_x, h_scale=s_h)
+    n = 1
+    elapsed = 0.0
+    done = 0
+    # grow the slice until the budget is used (each slice is an independent forward)
+    while True:
+        rows = np.arange(done, min(done + n, case.T))
+        if rows.size == 0:
+            break
+        sub = W.MoECase(case.name, case.layer, case.x[rows].copy(), case.act_dtype, case.fp8, case.x_calib)
+        t0 = time.perf_counter()
+        O.moe_forward(sub.layer, sub.x, sub.act_dtype, **scales)
+        elapsed += time.perf_counter() - t0
+        done += rows.size
+        if elapsed >= budget_s or done >= case.T:
+            break
+        n = min(n * 2, case.T - done)
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {done} of {case.T} tokens of {case.name}, float64 NumPy ({blas}), "
+                      f"{elapsed:.1f} s, slices of doubling size each dequantising their routed experts"}
+
+
+# ------------------------------------------------------------ main legs
+
+def bench_layer(args, dev):
+    import numpy as np
+    import torch
+
+    import mxfp4_quantized_moe_amd as mx
+    import workloads as W
+    from mxfp4_quantized_moe_amd.binding import STAGE_EVENTS, STAGES
+
+    case = make_case(args.workload)
+    L = case.layer
+    T = case.T
+    w0 = W.layer_to_torch(L, dev)
+    x = W.array_to_torch(case.x, dev)
+    _, _, counts, _, _, _ = mx.moe_mxfp4_route(w0, x)
+    n_active = int((W.torch_to_array(counts) > 0).sum())
+    # identical weight copies: enough that a copy's routed experts were last
+    # read more than 1 GB of traffic ago (past the 256 MB Infinity Cache)
+    per_step = n_active * layer_bytes(L) // L.E
+    copies = min(64, -(-int(1.0e9) // per_step) + 1) if args.copies is None else args.copies
+    weights = [w0] + [type(w0)(*[getattr(w0, f).clone() for f in ("gate_up_blocks", "gate_up_scales", "gate_up_bias",
+                                                                  "down_blocks", "down_scales", "down_bias",
+                                                                  "router_w", "router_b")], top_k=w0.top_k)
+                      for _ in range(copies - 1)]
+    fp8_kw = {}
+    if case.fp8:
+        sc = mx.moe_mxfp4_calibrate_fp8(weights[0], W.array_to_torch(case.x_calib, dev))
+        s = W.torch_to_array(sc)
+        fp8_kw = dict(fp8=True, x_scale=float(s[0]), h_scale=float(s[1]))
+    ws = mx.alloc_workspace(weights[0], T, x.dtype, case.fp8)
+    out = torch.empty_like(x)
+
+    # a plain copy of known size: the reference point that scales the HBM
+    # byte counters of a profiled run (bytes moved = 2 x 256 MiB)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    del src, dst
+
+    for i in range(args.warmup):
+        mx.moe_mxfp4_forward(weights[i % copies], x, out=out, workspace=ws, **fp8_kw)
+    torch.cuda.synchronize()
+
+    ev = [HipEvents(STAGE_EVENTS) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mx.moe_mxfp4_forward(weights[i % copies], x, out=out, workspace=ws, stage_events=ev[i].arr, **fp8_kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms = np.array([[e.elapsed_ms(j, j + 1) for j in range(STAGE_EVENTS - 1)] for e in ev])
+    for e in ev:
+        e.close()
+    avg = stage_ms.mean(axis=0)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # dominant kernel: the gate_up grouped GEMM (2/3 of the flops, 2/3 of the weight bytes)
+    gu_s = avg[3] * 1e-3
+    decode_shaped = T * L.top_k <= 16 * min(L.E, T * L.top_k) or case.act_dtype == "f32"
+    if decode_shaped:
+        byts = expert_gemm_bytes(case, 0, n_active)
+        achieved = byts / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_GBps"], "unit": "GB/s",
+                "frac": achieved / PEAK["hbm_GBps"]}
+        algo = f"{byts} B per launch ({n_active} routed experts)"
+    else:
+        fl = expert_gemm_flops(case, 0)
+        peak = PEAK["fp8_TFLOPs"] if case.fp8 else PEAK["bf16_TFLOPs"]
+        achieved = fl / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
+        algo = f"{fl} flop per launch"
+    roof["kernel"] = "gemm_prefill_kernel<phase 0>" if not decode_shaped else "gemm_decode_kernel<phase 0>"
+    roof["algorithmic"] = algo
+    roof["traffic"] = measured_traffic(args.workload, roof["kernel"])
+    res = {
+        "metric": METRIC,
+        "value": T * args.steps / (t1 - t0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x mxfp4" if case.fp8 else case.act_dtype,
+        "data": "synthetic (seeded random MXFP4 weights and activations of the named shapes)",
+        "config": {"workload": case.name, "E": L.E, "top_k": L.top_k, "H": L.H, "I": L.I, "T": T,
+                   "act": "fp8" if case.fp8 else case.act_dtype, "weight_copies": copies,
+                   "routed_experts": n_active},
+        "roofline": roof,
+        "stages_us": {name: float(v * 1e3) for name, v in zip(STAGES, avg)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    return res
+
+
+def bench_unpack(args, dev):
+    import torch
+
+    import mxfp4_quantized_moe_amd as mx
+    import workloads as W
+
+    case = W.unpack_20b()
+    tens = [(W.array_to_torch(b, dev), W.array_to_torch(s, dev)) for b, s in case.tensors]
+    outs = [torch.empty(b.shape[:-2] + (b.shape[-2] * 32,), dtype=torch.bfloat16, device=dev) for b, _ in tens]
+    byts = sum(b.numel() + s.numel() + o.numel() * 2 for (b, s), o in zip(tens, outs))
+    for _ in range(args.warmup):
+        for (b, s), o in zip(tens, outs):
+            mx.mxfp4_unpack(b, s, out=o)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for (b, s), o in zip(tens, outs):
+            mx.mxfp4_unpack(b, s, out=o)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gbps = byts * args.steps / (t1 - t0) / 1e9
+    return {"metric": "mxfp4_unpack GB/s (bf16 out)", "value": gbps, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8->bf16",
+            "data": "synthetic", "config": {"workload": case.name, "bytes_per_step": byts},
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK["hbm_GBps"], "unit": "GB/s",
+                         "frac": gbps / PEAK["hbm_GBps"], "traffic": measured_traffic("unpack_20b", "unpack_kernel")}}
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        ent = t.get(workload)
+        if ent and ent.get("kernel_source_hash") == kernel_source_hash():
+            return ent["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_120b_t4096")
+    ap.add_argument("--copies", type=int, default=None, help="weight copies cycled through (default: >= 2 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the MoE layer is measured on one MI355X; "
+                                   "expert-parallel sharding across GPUs is described in DESIGN.md, not launched",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    if args.steps < 1:
+        raise SystemExit("--steps must be >= 1")
+
+    import torch
+
+    import mxfp4_quantized_moe_amd as mx
+
+    mx.load_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    if args.workload == "unpack_20b":
+        res = bench_unpack(args, dev)
+    else:
+        res = bench_layer(args, dev)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

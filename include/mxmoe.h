@@ -126,7 +126,17 @@ typedef struct {
   float h_scale;      /* FP8 mode: static per-tensor scale of the SwiGLU output */
   int32_t* topk_idx_out; /* optional device (T, top_k) int32: chosen experts */
   float* topk_w_out;     /* optional device (T, top_k) fp32: their weights */
+  /* optional: MXMOE_STAGE_EVENTS hipEvent_t handles created by the caller;
+   * event i is recorded on `stream` just before stage i (router, grouping,
+   * FP8 quantisation of x, gate_up + SwiGLU, down, combine) and the last one
+   * after the combine, so stage i takes elapsed(event i, event i+1).  A
+   * stage that does not run records its event at the same point as the
+   * next.  NULL records nothing. */
+  void* const* stage_events;
 } mxmoe_fwd_opts_t;
+
+/* Number of handles stage_events points to. */
+#define MXMOE_STAGE_EVENTS 7
 
 /*
  * Workspace size in bytes for moe_mxfp4_forward with these arguments

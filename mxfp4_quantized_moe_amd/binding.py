@@ -77,7 +77,12 @@ class FwdOpts(ctypes.Structure):
         ("h_scale", ctypes.c_float),
         ("topk_idx_out", ctypes.c_void_p),
         ("topk_w_out", ctypes.c_void_p),
+        ("stage_events", ctypes.c_void_p),
     ]
+
+
+STAGE_EVENTS = 7
+STAGES = ("router", "grouping", "quant_fp8", "gate_up_swiglu", "down", "combine")
 
 
 _lib = None
@@ -209,9 +214,11 @@ class MoEWeights:
             router_b=_ptr(self.router_b))
 
 
-def _opts(act_dtype: torch.dtype, fp8: bool, x_scale: float, h_scale: float, idx_out=None, w_out=None) -> FwdOpts:
+def _opts(act_dtype: torch.dtype, fp8: bool, x_scale: float, h_scale: float, idx_out=None, w_out=None,
+          stage_events=None) -> FwdOpts:
     return FwdOpts(act_dtype=_dtype_code(act_dtype), fp8_act=1 if fp8 else 0, x_scale=x_scale, h_scale=h_scale,
-                   topk_idx_out=_ptr(idx_out), topk_w_out=_ptr(w_out))
+                   topk_idx_out=_ptr(idx_out), topk_w_out=_ptr(w_out),
+                   stage_events=ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None)
 
 
 def workspace_bytes(layer: MoEWeights, T: int, act_dtype: torch.dtype, fp8: bool = False) -> int:
@@ -231,15 +238,18 @@ def alloc_workspace(layer: MoEWeights, T: int, act_dtype: torch.dtype, fp8: bool
 def moe_mxfp4_forward(layer: MoEWeights, x: torch.Tensor, fp8: bool = False, x_scale: float = 1.0,
                       h_scale: float = 1.0, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, topk_idx_out: Optional[torch.Tensor] = None,
-                      topk_w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The routed MXFP4 MoE layer on x (T, H); returns out (T, H)."""
+                      topk_w_out: Optional[torch.Tensor] = None, stage_events=None) -> torch.Tensor:
+    """The routed MXFP4 MoE layer on x (T, H); returns out (T, H).
+
+    stage_events: optional ctypes array of STAGE_EVENTS hipEvent_t handles
+    (see include/mxmoe.h) recorded around the stages on the current stream."""
     T = int(x.shape[0])
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
         workspace = alloc_workspace(layer, T, x.dtype, fp8)
     d = layer.descriptor()
-    o = _opts(x.dtype, fp8, x_scale, h_scale, topk_idx_out, topk_w_out)
+    o = _opts(x.dtype, fp8, x_scale, h_scale, topk_idx_out, topk_w_out, stage_events)
     _check(load_library().moe_mxfp4_forward(ctypes.byref(d), _ptr(x), T, _ptr(out), ctypes.byref(o),
                                             _ptr(workspace), workspace.numel(), _stream(x.device)))
     return out

@@ -101,7 +101,7 @@ T* at(void* base, size_t off) {
 // Router + grouping into the workspace; optional copies for the caller.
 hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act_dtype, const Workspace& w,
                        void* ws, int32_t* idx_out, float* w_out, int32_t* counts_out, int32_t* offsets_out,
-                       int32_t* sorted_buf, int32_t* pos_buf, hipStream_t s) {
+                       int32_t* sorted_buf, int32_t* pos_buf, hipStream_t s, hipEvent_t mid = nullptr) {
   RouteArgs ra{};
   ra.x = x;
   ra.w_r = L->router_w;
@@ -117,6 +117,7 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   ra.wts_out = w_out;
   hipError_t e = launch_route(ra, s);
   if (e != hipSuccess) return e;
+  if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
   PermuteArgs pa{};
   pa.idx = ra.idx;
   pa.n_slots = int(T * L->top_k);
@@ -243,9 +244,13 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
   if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  void* const* ev = o->stage_events;
+  auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
+  if (mark(0) != hipSuccess) return MXMOE_ERR_HIP;
   hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
-                             nullptr, s);
+                             nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr);
   if (e != hipSuccess) return MXMOE_ERR_HIP;
+  if (mark(2) != hipSuccess) return MXMOE_ERR_HIP;
   const int act = fp8 ? ACT_FP8 : (o->act_dtype == MXMOE_BF16 ? ACT_BF16 : ACT_F32);
   const float inv_x = fp8 ? 1.0f / o->x_scale : 1.0f;
   const float inv_h = fp8 ? 1.0f / o->h_scale : 1.0f;
@@ -253,6 +258,7 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
     e = launch_quant_fp8(static_cast<const uint16_t*>(x), T * L->H, inv_x, at<uint8_t>(ws, w.xq), s);
     if (e != hipSuccess) return MXMOE_ERR_HIP;
   }
+  if (mark(3) != hipSuccess) return MXMOE_ERR_HIP;
   const bool prefill = use_prefill(L, T, act);
   GemmArgs g0 = gemm_args(L, w, ws, T, act, 0);
   g0.bsrc = fp8 ? at<void>(ws, w.xq) : x;
@@ -261,9 +267,11 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
     g0.out_inv_scale = inv_h;
   }
   if ((e = launch_moe_gemm(g0, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  if (mark(4) != hipSuccess) return MXMOE_ERR_HIP;
   GemmArgs g1 = gemm_args(L, w, ws, T, act, 1);
   if (fp8) g1.acc_scale = o->h_scale;
   if ((e = launch_moe_gemm(g1, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  if (mark(5) != hipSuccess) return MXMOE_ERR_HIP;
   CombineArgs ca{};
   ca.Y = at<float>(ws, w.y);
   ca.pos = at<int32_t>(ws, w.pos);
@@ -273,7 +281,8 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
   ca.T = int(T);
   ca.H = L->H;
   ca.top_k = L->top_k;
-  return hip_status(launch_combine(ca, s));
+  if ((e = launch_combine(ca, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  return hip_status(mark(6));
 }
 
 mxmoe_status_t moe_mxfp4_route(const mxmoe_layer_t* L, const void* x, int64_t T, const mxmoe_fwd_opts_t* o,
