@@ -64,7 +64,7 @@ class HipEvents:
     def __init__(self, n: int):
         if HipEvents._hip is None:
             hip = ctypes.CDLL("libamdhip64.so")
-            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
             HipEvents._hip = hip
@@ -72,7 +72,8 @@ class HipEvents:
         self.arr = (ctypes.c_void_p * n)()
         for i in range(n):
             h = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+            # device-scope release: a timing marker without a system-wide cache flush
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(h), 0x40000000) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.arr[i] = h
         self.n = n

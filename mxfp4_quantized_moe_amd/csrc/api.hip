@@ -21,7 +21,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Workspace {
-  size_t idx, wts, counts, offsets, active, tile_off, sorted, pos, calib, xq, h, y, total;
+  size_t idx, wts, counts, offsets, active, tile_off, tiles, sorted, sorted_tok, pos, calib, xq, h, y, total;
 };
 
 // Byte offsets of the forward's scratch buffers inside the caller's workspace.
@@ -40,7 +40,10 @@ Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8)
   w.offsets = take(size_t(E + 1) * 4);
   w.active = take(size_t(E + 1) * 4);
   w.tile_off = take(size_t(E + 1) * 4);
+  const size_t active_max = slots < size_t(E) ? slots : size_t(E);
+  w.tiles = take((slots + kPrefillTokens - 1) / kPrefillTokens * 16 + active_max * 16);
   w.sorted = take(slots * 4);
+  w.sorted_tok = take(slots * 4);
   w.pos = take(slots * 4);
   w.calib = take(16);
   w.xq = take(fp8 ? size_t(T) * size_t(H) : 0);
@@ -85,9 +88,16 @@ mxmoe_status_t check_opts(const mxmoe_layer_t* L, const mxmoe_fwd_opts_t* o, boo
   return MXMOE_OK;
 }
 
+// The kernels address each expert's weights, x and the intermediate h
+// through 32-bit range-checked buffer windows below 2^31 bytes.
+constexpr int64_t kMaxWindow = (int64_t(1) << 31) - 1;
+
 mxmoe_status_t check_tokens(const mxmoe_layer_t* L, int64_t T) {
   if (T < 0) return MXMOE_ERR_SHAPE;
   if (T * int64_t(L->top_k) > kMaxSlots) return MXMOE_ERR_SHAPE;
+  const int64_t slots = T * L->top_k;
+  if (T * int64_t(L->H) * 4 > kMaxWindow || slots * int64_t(L->I) * 4 > kMaxWindow) return MXMOE_ERR_SHAPE;
+  if (int64_t(2) * L->I * L->H / 2 > kMaxWindow) return MXMOE_ERR_SHAPE;
   return MXMOE_OK;
 }
 
@@ -126,8 +136,11 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   pa.offsets = at<int32_t>(ws, w.offsets);
   pa.sorted = sorted_buf ? sorted_buf : at<int32_t>(ws, w.sorted);
   pa.pos = pos_buf ? pos_buf : at<int32_t>(ws, w.pos);
+  pa.sorted_tok = at<int32_t>(ws, w.sorted_tok);
+  pa.top_k = L->top_k;
   pa.active = at<int32_t>(ws, w.active);
   pa.tile_off = at<int32_t>(ws, w.tile_off);
+  pa.tiles = at<int4>(ws, w.tiles);
   pa.counts_out = counts_out;
   pa.offsets_out = offsets_out;
   return launch_permute(pa, s);
@@ -141,9 +154,11 @@ GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t
   g.top_k = L->top_k;
   g.E = L->E;
   g.sorted = at<int32_t>(ws, w.sorted);
+  g.sorted_tok = at<int32_t>(ws, w.sorted_tok);
   g.offsets = at<int32_t>(ws, w.offsets);
   g.active = at<int32_t>(ws, w.active);
   g.tile_off = at<int32_t>(ws, w.tile_off);
+  g.tiles = at<int4>(ws, w.tiles);
   const int64_t slots = T * L->top_k;
   g.n_slots = int(slots);
   g.max_active = int(slots < L->E ? slots : L->E);
@@ -156,6 +171,7 @@ GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t
     g.bias = L->gate_up_bias;
     g.R = 2 * L->I;
     g.nb = L->H / 32;
+    g.b_rows = T;
     g.out = at<void>(ws, w.h);
   } else {
     g.wblk = L->down_blocks;
@@ -163,6 +179,7 @@ GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t
     g.bias = L->down_bias;
     g.R = L->H;
     g.nb = L->I / 32;
+    g.b_rows = slots;
     g.bsrc = at<void>(ws, w.h);
     g.out = at<void>(ws, w.y);
   }

@@ -80,6 +80,34 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t w, float scale) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// ----------------------------------------------------------- buffer loads
+//
+// Raw buffer loads with hardware range checking: every dword at or past
+// `bytes` reads as zero.  That turns the tails of the tiles (rows past the
+// matrix, K past the contracting dimension, tokens past the expert's count)
+// into unconditional loads, so the compiler can count outstanding loads
+// exactly instead of draining all of them at each conditional one.  Buffers
+// must be smaller than 2^31 bytes so that kOOB is out of range for all.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+
+// a + b for buffer offsets, staying out of range if either one is.
+__device__ __forceinline__ uint32_t oob_add(uint32_t a, uint32_t b) { return ((a | b) & kOOB) ? kOOB : a + b; }
+
+__device__ __forceinline__ uint4 buf_load_b128(rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // ----------------------------------------------------------------- misc
 
 __device__ __forceinline__ float clamped_swiglu(float gate, float up) {

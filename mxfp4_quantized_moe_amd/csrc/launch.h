@@ -10,10 +10,20 @@ namespace mxmoe {
 // weights, or FP8 activations on the scaled MXFP4 x FP8 instructions.
 enum Act : int { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2 };
 
-// Token-tile height of the prefill grouped GEMM (tokens per workgroup tile).
-constexpr int kPrefillTokens = 64;
-// Rows of a prefill workgroup stripe (4 waves x 64 rows).
-constexpr int kPrefillRows = 256;
+// Tile shape of the prefill grouped GEMM: weight rows per workgroup (4 row
+// groups x 16*RT rows), tokens per workgroup tile, and LDS pipeline stages
+// (128-K chunks in flight + 1).  Overridable at build time for tile sweeps.
+#ifndef MXMOE_PREFILL_ROWS
+#define MXMOE_PREFILL_ROWS 256
+#endif
+#ifndef MXMOE_PREFILL_TOKENS
+#define MXMOE_PREFILL_TOKENS 64
+#endif
+#ifndef MXMOE_PREFILL_STAGES
+#define MXMOE_PREFILL_STAGES 3
+#endif
+constexpr int kPrefillRows = MXMOE_PREFILL_ROWS;
+constexpr int kPrefillTokens = MXMOE_PREFILL_TOKENS;
 
 hipError_t launch_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t nblocks, void* out, bool out_bf16,
                          hipStream_t stream);
@@ -39,9 +49,12 @@ struct PermuteArgs {
   int32_t* counts;      // (E)
   int32_t* offsets;     // (E+1)
   int32_t* sorted;      // (T*k)
+  int32_t* sorted_tok;  // (T*k): token id (slot / top_k) of each sorted row
+  int top_k;
   int32_t* pos;         // (T*k)
   int32_t* active;      // (E + 1): active[0] = count, active[1..] = expert ids ascending
   int32_t* tile_off;    // (E+1): prefix of ceil(count / kPrefillTokens)
+  int4* tiles;          // (tile_off[E]): {expert, first sorted row, tokens, 0} per prefill tile
   int32_t* counts_out;  // optional copies
   int32_t* offsets_out;
 };
@@ -59,10 +72,13 @@ struct GemmArgs {
   int bias_bf16;
   int R, nb, top_k, E;
   const void* bsrc;           // phase 0: x (T, K) act storage; phase 1: h (T*k, K) act storage
+  int64_t b_rows;             // rows of bsrc (T or T*k)
   const int32_t* sorted;      // (T*k) flat slot ids in expert order
+  const int32_t* sorted_tok;  // (T*k) their token ids
   const int32_t* offsets;     // (E+1)
   const int32_t* active;      // (E+1)
   const int32_t* tile_off;    // (E+1)
+  const int4* tiles;          // prefill tile table
   void* out;                  // phase 0: h (T*k, R/2) act storage; phase 1: Y (T*k, R) fp32
   float acc_scale;            // fp8: the static scale of the B operand; else 1
   float out_inv_scale;        // phase 0 fp8: 1 / h_scale

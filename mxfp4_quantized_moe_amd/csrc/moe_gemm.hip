@@ -29,31 +29,54 @@
 // This is a permutation of K applied to both operands, so each dot product
 // is unchanged.  Blocks past K (when K/32 is not a multiple of 4) read as
 // zero on both sides.
+//
+// All tile loads are range-checked buffer loads (see device_common.h): the
+// tails read as zero without branches.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace mxmoe {
 
 constexpr int kDecodeRowTiles = 1;  // 16 weight rows per decode workgroup
-constexpr int kDecodeChunkBuf = 8;  // 128-K chunks kept in flight per wave
+constexpr int kDecodeChunkBuf = 6;  // 128-K chunks in flight per wave
 
 // ------------------------------------------------------------ operands
 
 struct AFrag {
   uint4 q;       // 16 bytes = 32 nibbles of one block of one weight row
-  uint32_t s;    // its e8m0 scale byte
+  uint32_t sw;   // the aligned dword holding its e8m0 scale byte (0 past the tensor)
+  uint32_t sh;   // bit position of that byte in sw
+  // The scale byte is extracted at its use, not right after the load: an
+  // extension next to the load would make every prefetch wait at once.
+  __device__ __forceinline__ uint32_t scale() const { return (sw >> sh) & 0xFFu; }
 };
 
-__device__ __forceinline__ AFrag load_a(const uint8_t* wblk, const uint8_t* wsc, int row, int nb, int block) {
+// Weights of one expert as buffers: blocks (R, nb, 16) and scales (R, nb).
+struct WBuf {
+  rsrc_t blk, sc;
+  int R, nb;
+};
+
+__device__ __forceinline__ WBuf expert_weights(const GemmArgs& a, int e) {
+  WBuf w;
+  const int64_t rb = int64_t(a.R) * a.nb;
+  w.blk = make_rsrc(a.wblk + int64_t(e) * rb * 16, uint32_t(rb * 16));
+  w.sc = make_rsrc(a.wsc + int64_t(e) * rb, uint32_t(rb));
+  w.R = a.R;
+  w.nb = a.nb;
+  return w;
+}
+
+// Block `block` of weight row `row`; zero when either is out of range.
+__device__ __forceinline__ AFrag load_a(const WBuf& w, int row, int block) {
+  const bool ok = row < w.R && block < w.nb;
+  const uint32_t o = uint32_t(row * w.nb + block);
   AFrag f;
-  if (block < nb) {
-    const int64_t o = int64_t(row) * nb + block;
-    f.q = *reinterpret_cast<const uint4*>(wblk + o * 16);
-    f.s = wsc[o];
-  } else {
-    f.q = make_uint4(0, 0, 0, 0);
-    f.s = 127;
-  }
+  f.q = buf_load_b128(w.blk, ok ? o * 16u : kOOB);
+  f.sw = buf_load_b32(w.sc, ok ? (o & ~3u) : kOOB);
+  f.sh = (o & 3u) * 8u;
   return f;
 }
 
@@ -61,17 +84,23 @@ __device__ __forceinline__ uint32_t dword(const uint4& q, int i) {
   return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
 }
 
+// Byte offset of token row j (of n >= 1) of a tile inside bsrc, or kOOB.
+// gate_up gathers x rows by token id; down reads h rows in sorted order.
+// The token-id load is unconditional (clamped index) so it needs no branch.
+__device__ __forceinline__ uint32_t act_row_offset(const GemmArgs& a, int phase, int row_start, int j, int n,
+                                                   uint32_t row_bytes) {
+  const int p = row_start + min(j, n - 1);
+  const int src_row = phase == 0 ? a.sorted_tok[p] : p;
+  return j < n ? uint32_t(src_row) * row_bytes : kOOB;
+}
+
 // ------------------------------------------------------------ epilogue
 
-// Store one lane's 4 accumulator rows (r0 .. r0+3) of one token (sorted row p).
+// Store rows r0 .. r0+3 of one token (sorted row p), bias already added:
+// gate_up applies the SwiGLU and writes h, down writes Y.
 template <int ACT, int PHASE>
-__device__ __forceinline__ void store_rows(const GemmArgs& a, int e, int r0, int64_t p, float v0, float v1, float v2,
-                                           float v3) {
-  const int64_t bo = int64_t(e) * a.R + r0;
-  v0 = v0 * a.acc_scale + load_param(a.bias, bo + 0, a.bias_bf16);
-  v1 = v1 * a.acc_scale + load_param(a.bias, bo + 1, a.bias_bf16);
-  v2 = v2 * a.acc_scale + load_param(a.bias, bo + 2, a.bias_bf16);
-  v3 = v3 * a.acc_scale + load_param(a.bias, bo + 3, a.bias_bf16);
+__device__ __forceinline__ void store_rows_biased(const GemmArgs& a, int r0, int64_t p, float v0, float v1, float v2,
+                                                  float v3) {
   if constexpr (PHASE == 0) {
     // rows r0, r0+1 = (gate, up) of h column r0/2; rows r0+2, r0+3 the next
     const float h0 = clamped_swiglu(v0, v1);
@@ -89,6 +118,28 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, int e, int r0, int
   } else {
     *reinterpret_cast<float4*>(static_cast<float*>(a.out) + p * a.R + r0) = make_float4(v0, v1, v2, v3);
   }
+}
+
+// Scale, add the bias of rows r0 .. r0+3 of expert e, and store.
+template <int ACT, int PHASE>
+__device__ __forceinline__ void store_rows(const GemmArgs& a, int e, int r0, int64_t p, float v0, float v1, float v2,
+                                           float v3) {
+  const int64_t bo = int64_t(e) * a.R + r0;
+  store_rows_biased<ACT, PHASE>(a, r0, p, v0 * a.acc_scale + load_param(a.bias, bo + 0, a.bias_bf16),
+                                v1 * a.acc_scale + load_param(a.bias, bo + 1, a.bias_bf16),
+                                v2 * a.acc_scale + load_param(a.bias, bo + 2, a.bias_bf16),
+                                v3 * a.acc_scale + load_param(a.bias, bo + 3, a.bias_bf16));
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Workgroup barrier that orders LDS traffic only: the global prefetches of
+// later chunks stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // =====================================================================
@@ -115,88 +166,79 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   const int nb = a.nb, K = nb * 32;
   const int nchunks = (nb + 3) >> 2;
   const int rbase = blockIdx.x * (16 * RT);
-  const uint8_t* wblk = a.wblk + int64_t(e) * a.R * nb * 16;
-  const uint8_t* wsc = a.wsc + int64_t(e) * a.R * nb;
+  const WBuf wb = expert_weights(a, e);
   constexpr int EB = ACT == ACT_F32 ? 4 : (ACT == ACT_BF16 ? 2 : 1);  // bytes per B element
-  const uint8_t* bsrc = static_cast<const uint8_t*>(a.bsrc);
+  const uint32_t row_bytes = uint32_t(K) * EB;
+  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
 
   for (int tg = 0; tg < n_e; tg += 64) {
-    // this lane's token row for each of the 4 token sub-tiles
-    const uint8_t* brow[4];
+    // byte offset of this lane's token row for each of the 4 token sub-tiles
+    uint32_t boff[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int j = tg + nt * 16 + r16;
-      brow[nt] = nullptr;
-      if (j < n_e) {
-        const int64_t p = row_start + j;
-        const int64_t src_row = PHASE == 0 ? int64_t(a.sorted[p] / a.top_k) : p;
-        brow[nt] = bsrc + src_row * K * EB;
-      }
-    }
+    for (int nt = 0; nt < 4; ++nt) boff[nt] = act_row_offset(a, PHASE, row_start, tg + nt * 16 + r16, n_e, row_bytes);
     const int nt_active = min(4, (n_e - tg + 15) >> 4);
 
-    f32x4_t acc[RT][4];
+    // specialised on the number of active token sub-tiles: no branches
+    // between the loads and the MFMAs of a chunk group
+    auto pass = [&](auto ntc) __attribute__((always_inline)) {
+      constexpr int NA = decltype(ntc)::value;
+      f32x4_t acc[RT][NA];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = wave; c0 < nchunks; c0 += 4 * kDecodeChunkBuf) {
-      AFrag af[kDecodeChunkBuf][RT];
+      for (int c0 = wave; c0 < nchunks; c0 += 4 * kDecodeChunkBuf) {
+        AFrag af[kDecodeChunkBuf][RT];
 #pragma unroll
-      for (int u = 0; u < kDecodeChunkBuf; ++u) {
-        const int c = c0 + 4 * u;
+        for (int u = 0; u < kDecodeChunkBuf; ++u)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          af[u][rt] = load_a(wblk, wsc, rbase + 16 * rt + r16, nb, c < nchunks ? 4 * c + g : nb);
-      }
+          for (int rt = 0; rt < RT; ++rt) af[u][rt] = load_a(wb, rbase + 16 * rt + r16, 4 * (c0 + 4 * u) + g);
+        // chunks past the end are all zeros (range-checked loads)
 #pragma unroll
-      for (int u = 0; u < kDecodeChunkBuf; ++u) {
-        const int c = c0 + 4 * u;
-        if (c >= nchunks) break;
-        const bool kvalid = 4 * c + g < nb;
-        if constexpr (ACT == ACT_BF16) {
+        for (int u = 0; u < kDecodeChunkBuf; ++u) {
+          const int c = c0 + 4 * u;
+          if constexpr (ACT == ACT_BF16) {
+            const uint32_t kofs = (4 * c + g < nb) ? uint32_t(128 * c + 32 * g) * 2 : kOOB;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            bf16x8_t b[4];
+            for (int s = 0; s < 4; ++s) {
+              bf16x8_t b[NA];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-              uint4 q = make_uint4(0, 0, 0, 0);
-              if (brow[nt] && kvalid) q = *reinterpret_cast<const uint4*>(brow[nt] + (128 * c + 32 * g + 8 * s) * 2);
-              b[nt] = __builtin_bit_cast(bf16x8_t, q);
+              for (int nt = 0; nt < NA; ++nt)
+                b[nt] = __builtin_bit_cast(bf16x8_t, buf_load_b128(bsrc, oob_add(boff[nt], kofs + 16 * s)));
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt) {
+                const bf16x8_t av = fp4x8_to_bf16x8(dword(af[u][rt].q, s), e8m0_as_scale_operand(af[u][rt].scale()));
+#pragma unroll
+                for (int nt = 0; nt < NA; ++nt)
+                  acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nt], acc[rt][nt], 0, 0, 0);
+              }
             }
+          } else if constexpr (ACT == ACT_F32) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-              const bf16x8_t av = fp4x8_to_bf16x8(dword(af[u][rt].q, s), e8m0_as_scale_operand(af[u][rt].s));
+            for (int s4 = 0; s4 < 8; ++s4) {
+              const uint32_t kofs = (4 * c + g < nb) ? uint32_t(128 * c + 32 * g + 4 * s4) * 4 : kOOB;
+              float4 b[NA];
 #pragma unroll
-              for (int nt = 0; nt < 4; ++nt)
-                if (nt < nt_active) acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nt], acc[rt][nt], 0, 0, 0);
-            }
-          }
-        } else if constexpr (ACT == ACT_F32) {
-#pragma unroll
-          for (int s4 = 0; s4 < 8; ++s4) {
-            float4 b[4];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-              b[nt] = make_float4(0.f, 0.f, 0.f, 0.f);
-              if (brow[nt] && kvalid) b[nt] = *reinterpret_cast<const float4*>(brow[nt] + (128 * c + 32 * g + 4 * s4) * 4);
-            }
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-              const uint32_t w = dword(af[u][rt].q, s4 >> 1);
-              const float sc = e8m0_as_scale_operand(af[u][rt].s);
-              f32x2_t lo, hi;
-              if (s4 & 1) {
-                lo = fp4x2_to_f32x2<2>(w, sc);
-                hi = fp4x2_to_f32x2<3>(w, sc);
-              } else {
-                lo = fp4x2_to_f32x2<0>(w, sc);
-                hi = fp4x2_to_f32x2<1>(w, sc);
+              for (int nt = 0; nt < NA; ++nt) {
+                const uint4 q = buf_load_b128(bsrc, oob_add(boff[nt], kofs));
+                b[nt] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z),
+                                    __uint_as_float(q.w));
               }
 #pragma unroll
-              for (int nt = 0; nt < 4; ++nt) {
-                if (nt < nt_active) {
+              for (int rt = 0; rt < RT; ++rt) {
+                const uint32_t w = dword(af[u][rt].q, s4 >> 1);
+                const float sc = e8m0_as_scale_operand(af[u][rt].scale());
+                f32x2_t lo, hi;
+                if (s4 & 1) {
+                  lo = fp4x2_to_f32x2<2>(w, sc);
+                  hi = fp4x2_to_f32x2<3>(w, sc);
+                } else {
+                  lo = fp4x2_to_f32x2<0>(w, sc);
+                  hi = fp4x2_to_f32x2<1>(w, sc);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NA; ++nt) {
                   acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(lo[0], b[nt].x, acc[rt][nt], 0, 0, 0);
                   acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(lo[1], b[nt].y, acc[rt][nt], 0, 0, 0);
                   acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(hi[0], b[nt].z, acc[rt][nt], 0, 0, 0);
@@ -204,43 +246,45 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
                 }
               }
             }
-          }
-        } else {
-          // FP8: B lane group g holds K = 128c + 16g .. +16 and 128c + 64 + 16g .. +16
-          const bool v0 = 4 * c + (g >> 1) < nb;
-          const bool v1 = 4 * c + 2 + (g >> 1) < nb;
-          i32x8_t b[4];
+          } else {
+            // FP8: B lane group g holds K = 128c + 16g .. +16 and 128c + 64 + 16g .. +16
+            const uint32_t k0 = (4 * c + (g >> 1) < nb) ? uint32_t(128 * c + 16 * g) : kOOB;
+            const uint32_t k1 = (4 * c + 2 + (g >> 1) < nb) ? uint32_t(128 * c + 64 + 16 * g) : kOOB;
+            i32x8_t b[NA];
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            uint4 p0 = make_uint4(0, 0, 0, 0), p1 = make_uint4(0, 0, 0, 0);
-            if (brow[nt]) {
-              if (v0) p0 = *reinterpret_cast<const uint4*>(brow[nt] + 128 * c + 16 * g);
-              if (v1) p1 = *reinterpret_cast<const uint4*>(brow[nt] + 128 * c + 64 + 16 * g);
+            for (int nt = 0; nt < NA; ++nt) {
+              const uint4 p0 = buf_load_b128(bsrc, oob_add(boff[nt], k0));
+              const uint4 p1 = buf_load_b128(bsrc, oob_add(boff[nt], k1));
+              b[nt] = i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
             }
-            b[nt] = i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
-          }
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            const uint4 q = af[u][rt].q;
-            const i32x8_t av = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
+            for (int rt = 0; rt < RT; ++rt) {
+              const uint4 q = af[u][rt].q;
+              const i32x8_t av = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              if (nt < nt_active)
+              for (int nt = 0; nt < NA; ++nt)
                 acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b[nt], acc[rt][nt], 4, 0, 0,
-                                                                               int(af[u][rt].s), 0, 127);
+                                                                               int(af[u][rt].scale()), 0, 127);
+            }
           }
         }
       }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NA; ++nt) red[wave][rt][nt][lane] = acc[rt][nt];
+    };
+    switch (nt_active) {
+      case 1: pass(IC<1>{}); break;
+      case 2: pass(IC<2>{}); break;
+      case 3: pass(IC<3>{}); break;
+      default: pass(IC<4>{}); break;
     }
-
-    // fixed-order reduction of the 4 waves' partial sums
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) red[wave][rt][nt][lane] = acc[rt][nt];
     __syncthreads();
+
+    // fixed-order sum of the 4 waves' partial sums; wave w finishes sub-tile w
     {
-      const int nt = wave;  // wave w finishes token sub-tile w
+      const int nt = wave;
       const int j = tg + nt * 16 + r16;
       if (nt < nt_active && j < n_e) {
         const int64_t p = row_start + j;
@@ -260,40 +304,99 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
 
 // =====================================================================
 // Prefill-shaped GEMM: many tokens per expert, bound by the matrix cores.
-// Workgroup tile = 256 weight rows (4 waves x 64 rows) x 64 tokens of one
-// expert.  Activations of each 128-K chunk are staged in LDS (double
-// buffered, rows padded by 16 bytes so the 16 lanes of a lane group hit
-// distinct banks); each wave streams its own 64 weight rows straight into
-// registers (one 128-bit load per row tile per chunk, prefetched a chunk
-// ahead) and decodes them in registers.  The work list is (token tile,
-// row stripe) with the stripe fastest; workgroup ids are remapped so that
-// consecutive items land on the same XCD and share its L2.
+//
+// Workgroup tile = kPrefillRows weight rows x 64 tokens of one expert, K
+// walked in 128-wide chunks, 8 waves = 4 row groups (16*RT rows each) x 2
+// token halves (32 tokens each), two waves per SIMD so that one wave's
+// MFMAs cover the other's LDS reads, decodes and barrier waits.
+//   * Both operands of a chunk travel global -> LDS by the buffer-to-LDS
+//     DMA form of the loads (no registers held while in flight) into a ring
+//     of S stages, so S-1 chunks are in flight while one is computed; one
+//     barrier per chunk publishes a landed stage and frees the one computed
+//     last.
+//   * A (weights): 16 rows x 4 blocks (1 KB) per row tile, the block of each
+//     16-byte piece XOR-swizzled with the row so that the 16 lanes of a lane
+//     group read 16 different bank groups.  Scale bytes go to registers
+//     (one aligned dword per row tile).
+//   * B (activations): 64 gathered token rows of the chunk, pieces
+//     XOR-swizzled by token the same way.
+// The two waves of a row group decode the same weights into bf16 registers
+// right before their MFMAs (the decode is cheap next to the MFMA work it
+// feeds).  The work list is (token tile, row stripe) with the stripe
+// fastest, and workgroup ids are remapped so that consecutive items land on
+// the same XCD and share its L2.  Expert, first row and token count of each
+// tile come from the table the grouping kernel writes.
 // =====================================================================
 
-__device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int tile) {
-  // largest e with tile_off[e] <= tile (tile_off is non-decreasing)
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_off[mid] <= tile)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
+constexpr int kPrefillRT = kPrefillRows / 64;      // row tiles of 16 per row group
+constexpr int kPrefillStages = MXMOE_PREFILL_STAGES;
+constexpr int kPrefillThreads = 512;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, const uint8_t* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_dst), 16, off, 0, 0, 0);
+}
+
+// Compiler-only ordering point for memory operations (emits nothing).  The
+// explicit vmcnt waits count loads per chunk, so the compiler must not mix
+// the loads of two chunks or move a load across a wait.
+__device__ __forceinline__ void order_point() { __asm__ __volatile__("" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  order_point();
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  order_point();
 }
 
 template <int ACT, int PHASE>
-__global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs a) {
   static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "prefill path takes bf16 or fp8 activations");
+  static_assert(kPrefillTokens == 64, "two 32-token halves per tile");
+  constexpr int RT = kPrefillRT, S = kPrefillStages;
   constexpr int EB = ACT == ACT_BF16 ? 2 : 1;
-  constexpr int KB = 128 * EB;  // bytes of one token row per chunk
-  constexpr int LD = KB + 16;   // padded LDS row stride
-  constexpr int PIECES = KB / 16;
-  constexpr int PPT = PIECES / 4;  // 16-byte pieces per thread per chunk
-  __shared__ __align__(16) uint8_t bs[2][64 * LD];
+  constexpr int KB = 128 * EB;                  // bytes of one token row per chunk
+  constexpr int PPR = KB / 16;                  // 16-byte pieces per token row (16 or 8)
+  constexpr int TPL = 64 / PPR;                 // tokens per 1 KB B load (4 or 8)
+  constexpr int NBL = 64 / TPL;                 // B loads per chunk (16 or 8)
+  constexpr int BLOADS = (NBL + 7) / 8;         // B loads per wave per chunk (2 or 1)
+  constexpr int ALOADS = RT / 2;                // A loads per wave per chunk
+  constexpr int A_BYTES = 4 * RT * 1024;        // A region of a stage
+  constexpr int B_BYTES = 64 * KB;              // B region of a stage
+  constexpr int LOADS = ALOADS + RT + BLOADS;   // VMEM instructions per wave per chunk
+  static_assert(RT % 2 == 0, "row tiles split between the two waves of a row group");
+  static_assert(NBL % 8 == 0, "B loads split evenly over the 8 waves");
+  static_assert(S >= 2 && S <= 5, "2..5 stages");
+  // One LDS object per stage and operand: distinct objects let the compiler
+  // see that a DMA into one stage cannot alias reads of another, so it does
+  // not drain the loads in flight before every LDS read.
+  __shared__ __align__(16) uint8_t sA0[A_BYTES], sA1[A_BYTES], sA2[S > 2 ? A_BYTES : 16],
+      sA3[S > 3 ? A_BYTES : 16], sA4[S > 4 ? A_BYTES : 16];
+  __shared__ __align__(16) uint8_t sB0[B_BYTES], sB1[B_BYTES], sB2[S > 2 ? B_BYTES : 16],
+      sB3[S > 3 ? B_BYTES : 16], sB4[S > 4 ? B_BYTES : 16];
+  auto stage_a = [&](auto uc) -> uint8_t* {
+    constexpr int u = decltype(uc)::value;
+    if constexpr (u == 0) return sA0;
+    else if constexpr (u == 1) return sA1;
+    else if constexpr (u == 2) return sA2;
+    else if constexpr (u == 3) return sA3;
+    else return sA4;
+  };
+  auto stage_b = [&](auto uc) -> uint8_t* {
+    constexpr int u = decltype(uc)::value;
+    if constexpr (u == 0) return sB0;
+    else if constexpr (u == 1) return sB1;
+    else if constexpr (u == 2) return sB2;
+    else if constexpr (u == 3) return sB3;
+    else return sB4;
+  };
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = wave >> 1, th = wave & 1;  // row group, token half
   const int g = lane >> 4, r16 = lane & 15;
 
   // XCD-aware remap: hardware places workgroup b on XCD b % 8
@@ -302,129 +405,203 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   const int nstripes = (a.R + kPrefillRows - 1) / kPrefillRows;
   const int tile = item / nstripes, stripe = item - tile * nstripes;
   if (tile >= a.tile_off[a.E]) return;
-  const int e = find_expert(a.tile_off, a.E, tile);
-  const int tok0 = (tile - a.tile_off[e]) * kPrefillTokens;
-  const int row_start = a.offsets[e] + tok0;
-  const int ntok = min(kPrefillTokens, a.offsets[e + 1] - a.offsets[e] - tok0);
-  const int nt_active = (ntok + 15) >> 4;
+  const int4 ti = a.tiles[tile];  // {expert, first sorted row, tokens}
+  const int e = ti.x, row_start = ti.y, ntok = ti.z;
+  const int na = max(0, min(2, (ntok - 32 * th + 15) >> 4));  // active 16-token sub-tiles of this wave
   const int nb = a.nb, K = nb * 32;
   const int nchunks = (nb + 3) >> 2;
-  const int wrow = stripe * kPrefillRows + wave * 64;
-  const int rt_active = max(0, min(4, (a.R - wrow) >> 4));
-  const uint8_t* wblk = a.wblk + int64_t(e) * a.R * nb * 16;
-  const uint8_t* wsc = a.wsc + int64_t(e) * a.R * nb;
+  const int grow = stripe * kPrefillRows + rg * (16 * RT);  // first row of the row group
+  const int rt_active = max(0, min(RT, (a.R - grow) >> 4));
+  const WBuf wb = expert_weights(a, e);
+  const uint32_t row_bytes = uint32_t(K) * EB;
+  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
 
-  // B staging: thread t copies row t/4, pieces (t%4) + 4i
-  const int brow_j = threadIdx.x >> 2, bq = threadIdx.x & 3;
-  const uint8_t* bsrc = nullptr;
-  if (brow_j < ntok) {
-    const int64_t p = row_start + brow_j;
-    const int64_t src_row = PHASE == 0 ? int64_t(a.sorted[p] / a.top_k) : p;
-    bsrc = static_cast<const uint8_t*>(a.bsrc) + src_row * int64_t(K) * EB;
+  // bias of this lane's 4 output rows per row tile (bf16: the parameters
+  // share the activations' dtype), fetched early as one 8-byte load each
+  // (raw bits here; widened only in the epilogue so nothing waits on them)
+  uint2 biasq[RT];
+  {
+    const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r0 = grow + 16 * rt + 4 * g;
+      biasq[rt] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, r0 < a.R ? uint32_t(r0) * 2u : kOOB, 0, 0));
+    }
   }
-  uint4 breg[PPT];
-  auto load_b = [&](int c) {
+
+  // A DMA: wave (rg, th) carries row tiles ALOADS*th + j of its row group;
+  // lane i carries row (i >> 2) of the tile, block slot i & 3.
+  const int a_r = lane >> 2;
+  const int a_blk = (lane & 3) ^ ((a_r >> 2) & 3);
+  // B DMA: the 64 tokens are NBL loads of TPL tokens; wave w carries loads
+  // BLOADS*w .. BLOADS*w + BLOADS-1; lane i carries token TPL*load + i/PPR,
+  // piece slot i%PPR.
+  uint32_t boff[BLOADS];
+  int bpiece[BLOADS];
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int piece = bq + 4 * i;
-      const int kel = 128 * c + piece * (16 / EB);  // first K index of the piece
-      breg[i] = make_uint4(0, 0, 0, 0);
-      if (bsrc && kel < K) breg[i] = *reinterpret_cast<const uint4*>(bsrc + int64_t(kel) * EB);
+  for (int jj = 0; jj < BLOADS; ++jj) {
+    const int tok = TPL * (BLOADS * wave + jj) + lane / PPR;
+    const int slot = lane % PPR;
+    const int p = ACT == ACT_BF16 ? (slot ^ (tok & 15)) : (slot ^ ((tok >> 1) & 7));
+    bpiece[jj] = p;
+    const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
+    boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
+  }
+  uint32_t sw[S][RT];  // scale dwords per stage
+
+  auto issue = [&](int c, auto stc, uint32_t* swd) __attribute__((always_inline)) {
+    uint8_t* sta = stage_a(stc);
+    uint8_t* stb = stage_b(stc);
+#pragma unroll
+    for (int j = 0; j < ALOADS; ++j) {
+      const int rt = ALOADS * th + j;
+      const int row = grow + 16 * rt + a_r;
+      const int blk = 4 * c + a_blk;
+      const bool ok = row < a.R && blk < nb;
+      dma16(wb.blk, ok ? uint32_t(row * nb + blk) * 16u : kOOB, sta + (rg * RT + rt) * 1024);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = grow + 16 * rt + r16;
+      const int blk = 4 * c + g;
+      const bool ok = row < a.R && blk < nb;
+      swd[rt] = buf_load_b32(wb.sc, ok ? (uint32_t(row * nb + blk) & ~3u) : kOOB);
+    }
+#pragma unroll
+    for (int jj = 0; jj < BLOADS; ++jj) {
+      const bool kok = 128 * c + bpiece[jj] * (16 / EB) < K;
+      dma16(bsrc, oob_add(boff[jj], kok ? uint32_t(c) * KB : kOOB), stb + (BLOADS * wave + jj) * 1024);
     }
   };
-  auto store_b = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i)
-      *reinterpret_cast<uint4*>(&bs[buf][brow_j * LD + (bq + 4 * i) * 16]) = breg[i];
+
+  // Barrier between chunks.  The empty asm statements keep the compiler
+  // from moving LDS reads across it; the DMA of the chunk about to be read
+  // was waited for just before (its own vmcnt), so no other wait is needed.
+  auto barrier = [&]() __attribute__((always_inline)) {
+    order_point();
+    __builtin_amdgcn_s_barrier();
+    order_point();
   };
 
-  AFrag acur[4], anext[4];
-  auto load_a4 = [&](AFrag* dst, int c) {
+  auto main_loop = [&](auto ntc) __attribute__((always_inline)) {
+    constexpr int NA = decltype(ntc)::value;  // 0, 1 or 2 active sub-tiles
+    constexpr int NAC = NA > 0 ? NA : 1;
+    f32x4_t acc[RT][NAC];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-      if (rt < rt_active) dst[rt] = load_a(wblk, wsc, wrow + 16 * rt + r16, nb, 4 * c + g);
-  };
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NAC; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  f32x4_t acc[4][4];
+    auto compute = [&](auto stc, const uint32_t* swd, int c) __attribute__((always_inline)) {
+      if constexpr (NA > 0) {
+        const uint8_t* sa = stage_a(stc) + rg * RT * 1024;
+        const uint8_t* sb = stage_b(stc) + th * 32 * KB;
+        uint4 aq[RT];
+        uint32_t ascb[RT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+          aq[rt] = *reinterpret_cast<const uint4*>(sa + rt * 1024 + (r16 * 4 + (g ^ ((r16 >> 2) & 3))) * 16);
+          const uint32_t o = uint32_t((grow + 16 * rt + r16) * nb + 4 * c + g);
+          ascb[rt] = (swd[rt] >> ((o & 3u) * 8u)) & 0xFFu;
+        }
+        if constexpr (ACT == ACT_BF16) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  load_b(0);
-  load_a4(acur, 0);
-  store_b(0);
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_b(c + 1);
-      load_a4(anext, c + 1);
-    }
-    const uint8_t* tileb = bs[buf];
-    if constexpr (ACT == ACT_BF16) {
+          for (int st = 0; st < 4; ++st) {
+            bf16x8_t b[NA];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8_t b[4];
+            for (int nt = 0; nt < NA; ++nt)
+              b[nt] = *reinterpret_cast<const bf16x8_t*>(sb + ((nt * 16 + r16) * 16 + ((4 * g + st) ^ r16)) * 16);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          if (nt < nt_active)
-            b[nt] = *reinterpret_cast<const bf16x8_t*>(tileb + (nt * 16 + r16) * LD + 64 * g + 16 * s);
+            for (int rt = 0; rt < RT; ++rt) {
+              const bf16x8_t av = fp4x8_to_bf16x8(dword(aq[rt], st), e8m0_as_scale_operand(ascb[rt]));
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          if (rt < rt_active) {
-            const bf16x8_t av = fp4x8_to_bf16x8(dword(acur[rt].q, s), e8m0_as_scale_operand(acur[rt].s));
+              for (int nt = 0; nt < NA; ++nt)
+                acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nt], acc[rt][nt], 0, 0, 0);
+            }
+          }
+        } else {
+          i32x8_t b[NA];
+          const int sw8 = (r16 >> 1) & 7;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              if (nt < nt_active) acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nt], acc[rt][nt], 0, 0, 0);
+          for (int nt = 0; nt < NA; ++nt) {
+            const uint8_t* rowp = sb + (nt * 16 + r16) * 128;
+            const uint4 p0 = *reinterpret_cast<const uint4*>(rowp + (g ^ sw8) * 16);
+            const uint4 p1 = *reinterpret_cast<const uint4*>(rowp + ((4 + g) ^ sw8) * 16);
+            b[nt] = i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const i32x8_t av = i32x8_t{int(aq[rt].x), int(aq[rt].y), int(aq[rt].z), int(aq[rt].w), 0, 0, 0, 0};
+#pragma unroll
+            for (int nt = 0; nt < NA; ++nt)
+              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b[nt], acc[rt][nt], 4, 0, 0,
+                                                                             int(ascb[rt]), 0, 127);
           }
         }
       }
-    } else {
-      i32x8_t b[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        if (nt < nt_active) {
-          const uint8_t* r = tileb + (nt * 16 + r16) * LD;
-          const uint4 p0 = *reinterpret_cast<const uint4*>(r + 16 * g);
-          const uint4 p1 = *reinterpret_cast<const uint4*>(r + 64 + 16 * g);
-          b[nt] = i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
-        }
-      }
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        if (rt < rt_active) {
-          const uint4 q = acur[rt].q;
-          const i32x8_t av = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            if (nt < nt_active)
-              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b[nt], acc[rt][nt], 4, 0, 0,
-                                                                             int(acur[rt].s), 0, 127);
-        }
-      }
-    }
-    if (more) {
-      store_b(buf ^ 1);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acur[rt] = anext[rt];
-    }
-    __syncthreads();
-  }
+    };
 
+    // prologue: chunks 0 .. S-2 in flight, issued in chunk order
+    order_point();
+    issue(0, IC<0>{}, sw[0]);
+    order_point();
+    if constexpr (S > 2) issue(1, IC<1>{}, sw[1]);
+    order_point();
+    if constexpr (S > 3) issue(2, IC<2>{}, sw[2]);
+    order_point();
+    if constexpr (S > 4) issue(3, IC<3>{}, sw[3]);
+    order_point();
+
+    // iteration c: wait for chunk c, barrier, refill the stage of chunk c-1
+    // with chunk c+S-1, compute chunk c.  Every iteration issues the same
+    // loads (chunks past the end read as zeros), so the wait count is fixed.
+    auto iteration = [&](int c, auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;  // c % S
+      wait_vmcnt<(S - 2) * LOADS>();
+      barrier();
+      issue(c + S - 1, IC<(u + S - 1) % S>{}, sw[(u + S - 1) % S]);
+      order_point();
+      compute(IC<u>{}, sw[u], c);
+    };
+    int c0 = 0;
+    for (; c0 + S <= nchunks; c0 += S) {
+      iteration(c0 + 0, IC<0>{});
+      iteration(c0 + 1, IC<1>{});
+      if constexpr (S > 2) iteration(c0 + 2, IC<2 % S>{});
+      if constexpr (S > 3) iteration(c0 + 3, IC<3 % S>{});
+      if constexpr (S > 4) iteration(c0 + 4, IC<4 % S>{});
+    }
+    if (c0 + 0 < nchunks) iteration(c0 + 0, IC<0>{});
+    if (c0 + 1 < nchunks) iteration(c0 + 1, IC<1 % S>{});
+    if constexpr (S > 3) if (c0 + 2 < nchunks) iteration(c0 + 2, IC<2 % S>{});
+    if constexpr (S > 4) if (c0 + 3 < nchunks) iteration(c0 + 3, IC<3 % S>{});
+
+    if constexpr (NA > 0) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    if (rt < rt_active) {
+      for (int rt = 0; rt < RT; ++rt) {
+        if (rt < rt_active) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int j = nt * 16 + r16;
-        if (nt < nt_active && j < ntok)
-          store_rows<ACT, PHASE>(a, e, wrow + 16 * rt + 4 * g, row_start + j, acc[rt][nt][0], acc[rt][nt][1],
-                                 acc[rt][nt][2], acc[rt][nt][3]);
+          for (int nt = 0; nt < NA; ++nt) {
+            const int j = 32 * th + nt * 16 + r16;
+            if (j < ntok) {
+              const f32x4_t v = acc[rt][nt];
+              const uint2 q = biasq[rt];
+              store_rows_biased<ACT, PHASE>(a, grow + 16 * rt + 4 * g, row_start + j,
+                                            v[0] * a.acc_scale + __uint_as_float(q.x << 16),
+                                            v[1] * a.acc_scale + __uint_as_float(q.x & 0xFFFF0000u),
+                                            v[2] * a.acc_scale + __uint_as_float(q.y << 16),
+                                            v[3] * a.acc_scale + __uint_as_float(q.y & 0xFFFF0000u));
+            }
+          }
+        }
       }
     }
+  };
+  // the branches run the same loads and barriers; only the MFMA count differs
+  switch (na) {
+    case 0: main_loop(IC<0>{}); break;
+    case 1: main_loop(IC<1>{}); break;
+    default: main_loop(IC<2>{}); break;
   }
 }
 
@@ -435,7 +612,7 @@ static void launch_one(const GemmArgs& a, bool prefill, hipStream_t stream) {
       const int nstripes = (a.R + kPrefillRows - 1) / kPrefillRows;
       int64_t items = int64_t(a.max_tiles) * nstripes;
       items = (items + 7) / 8 * 8;
-      gemm_prefill_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(256), 0, stream>>>(a);
+      gemm_prefill_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
     }
   } else {
     const unsigned gx = unsigned(a.R / (16 * kDecodeRowTiles));

@@ -221,6 +221,7 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) {
   __shared__ int cnt[256];
   __shared__ int off[257];
+  __shared__ int toff[257];
   __shared__ int run_base[256];
   __shared__ int chunk_total[256];
   __shared__ int wcnt[kPermWaves][256];
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) {
         a.offsets[e] = cbase;
         a.counts[e] = c[j];
         a.tile_off[e] = tbase;
+        toff[e] = tbase;
         if (a.counts_out) a.counts_out[e] = c[j];
         if (a.offsets_out) a.offsets_out[e] = cbase;
         if (c[j] > 0) a.active[1 + abase++] = e;
@@ -279,6 +281,14 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) {
     }
   }
   __syncthreads();
+
+  // prefill tile table: expert e owns tiles tile_off[e] .. tile_off[e+1)
+  for (int e = tid; e < E; e += kPermThreads) {
+    const int c = cnt[e];
+    const int t0 = toff[e];
+    for (int j = 0; j * kPrefillTokens < c; ++j)
+      a.tiles[t0 + j] = make_int4(e, off[e] + j * kPrefillTokens, min(kPrefillTokens, c - j * kPrefillTokens), 0);
+  }
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = 0; base < N; base += kPermThreads) {
@@ -314,6 +324,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) {
     if (valid) {
       const int p = off[key] + run_base[key] + wcnt[wave][key] + rank;
       a.sorted[p] = s;
+      a.sorted_tok[p] = s / a.top_k;
       a.pos[s] = p;
     }
     __syncthreads();
