@@ -14,13 +14,13 @@ enum Act : int { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2 };
 // groups x 16*RT rows), tokens per workgroup tile, and LDS pipeline stages
 // (128-K chunks in flight + 1).  Overridable at build time for tile sweeps.
 #ifndef MXMOE_PREFILL_ROWS
-#define MXMOE_PREFILL_ROWS 256
+#define MXMOE_PREFILL_ROWS 512
 #endif
 #ifndef MXMOE_PREFILL_TOKENS
-#define MXMOE_PREFILL_TOKENS 64
+#define MXMOE_PREFILL_TOKENS 128
 #endif
 #ifndef MXMOE_PREFILL_STAGES
-#define MXMOE_PREFILL_STAGES 3
+#define MXMOE_PREFILL_STAGES 2
 #endif
 constexpr int kPrefillRows = MXMOE_PREFILL_ROWS;
 constexpr int kPrefillTokens = MXMOE_PREFILL_TOKENS;

@@ -302,13 +302,15 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   }
 }
 
-// =====================================================================
 // Prefill-shaped GEMM: many tokens per expert, bound by the matrix cores.
 //
-// Workgroup tile = kPrefillRows weight rows x 64 tokens of one expert, K
-// walked in 128-wide chunks, 8 waves = 4 row groups (16*RT rows each) x 2
-// token halves (32 tokens each), two waves per SIMD so that one wave's
-// MFMAs cover the other's LDS reads, decodes and barrier waits.
+// Workgroup tile = kPrefillRows weight rows x 128 tokens of one expert, K
+// walked in 128-wide chunks, 8 waves of 16*RT rows x all 128 tokens each,
+// two waves per SIMD so that one wave's MFMAs cover the other's LDS reads,
+// decodes and barrier waits.  The tile is sized for the bytes a CU can
+// pull from L2: with ~50 outstanding 64-byte misses per CU and ~360-cycle
+// L2 latency a CU streams ~20 GB/s, so the tile must do ~250 flops per
+// byte it fetches (a 256 x 64 tile does ~125 and stalls on memory).
 //   * Both operands of a chunk travel global -> LDS by the buffer-to-LDS
 //     DMA form of the loads (no registers held while in flight) into a ring
 //     of S stages, so S-1 chunks are in flight while one is computed; one
@@ -320,15 +322,15 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
 //     (one aligned dword per row tile).
 //   * B (activations): 64 gathered token rows of the chunk, pieces
 //     XOR-swizzled by token the same way.
-// The two waves of a row group decode the same weights into bf16 registers
-// right before their MFMAs (the decode is cheap next to the MFMA work it
-// feeds).  The work list is (token tile, row stripe) with the stripe
+// Each wave decodes its own weight rows into bf16 registers right before
+// the MFMAs; a wave whose rows all lie past the matrix skips its MFMAs, so
+// a partial last row stripe costs little.  The work list is (token tile, row stripe) with the stripe
 // fastest, and workgroup ids are remapped so that consecutive items land on
 // the same XCD and share its L2.  Expert, first row and token count of each
 // tile come from the table the grouping kernel writes.
 // =====================================================================
 
-constexpr int kPrefillRT = kPrefillRows / 64;      // row tiles of 16 per row group
+constexpr int kPrefillRT = kPrefillRows / 128;      // row tiles of 16 per row group
 constexpr int kPrefillStages = MXMOE_PREFILL_STAGES;
 constexpr int kPrefillThreads = 512;
 
@@ -355,20 +357,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int ACT, int PHASE>
 __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs a) {
   static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "prefill path takes bf16 or fp8 activations");
-  static_assert(kPrefillTokens == 64, "two 32-token halves per tile");
+  static_assert(kPrefillTokens == 128, "eight 16-token sub-tiles per tile");
   constexpr int RT = kPrefillRT, S = kPrefillStages;
   constexpr int EB = ACT == ACT_BF16 ? 2 : 1;
   constexpr int KB = 128 * EB;                  // bytes of one token row per chunk
   constexpr int PPR = KB / 16;                  // 16-byte pieces per token row (16 or 8)
   constexpr int TPL = 64 / PPR;                 // tokens per 1 KB B load (4 or 8)
-  constexpr int NBL = 64 / TPL;                 // B loads per chunk (16 or 8)
-  constexpr int BLOADS = (NBL + 7) / 8;         // B loads per wave per chunk (2 or 1)
-  constexpr int ALOADS = RT / 2;                // A loads per wave per chunk
-  constexpr int A_BYTES = 4 * RT * 1024;        // A region of a stage
-  constexpr int B_BYTES = 64 * KB;              // B region of a stage
-  constexpr int LOADS = ALOADS + RT + BLOADS;   // VMEM instructions per wave per chunk
-  static_assert(RT % 2 == 0, "row tiles split between the two waves of a row group");
-  static_assert(NBL % 8 == 0, "B loads split evenly over the 8 waves");
+  constexpr int NBL = 128 / TPL;                // B loads per chunk (32 or 16)
+  constexpr int BLOADS = NBL / 8;               // B loads per wave per chunk (4 or 2)
+  constexpr int A_BYTES = 8 * RT * 1024;        // A region of a stage
+  constexpr int B_BYTES = 128 * KB;             // B region of a stage
+  constexpr int LOADS = RT + RT + BLOADS;       // VMEM instructions per wave per chunk
   static_assert(S >= 2 && S <= 5, "2..5 stages");
   // One LDS object per stage and operand: distinct objects let the compiler
   // see that a DMA into one stage cannot alias reads of another, so it does
@@ -396,7 +395,6 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = wave >> 1, th = wave & 1;  // row group, token half
   const int g = lane >> 4, r16 = lane & 15;
 
   // XCD-aware remap: hardware places workgroup b on XCD b % 8
@@ -407,11 +405,12 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   if (tile >= a.tile_off[a.E]) return;
   const int4 ti = a.tiles[tile];  // {expert, first sorted row, tokens}
   const int e = ti.x, row_start = ti.y, ntok = ti.z;
-  const int na = max(0, min(2, (ntok - 32 * th + 15) >> 4));  // active 16-token sub-tiles of this wave
+  const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
   const int nb = a.nb, K = nb * 32;
   const int nchunks = (nb + 3) >> 2;
-  const int grow = stripe * kPrefillRows + rg * (16 * RT);  // first row of the row group
+  const int grow = stripe * kPrefillRows + wave * (16 * RT);  // first row of this wave
   const int rt_active = max(0, min(RT, (a.R - grow) >> 4));
+  const bool busy = rt_active > 0;  // wave-uniform
   const WBuf wb = expert_weights(a, e);
   const uint32_t row_bytes = uint32_t(K) * EB;
   const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
@@ -429,11 +428,11 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
     }
   }
 
-  // A DMA: wave (rg, th) carries row tiles ALOADS*th + j of its row group;
-  // lane i carries row (i >> 2) of the tile, block slot i & 3.
+  // A DMA: each wave carries its own RT row tiles; lane i carries row
+  // (i >> 2) of the tile, block slot i & 3.
   const int a_r = lane >> 2;
   const int a_blk = (lane & 3) ^ ((a_r >> 2) & 3);
-  // B DMA: the 64 tokens are NBL loads of TPL tokens; wave w carries loads
+  // B DMA: the 128 tokens are NBL loads of TPL tokens; wave w carries loads
   // BLOADS*w .. BLOADS*w + BLOADS-1; lane i carries token TPL*load + i/PPR,
   // piece slot i%PPR.
   uint32_t boff[BLOADS];
@@ -453,12 +452,11 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
     uint8_t* sta = stage_a(stc);
     uint8_t* stb = stage_b(stc);
 #pragma unroll
-    for (int j = 0; j < ALOADS; ++j) {
-      const int rt = ALOADS * th + j;
+    for (int rt = 0; rt < RT; ++rt) {
       const int row = grow + 16 * rt + a_r;
       const int blk = 4 * c + a_blk;
       const bool ok = row < a.R && blk < nb;
-      dma16(wb.blk, ok ? uint32_t(row * nb + blk) * 16u : kOOB, sta + (rg * RT + rt) * 1024);
+      dma16(wb.blk, ok ? uint32_t(row * nb + blk) * 16u : kOOB, sta + (wave * RT + rt) * 1024);
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -484,18 +482,17 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   };
 
   auto main_loop = [&](auto ntc) __attribute__((always_inline)) {
-    constexpr int NA = decltype(ntc)::value;  // 0, 1 or 2 active sub-tiles
-    constexpr int NAC = NA > 0 ? NA : 1;
-    f32x4_t acc[RT][NAC];
+    constexpr int NA = decltype(ntc)::value;  // 1 .. 8 active sub-tiles
+    f32x4_t acc[RT][NA];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < NAC; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](auto stc, const uint32_t* swd, int c) __attribute__((always_inline)) {
-      if constexpr (NA > 0) {
-        const uint8_t* sa = stage_a(stc) + rg * RT * 1024;
-        const uint8_t* sb = stage_b(stc) + th * 32 * KB;
+      if (busy) {
+        const uint8_t* sa = stage_a(stc) + wave * RT * 1024;
+        const uint8_t* sb = stage_b(stc);
         uint4 aq[RT];
         uint32_t ascb[RT];
 #pragma unroll
@@ -576,13 +573,13 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
     if constexpr (S > 3) if (c0 + 2 < nchunks) iteration(c0 + 2, IC<2 % S>{});
     if constexpr (S > 4) if (c0 + 3 < nchunks) iteration(c0 + 3, IC<3 % S>{});
 
-    if constexpr (NA > 0) {
+    {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         if (rt < rt_active) {
 #pragma unroll
           for (int nt = 0; nt < NA; ++nt) {
-            const int j = 32 * th + nt * 16 + r16;
+            const int j = nt * 16 + r16;
             if (j < ntok) {
               const f32x4_t v = acc[rt][nt];
               const uint2 q = biasq[rt];
@@ -599,9 +596,14 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   };
   // the branches run the same loads and barriers; only the MFMA count differs
   switch (na) {
-    case 0: main_loop(IC<0>{}); break;
     case 1: main_loop(IC<1>{}); break;
-    default: main_loop(IC<2>{}); break;
+    case 2: main_loop(IC<2>{}); break;
+    case 3: main_loop(IC<3>{}); break;
+    case 4: main_loop(IC<4>{}); break;
+    case 5: main_loop(IC<5>{}); break;
+    case 6: main_loop(IC<6>{}); break;
+    case 7: main_loop(IC<7>{}); break;
+    default: main_loop(IC<8>{}); break;
   }
 }
 
