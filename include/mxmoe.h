@@ -59,7 +59,7 @@ typedef enum {
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* mxmoe_status_string(int32_t status);
 
-/* Interface version, bumped on any ABI change (currently 1). */
+/* Interface version, bumped on any ABI change (currently 2). */
 int32_t mxmoe_version(void);
 
 /*
@@ -100,6 +100,50 @@ mxmoe_status_t mxfp4_unpack(const uint8_t* blocks, const uint8_t* scales, int64_
 mxmoe_status_t mxfp4_pack(const void* w, int32_t w_dtype, int64_t rows, int64_t k,
                           uint8_t* blocks, uint8_t* scales, void* stream);
 
+/*
+ * Storage orders of the expert weights.
+ *
+ * MXMOE_LAYOUT_ROWS is the checkpoint order: blocks (mats, rows, k/32, 16)
+ * and scales (mats, rows, k/32), as mxfp4_pack writes them.
+ *
+ * MXMOE_LAYOUT_TILED holds the same bytes regrouped so that the expert
+ * GEMMs read every weight tile as one contiguous piece.  For `mats`
+ * matrices of (rows, k) values, with RG = ceil(rows / 64) row groups, 4*RG
+ * row tiles of 16 rows and NC = ceil(k / 128) chunks of 4 blocks:
+ *   tiled blocks: uint8 [mats][4*RG][NC][64][16].  Entry (m, t, c, s, j)
+ *     with s = 4*r + (b ^ ((r >> 2) & 3)), r in 0..15, b in 0..3, is byte j
+ *     of block 4c+b of row 16t+r of matrix m.
+ *   tiled scales: uint8 [mats][RG][NC][64][4].  Entry (m, q, c, l, i) with
+ *     l = 16*b + r is the scale of row 64q+16i+r, block 4c+b of matrix m.
+ * Positions whose row >= rows or block >= k/32 hold 0 (the value +0 in
+ * every block it pads).  Sizes come from mxfp4_tiled_bytes.
+ */
+typedef enum {
+  MXMOE_LAYOUT_ROWS = 0,
+  MXMOE_LAYOUT_TILED = 1
+} mxmoe_layout_t;
+
+/*
+ * mxfp4_tiled_bytes — byte sizes of the MXMOE_LAYOUT_TILED copy of `mats`
+ * MXFP4 matrices of (rows, k) values.  Host only; nothing is launched.
+ * Errors: mats < 0, rows < 0, k <= 0 or k % 32 != 0 -> MXMOE_ERR_SHAPE;
+ * NULL outputs -> MXMOE_ERR_NULL.
+ */
+mxmoe_status_t mxfp4_tiled_bytes(int64_t mats, int64_t rows, int64_t k, int64_t* blocks_bytes,
+                                 int64_t* scales_bytes);
+
+/*
+ * mxfp4_tile — copy `mats` MXFP4 matrices of (rows, k) values from the
+ * MXMOE_LAYOUT_ROWS order (blocks, scales) into the MXMOE_LAYOUT_TILED
+ * order (tiled_blocks, tiled_scales, sized by mxfp4_tiled_bytes), padding
+ * included.  A one-time step when weights are loaded; the values are not
+ * changed.  The outputs must not overlap the inputs.  Errors as for
+ * mxfp4_tiled_bytes, plus NULL / unaligned pointers.  mats or rows == 0 is
+ * a no-op.
+ */
+mxmoe_status_t mxfp4_tile(const uint8_t* blocks, const uint8_t* scales, int64_t mats, int64_t rows, int64_t k,
+                          uint8_t* tiled_blocks, uint8_t* tiled_scales, void* stream);
+
 /* One MoE layer's parameters, all device pointers (see the file header). */
 typedef struct {
   int32_t E;            /* experts, 1..MXMOE_MAX_EXPERTS */
@@ -107,7 +151,10 @@ typedef struct {
   int32_t I;            /* intermediate size, multiple of 32 */
   int32_t top_k;        /* experts per token, 1..min(E, MXMOE_MAX_TOPK) */
   int32_t param_dtype;  /* dtype of biases and router: MXMOE_BF16 or MXMOE_F32 */
-  int32_t reserved0;
+  int32_t weight_layout; /* mxmoe_layout_t of the four MXFP4 tensors below */
+  /* The shapes below are those of MXMOE_LAYOUT_ROWS; with
+   * MXMOE_LAYOUT_TILED the same tensors are in the tiled order, with
+   * (mats, rows, k) = (E, 2I, H) for gate_up and (E, H, I) for down. */
   const uint8_t* gate_up_blocks; /* (E, 2I, H/32, 16) */
   const uint8_t* gate_up_scales; /* (E, 2I, H/32) */
   const void* gate_up_bias;      /* (E, 2I) param_dtype; added before the SwiGLU */

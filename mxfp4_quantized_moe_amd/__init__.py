@@ -5,6 +5,8 @@ include/mxmoe.h); this package only loads it and marshals torch tensors.
 """
 from .binding import (  # noqa: F401
     EXPORTED,
+    LAYOUT_ROWS,
+    LAYOUT_TILED,
     LIB_PATH,
     MoEWeights,
     MxmoeError,
@@ -14,6 +16,8 @@ from .binding import (  # noqa: F401
     moe_mxfp4_forward,
     moe_mxfp4_route,
     mxfp4_pack,
+    mxfp4_tile,
+    mxfp4_tiled_bytes,
     mxfp4_unpack,
     workspace_bytes,
 )

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
 
 MXMOE_F32 = 0
 MXMOE_BF16 = 1
+LAYOUT_ROWS = 0
+LAYOUT_TILED = 1
 
 STATUS_NAMES = {
     0: "MXMOE_OK",
@@ -37,6 +39,8 @@ EXPORTED = (
     "mxmoe_version",
     "mxfp4_unpack",
     "mxfp4_pack",
+    "mxfp4_tiled_bytes",
+    "mxfp4_tile",
     "moe_mxfp4_workspace_bytes",
     "moe_mxfp4_forward",
     "moe_mxfp4_route",
@@ -57,7 +61,7 @@ class Layer(ctypes.Structure):
         ("I", ctypes.c_int32),
         ("top_k", ctypes.c_int32),
         ("param_dtype", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32),
         ("gate_up_blocks", ctypes.c_void_p),
         ("gate_up_scales", ctypes.c_void_p),
         ("gate_up_bias", ctypes.c_void_p),
@@ -105,6 +109,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_unpack.argtypes = [vp, vp, i64, i64, vp, i32, vp]
     lib.mxfp4_pack.restype = i32
     lib.mxfp4_pack.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    lib.mxfp4_tiled_bytes.restype = i32
+    lib.mxfp4_tiled_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.mxfp4_tile.restype = i32
+    lib.mxfp4_tile.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
     lib.moe_mxfp4_workspace_bytes.restype = sz
     lib.moe_mxfp4_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i64, ctypes.POINTER(FwdOpts)]
     lib.moe_mxfp4_forward.restype = i32
@@ -176,12 +184,33 @@ def mxfp4_pack(w: torch.Tensor):
     return blocks, scales
 
 
+def mxfp4_tiled_bytes(mats: int, rows: int, k: int):
+    """Byte sizes (blocks, scales) of the tiled copy of `mats` (rows, k) MXFP4 matrices."""
+    bb, sb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(load_library().mxfp4_tiled_bytes(mats, rows, k, ctypes.byref(bb), ctypes.byref(sb)))
+    return int(bb.value), int(sb.value)
+
+
+def mxfp4_tile(blocks: torch.Tensor, scales: torch.Tensor):
+    """(mats, rows, nb, 16) blocks + (mats, rows, nb) scales in row order ->
+    flat uint8 (tiled_blocks, tiled_scales) in the tiled order of mxmoe.h."""
+    mats, rows, nb = (int(d) for d in blocks.shape[:3])
+    bb, sb = mxfp4_tiled_bytes(mats, rows, nb * 32)
+    tb = torch.empty(max(bb, 16), dtype=torch.uint8, device=blocks.device)[:bb]
+    ts = torch.empty(max(sb, 16), dtype=torch.uint8, device=blocks.device)[:sb]
+    _check(load_library().mxfp4_tile(_ptr(blocks), _ptr(scales), mats, rows, nb * 32, _ptr(tb), _ptr(ts),
+                                     _stream(blocks.device)))
+    return tb, ts
+
+
 # ----------------------------------------------------------------- layer
 
 
 @dataclass
 class MoEWeights:
-    """Device tensors of one MXFP4 MoE layer (see include/mxmoe.h)."""
+    """Device tensors of one MXFP4 MoE layer (see include/mxmoe.h).  With
+    layout LAYOUT_TILED the four MXFP4 tensors are the flat outputs of
+    mxfp4_tile; the shapes noted are those of LAYOUT_ROWS."""
 
     gate_up_blocks: torch.Tensor  # (E, 2I, H/32, 16) uint8
     gate_up_scales: torch.Tensor  # (E, 2I, H/32) uint8
@@ -192,10 +221,11 @@ class MoEWeights:
     router_w: torch.Tensor  # (E, H)
     router_b: torch.Tensor  # (E,)
     top_k: int
+    layout: int = LAYOUT_ROWS
 
     @property
     def E(self) -> int:
-        return int(self.gate_up_blocks.shape[0])
+        return int(self.router_w.shape[0])
 
     @property
     def H(self) -> int:
@@ -203,11 +233,22 @@ class MoEWeights:
 
     @property
     def I(self) -> int:
-        return int(self.down_blocks.shape[2]) * 32
+        return int(self.gate_up_bias.shape[1]) // 2
+
+    def tiled(self) -> "MoEWeights":
+        """A copy of the layer with its MXFP4 tensors in the tiled order
+        (the GEMM-friendly layout; a one-time step at load)."""
+        if self.layout == LAYOUT_TILED:
+            return self
+        gb, gs = mxfp4_tile(self.gate_up_blocks, self.gate_up_scales)
+        db, ds = mxfp4_tile(self.down_blocks, self.down_scales)
+        return MoEWeights(gb, gs, self.gate_up_bias, db, ds, self.down_bias, self.router_w, self.router_b,
+                          top_k=self.top_k, layout=LAYOUT_TILED)
 
     def descriptor(self) -> Layer:
         return Layer(
-            E=self.E, H=self.H, I=self.I, top_k=self.top_k, param_dtype=_dtype_code(self.router_w.dtype), reserved0=0,
+            E=self.E, H=self.H, I=self.I, top_k=self.top_k, param_dtype=_dtype_code(self.router_w.dtype),
+            weight_layout=self.layout,
             gate_up_blocks=_ptr(self.gate_up_blocks), gate_up_scales=_ptr(self.gate_up_scales),
             gate_up_bias=_ptr(self.gate_up_bias), down_blocks=_ptr(self.down_blocks),
             down_scales=_ptr(self.down_scales), down_bias=_ptr(self.down_bias), router_w=_ptr(self.router_w),

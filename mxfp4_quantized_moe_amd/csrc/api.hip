@@ -15,6 +15,16 @@ using namespace mxmoe;
 
 constexpr int64_t kMaxSlots = int64_t(1) << 26;  // T * top_k limit (grid sizes stay in range)
 constexpr int64_t kMaxDim = int64_t(1) << 20;    // H, I, pack/unpack k
+// One thread per element of the codec kernels' 1-D grids of 256-thread
+// workgroups: the grid's work-item count must stay below 2^32.
+constexpr int64_t kMaxGridItems = (int64_t(1) << 32) - 256;
+
+// Bytes of the tiled copy of `mats` (rows, k) matrices (layout in mxmoe.h).
+void tiled_sizes(int64_t mats, int64_t rows, int64_t k, int64_t* bb, int64_t* sb) {
+  const int64_t rg = (rows + 63) / 64, nc = (k / 32 + 3) / 4;
+  *bb = mats * 4 * rg * nc * 1024;
+  *sb = mats * rg * nc * 256;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -61,6 +71,7 @@ mxmoe_status_t check_layer(const mxmoe_layer_t* L) {
   if (L->H % 32 != 0 || L->I % 32 != 0) return MXMOE_ERR_SHAPE;
   if (L->top_k < 1 || L->top_k > MXMOE_MAX_TOPK || L->top_k > L->E) return MXMOE_ERR_SHAPE;
   if (L->param_dtype != MXMOE_F32 && L->param_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
+  if (L->weight_layout != MXMOE_LAYOUT_ROWS && L->weight_layout != MXMOE_LAYOUT_TILED) return MXMOE_ERR_VALUE;
   const void* ptrs[] = {L->gate_up_blocks, L->gate_up_scales, L->gate_up_bias, L->down_blocks,
                         L->down_scales,    L->down_bias,      L->router_w,     L->router_b};
   for (const void* p : ptrs)
@@ -98,6 +109,11 @@ mxmoe_status_t check_tokens(const mxmoe_layer_t* L, int64_t T) {
   const int64_t slots = T * L->top_k;
   if (T * int64_t(L->H) * 4 > kMaxWindow || slots * int64_t(L->I) * 4 > kMaxWindow) return MXMOE_ERR_SHAPE;
   if (int64_t(2) * L->I * L->H / 2 > kMaxWindow) return MXMOE_ERR_SHAPE;
+  int64_t bb, sb;  // one expert's tiled gate_up (the larger of the two matrices)
+  tiled_sizes(1, int64_t(2) * L->I, L->H, &bb, &sb);
+  if (bb > kMaxWindow) return MXMOE_ERR_SHAPE;
+  tiled_sizes(1, L->H, L->I, &bb, &sb);
+  if (bb > kMaxWindow) return MXMOE_ERR_SHAPE;
   return MXMOE_OK;
 }
 
@@ -165,6 +181,7 @@ GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t
   g.max_tiles = int((slots + kPrefillTokens - 1) / kPrefillTokens + g.max_active);
   g.acc_scale = 1.0f;
   g.out_inv_scale = 1.0f;
+  g.tiled = L->weight_layout == MXMOE_LAYOUT_TILED;
   if (phase == 0) {
     g.wblk = L->gate_up_blocks;
     g.wsc = L->gate_up_scales;
@@ -214,7 +231,7 @@ const char* mxmoe_status_string(int32_t s) {
   }
 }
 
-int32_t mxmoe_version(void) { return 1; }
+int32_t mxmoe_version(void) { return 2; }
 
 mxmoe_status_t mxfp4_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t rows, int64_t k, void* out,
                             int32_t out_dtype, void* stream) {
@@ -224,7 +241,7 @@ mxmoe_status_t mxfp4_unpack(const uint8_t* blocks, const uint8_t* scales, int64_
   if (!blocks || !scales || !out) return MXMOE_ERR_NULL;
   if (!aligned16(blocks) || !aligned16(scales) || !aligned16(out)) return MXMOE_ERR_ALIGN;
   const int64_t nblocks = rows * (k / 32);
-  if (nblocks / (k / 32) != rows || nblocks > (int64_t(1) << 40)) return MXMOE_ERR_SHAPE;
+  if (nblocks / (k / 32) != rows || nblocks > kMaxGridItems) return MXMOE_ERR_SHAPE;
   return hip_status(launch_unpack(blocks, scales, nblocks, out, out_dtype == MXMOE_BF16,
                                   static_cast<hipStream_t>(stream)));
 }
@@ -237,8 +254,34 @@ mxmoe_status_t mxfp4_pack(const void* w, int32_t w_dtype, int64_t rows, int64_t 
   if (!w || !blocks || !scales) return MXMOE_ERR_NULL;
   if (!aligned16(w) || !aligned16(blocks) || !aligned16(scales)) return MXMOE_ERR_ALIGN;
   const int64_t nblocks = rows * (k / 32);
-  if (nblocks / (k / 32) != rows || nblocks > (int64_t(1) << 40)) return MXMOE_ERR_SHAPE;
+  if (nblocks / (k / 32) != rows || nblocks > kMaxGridItems) return MXMOE_ERR_SHAPE;
   return hip_status(launch_pack(w, w_dtype == MXMOE_BF16, nblocks, blocks, scales, static_cast<hipStream_t>(stream)));
+}
+
+mxmoe_status_t mxfp4_tiled_bytes(int64_t mats, int64_t rows, int64_t k, int64_t* blocks_bytes,
+                                 int64_t* scales_bytes) {
+  if (mats < 0 || rows < 0 || k <= 0 || k % 32 != 0 || k > kMaxDim || rows > kMaxDim * 16) return MXMOE_ERR_SHAPE;
+  if (!blocks_bytes || !scales_bytes) return MXMOE_ERR_NULL;
+  int64_t bb, sb;
+  tiled_sizes(1, rows, k, &bb, &sb);
+  if (mats > 0 && bb > (int64_t(1) << 62) / mats) return MXMOE_ERR_SHAPE;
+  *blocks_bytes = bb * mats;
+  *scales_bytes = sb * mats;
+  return MXMOE_OK;
+}
+
+mxmoe_status_t mxfp4_tile(const uint8_t* blocks, const uint8_t* scales, int64_t mats, int64_t rows, int64_t k,
+                          uint8_t* tiled_blocks, uint8_t* tiled_scales, void* stream) {
+  int64_t bb, sb;
+  mxmoe_status_t st = mxfp4_tiled_bytes(mats, rows, k, &bb, &sb);
+  if (st != MXMOE_OK) return st;
+  if (mats == 0 || rows == 0) return MXMOE_OK;
+  if (bb / 16 > kMaxGridItems) return MXMOE_ERR_SHAPE;
+  if (!blocks || !scales || !tiled_blocks || !tiled_scales) return MXMOE_ERR_NULL;
+  if (!aligned16(blocks) || !aligned16(scales) || !aligned16(tiled_blocks) || !aligned16(tiled_scales))
+    return MXMOE_ERR_ALIGN;
+  return hip_status(launch_tile(blocks, scales, mats, int(rows), int(k / 32), tiled_blocks, tiled_scales,
+                                static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_mxfp4_workspace_bytes(const mxmoe_layer_t* L, int64_t T, const mxmoe_fwd_opts_t* o) {

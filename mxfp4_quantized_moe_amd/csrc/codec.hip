@@ -144,4 +144,63 @@ hipError_t launch_pack(const void* w, bool in_bf16, int64_t nblocks, uint8_t* bl
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ tile
+//
+// Row order -> tiled order (declared in mxmoe.h).  A one-time layout step:
+// one thread per 16-byte piece of the tiled blocks and one per dword of the
+// tiled scales, so the writes stream contiguously and the reads gather.
+
+__global__ __launch_bounds__(256) void tile_blocks_kernel(const uint4* __restrict__ blocks, uint4* __restrict__ out,
+                                                          int rows, int nb, int rt4, int nc, int64_t total) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int s = int(i & 63);
+  int64_t p = i >> 6;  // piece (m, t, c)
+  const int c = int(p % nc);
+  p /= nc;
+  const int t = int(p % rt4);
+  const int64_t m = p / rt4;
+  const int r = s >> 2;
+  const int b = (s & 3) ^ ((r >> 2) & 3);  // inverse of the slot swizzle
+  const int row = 16 * t + r, blk = 4 * c + b;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < rows && blk < nb) v = blocks[(m * rows + row) * nb + blk];
+  out[i] = v;
+}
+
+__global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t* __restrict__ scales,
+                                                          uint32_t* __restrict__ out, int rows, int nb, int rg,
+                                                          int nc, int64_t total) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int l = int(i & 63);
+  int64_t p = i >> 6;  // group (m, q, c)
+  const int c = int(p % nc);
+  p /= nc;
+  const int q = int(p % rg);
+  const int64_t m = p / rg;
+  const int b = l >> 4, r = l & 15;
+  const int blk = 4 * c + b;
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 64 * q + 16 * j + r;
+    if (row < rows && blk < nb) v |= uint32_t(scales[(m * rows + row) * nb + blk]) << (8 * j);
+  }
+  out[i] = v;
+}
+
+hipError_t launch_tile(const uint8_t* blocks, const uint8_t* scales, int64_t mats, int rows, int nb,
+                       uint8_t* tiled_blocks, uint8_t* tiled_scales, hipStream_t stream) {
+  const int rg = (rows + 63) / 64, nc = (nb + 3) / 4;
+  const int64_t pieces = mats * int64_t(4 * rg) * nc * 64;  // 16-byte pieces
+  const int64_t words = mats * int64_t(rg) * nc * 64;       // scale dwords
+  if (pieces == 0) return hipSuccess;
+  tile_blocks_kernel<<<dim3(unsigned((pieces + 255) / 256)), dim3(256), 0, stream>>>(
+      reinterpret_cast<const uint4*>(blocks), reinterpret_cast<uint4*>(tiled_blocks), rows, nb, 4 * rg, nc, pieces);
+  tile_scales_kernel<<<dim3(unsigned((words + 255) / 256)), dim3(256), 0, stream>>>(
+      scales, reinterpret_cast<uint32_t*>(tiled_scales), rows, nb, rg, nc, words);
+  return hipGetLastError();
+}
+
 }  // namespace mxmoe

@@ -29,6 +29,9 @@ hipError_t launch_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t n
                          hipStream_t stream);
 hipError_t launch_pack(const void* w, bool in_bf16, int64_t nblocks, uint8_t* blocks, uint8_t* scales,
                        hipStream_t stream);
+// Row order -> tiled order of `mats` (rows, 32*nb) matrices (layout in mxmoe.h).
+hipError_t launch_tile(const uint8_t* blocks, const uint8_t* scales, int64_t mats, int rows, int nb,
+                       uint8_t* tiled_blocks, uint8_t* tiled_scales, hipStream_t stream);
 
 struct RouteArgs {
   const void* x;        // (T, H) act dtype
@@ -66,8 +69,9 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8
 struct GemmArgs {
   int act;                    // Act: 0 f32, 1 bf16, 2 fp8
   int phase;                  // 0 = gate_up + SwiGLU -> h, 1 = down -> Y
-  const uint8_t* wblk;        // (E, R, nb, 16)
-  const uint8_t* wsc;         // (E, R, nb)
+  const uint8_t* wblk;        // (E, R, nb, 16), or the tiled order when `tiled`
+  const uint8_t* wsc;         // (E, R, nb), or the tiled order
+  int tiled;                  // 1: weights in the tiled order of mxfp4_tile
   const void* bias;           // (E, R)
   int bias_bf16;
   int R, nb, top_k, E;

@@ -53,21 +53,40 @@ struct AFrag {
   __device__ __forceinline__ uint32_t scale() const { return (sw >> sh) & 0xFFu; }
 };
 
-// Weights of one expert as buffers: blocks (R, nb, 16) and scales (R, nb).
+// Weights of one expert as buffers.  Row order: blocks (R, nb, 16) and
+// scales (R, nb).  Tiled order (declared in mxmoe.h): rt4 row tiles of 16
+// rows x nc chunks, one 1 KB piece each, in the order the LDS tiles are
+// read; scales in 256-byte groups per 64 rows and chunk, whose dword l
+// holds the scales of lane l for the group's 4 row tiles.
 struct WBuf {
   rsrc_t blk, sc;
   int R, nb;
+  int rt4, nc;  // tiled order only
 };
 
+template <bool TILED>
 __device__ __forceinline__ WBuf expert_weights(const GemmArgs& a, int e) {
   WBuf w;
-  const int64_t rb = int64_t(a.R) * a.nb;
-  w.blk = make_rsrc(a.wblk + int64_t(e) * rb * 16, uint32_t(rb * 16));
-  w.sc = make_rsrc(a.wsc + int64_t(e) * rb, uint32_t(rb));
   w.R = a.R;
   w.nb = a.nb;
+  w.nc = (a.nb + 3) >> 2;
+  w.rt4 = 4 * ((a.R + 63) >> 6);
+  if constexpr (TILED) {
+    const int64_t bb = int64_t(w.rt4) * w.nc * 1024, sb = int64_t(w.rt4 / 4) * w.nc * 256;
+    w.blk = make_rsrc(a.wblk + int64_t(e) * bb, uint32_t(bb));
+    w.sc = make_rsrc(a.wsc + int64_t(e) * sb, uint32_t(sb));
+  } else {
+    const int64_t rb = int64_t(a.R) * a.nb;
+    w.blk = make_rsrc(a.wblk + int64_t(e) * rb * 16, uint32_t(rb * 16));
+    w.sc = make_rsrc(a.wsc + int64_t(e) * rb, uint32_t(rb));
+  }
   return w;
 }
+
+// Slot of block b of row r (both within a 16 x 4 piece) in a 1 KB tile:
+// the block index is XOR-swizzled with the row so that the 16 lanes of a
+// lane group read 16 distinct bank groups.
+__device__ __forceinline__ int piece_slot(int r, int b) { return r * 4 + (b ^ ((r >> 2) & 3)); }
 
 // Block `block` of weight row `row`; zero when either is out of range.
 __device__ __forceinline__ AFrag load_a(const WBuf& w, int row, int block) {
@@ -77,6 +96,17 @@ __device__ __forceinline__ AFrag load_a(const WBuf& w, int row, int block) {
   f.q = buf_load_b128(w.blk, ok ? o * 16u : kOOB);
   f.sw = buf_load_b32(w.sc, ok ? (o & ~3u) : kOOB);
   f.sh = (o & 3u) * 8u;
+  return f;
+}
+
+// Tiled order: lane (g, r16) of row tile t, chunk c (block 4c+g of row
+// 16t + r16); zero past the padded tensor.
+__device__ __forceinline__ AFrag load_a_tiled(const WBuf& w, int t, int c, int r16, int g) {
+  const bool ok = t < w.rt4 && c < w.nc;
+  AFrag f;
+  f.q = buf_load_b128(w.blk, ok ? uint32_t((t * w.nc + c) * 1024 + piece_slot(r16, g) * 16) : kOOB);
+  f.sw = buf_load_b32(w.sc, ok ? uint32_t(((t >> 2) * w.nc + c) * 256 + (16 * g + r16) * 4) : kOOB);
+  f.sh = uint32_t(t & 3) * 8u;
   return f;
 }
 
@@ -152,7 +182,7 @@ __device__ __forceinline__ void lds_barrier() {
 // global memory, where they stay cache-resident.
 // =====================================================================
 
-template <int ACT, int PHASE>
+template <int ACT, int PHASE, bool TILED>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   constexpr int RT = kDecodeRowTiles;
   __shared__ f32x4_t red[4][RT][4][64];
@@ -166,7 +196,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   const int nb = a.nb, K = nb * 32;
   const int nchunks = (nb + 3) >> 2;
   const int rbase = blockIdx.x * (16 * RT);
-  const WBuf wb = expert_weights(a, e);
+  const WBuf wb = expert_weights<TILED>(a, e);
   constexpr int EB = ACT == ACT_F32 ? 4 : (ACT == ACT_BF16 ? 2 : 1);  // bytes per B element
   const uint32_t row_bytes = uint32_t(K) * EB;
   const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
@@ -193,7 +223,12 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
         for (int u = 0; u < kDecodeChunkBuf; ++u)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) af[u][rt] = load_a(wb, rbase + 16 * rt + r16, 4 * (c0 + 4 * u) + g);
+          for (int rt = 0; rt < RT; ++rt) {
+            if constexpr (TILED)
+              af[u][rt] = load_a_tiled(wb, (rbase >> 4) + rt, c0 + 4 * u, r16, g);
+            else
+              af[u][rt] = load_a(wb, rbase + 16 * rt + r16, 4 * (c0 + 4 * u) + g);
+          }
         // chunks past the end are all zeros (range-checked loads)
 #pragma unroll
         for (int u = 0; u < kDecodeChunkBuf; ++u) {
@@ -354,7 +389,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   order_point();
 }
 
-template <int ACT, int PHASE>
+template <int ACT, int PHASE, bool TILED>
 __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs a) {
   static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "prefill path takes bf16 or fp8 activations");
   static_assert(kPrefillTokens == 128, "eight 16-token sub-tiles per tile");
@@ -367,7 +402,9 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   constexpr int BLOADS = NBL / 8;               // B loads per wave per chunk (4 or 2)
   constexpr int A_BYTES = 8 * RT * 1024;        // A region of a stage
   constexpr int B_BYTES = 128 * KB;             // B region of a stage
-  constexpr int LOADS = RT + RT + BLOADS;       // VMEM instructions per wave per chunk
+  constexpr int SLOADS = TILED ? 1 : RT;        // scale dword loads per wave per chunk
+  constexpr int LOADS = RT + SLOADS + BLOADS;   // VMEM instructions per wave per chunk
+  static_assert(!TILED || RT == 1 || RT == 2 || RT == 4, "a wave's row tiles share one scale group");
   static_assert(S >= 2 && S <= 5, "2..5 stages");
   // One LDS object per stage and operand: distinct objects let the compiler
   // see that a DMA into one stage cannot alias reads of another, so it does
@@ -411,7 +448,7 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   const int grow = stripe * kPrefillRows + wave * (16 * RT);  // first row of this wave
   const int rt_active = max(0, min(RT, (a.R - grow) >> 4));
   const bool busy = rt_active > 0;  // wave-uniform
-  const WBuf wb = expert_weights(a, e);
+  const WBuf wb = expert_weights<TILED>(a, e);
   const uint32_t row_bytes = uint32_t(K) * EB;
   const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
 
@@ -446,24 +483,39 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
     const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
     boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
   }
-  uint32_t sw[S][RT];  // scale dwords per stage
+  const int t0 = grow >> 4;  // first row tile of this wave
+  uint32_t sw[S][SLOADS];    // scale dwords per stage
 
   auto issue = [&](int c, auto stc, uint32_t* swd) __attribute__((always_inline)) {
     uint8_t* sta = stage_a(stc);
     uint8_t* stb = stage_b(stc);
+    if constexpr (TILED) {
+      // one contiguous 1 KB piece per row tile, already in LDS order, and
+      // one scale dword per lane covering the wave's row tiles
+      const bool cok = c < wb.nc;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = grow + 16 * rt + a_r;
-      const int blk = 4 * c + a_blk;
-      const bool ok = row < a.R && blk < nb;
-      dma16(wb.blk, ok ? uint32_t(row * nb + blk) * 16u : kOOB, sta + (wave * RT + rt) * 1024);
-    }
+      for (int rt = 0; rt < RT; ++rt) {
+        const bool ok = cok && t0 + rt < wb.rt4;
+        dma16(wb.blk, ok ? uint32_t(((t0 + rt) * wb.nc + c) * 1024 + lane * 16) : kOOB,
+              sta + (wave * RT + rt) * 1024);
+      }
+      const bool sok = cok && t0 < wb.rt4;
+      swd[0] = buf_load_b32(wb.sc, sok ? uint32_t(((t0 >> 2) * wb.nc + c) * 256 + lane * 4) : kOOB);
+    } else {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = grow + 16 * rt + r16;
-      const int blk = 4 * c + g;
-      const bool ok = row < a.R && blk < nb;
-      swd[rt] = buf_load_b32(wb.sc, ok ? (uint32_t(row * nb + blk) & ~3u) : kOOB);
+      for (int rt = 0; rt < RT; ++rt) {
+        const int row = grow + 16 * rt + a_r;
+        const int blk = 4 * c + a_blk;
+        const bool ok = row < a.R && blk < nb;
+        dma16(wb.blk, ok ? uint32_t(row * nb + blk) * 16u : kOOB, sta + (wave * RT + rt) * 1024);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int row = grow + 16 * rt + r16;
+        const int blk = 4 * c + g;
+        const bool ok = row < a.R && blk < nb;
+        swd[rt] = buf_load_b32(wb.sc, ok ? (uint32_t(row * nb + blk) & ~3u) : kOOB);
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < BLOADS; ++jj) {
@@ -497,9 +549,13 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
         uint32_t ascb[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          aq[rt] = *reinterpret_cast<const uint4*>(sa + rt * 1024 + (r16 * 4 + (g ^ ((r16 >> 2) & 3))) * 16);
-          const uint32_t o = uint32_t((grow + 16 * rt + r16) * nb + 4 * c + g);
-          ascb[rt] = (swd[rt] >> ((o & 3u) * 8u)) & 0xFFu;
+          aq[rt] = *reinterpret_cast<const uint4*>(sa + rt * 1024 + piece_slot(r16, g) * 16);
+          if constexpr (TILED) {
+            ascb[rt] = (swd[0] >> (((t0 + rt) & 3) * 8)) & 0xFFu;
+          } else {
+            const uint32_t o = uint32_t((grow + 16 * rt + r16) * nb + 4 * c + g);
+            ascb[rt] = (swd[rt] >> ((o & 3u) * 8u)) & 0xFFu;
+          }
         }
         if constexpr (ACT == ACT_BF16) {
 #pragma unroll
@@ -607,19 +663,27 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   }
 }
 
-template <int ACT, int PHASE>
-static void launch_one(const GemmArgs& a, bool prefill, hipStream_t stream) {
+template <int ACT, int PHASE, bool TILED>
+static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
   if (prefill) {
     if constexpr (ACT != ACT_F32) {
       const int nstripes = (a.R + kPrefillRows - 1) / kPrefillRows;
       int64_t items = int64_t(a.max_tiles) * nstripes;
       items = (items + 7) / 8 * 8;
-      gemm_prefill_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
+      gemm_prefill_kernel<ACT, PHASE, TILED><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
     }
   } else {
     const unsigned gx = unsigned(a.R / (16 * kDecodeRowTiles));
-    gemm_decode_kernel<ACT, PHASE><<<dim3(gx, unsigned(a.max_active)), dim3(256), 0, stream>>>(a);
+    gemm_decode_kernel<ACT, PHASE, TILED><<<dim3(gx, unsigned(a.max_active)), dim3(256), 0, stream>>>(a);
   }
+}
+
+template <int ACT, int PHASE>
+static void launch_one(const GemmArgs& a, bool prefill, hipStream_t stream) {
+  if (a.tiled)
+    launch_layout<ACT, PHASE, true>(a, prefill, stream);
+  else
+    launch_layout<ACT, PHASE, false>(a, prefill, stream);
 }
 
 hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream) {

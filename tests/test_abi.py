@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(B.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mxmoe_version() == 1
+    assert lib.mxmoe_version() == 2
     for s in range(9):
         assert lib.mxmoe_status_string(s)
 
@@ -59,8 +59,33 @@ def test_unpack_pack_validation(lib):
     assert lib.mxfp4_pack(P, 1, 0, 64, P, P, s) == OK
 
 
+def test_tiled_bytes(lib):
+    bb, sb = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    # gpt-oss gate_up: rows 5760 = 90 groups of 64, k 2880 = 90 blocks -> 23 chunks of 4 blocks
+    assert lib.mxfp4_tiled_bytes(2, 5760, 2880, ctypes.byref(bb), ctypes.byref(sb)) == OK
+    assert (bb.value, sb.value) == (2 * 360 * 23 * 1024, 2 * 90 * 23 * 256)
+    # ragged: 70 rows -> 2 groups (8 row tiles), k 96 -> 3 blocks -> 1 chunk
+    assert lib.mxfp4_tiled_bytes(3, 70, 96, ctypes.byref(bb), ctypes.byref(sb)) == OK
+    assert (bb.value, sb.value) == (3 * 8 * 1 * 1024, 3 * 2 * 1 * 256)
+    assert lib.mxfp4_tiled_bytes(0, 70, 96, ctypes.byref(bb), ctypes.byref(sb)) == OK and bb.value == 0
+    assert lib.mxfp4_tiled_bytes(1, 64, 48, ctypes.byref(bb), ctypes.byref(sb)) == SHAPE
+    assert lib.mxfp4_tiled_bytes(-1, 64, 64, ctypes.byref(bb), ctypes.byref(sb)) == SHAPE
+    assert lib.mxfp4_tiled_bytes(1, 64, 64, None, ctypes.byref(sb)) == NULL
+
+
+def test_tile_validation(lib):
+    s = None
+    assert lib.mxfp4_tile(P, P, 2, 64, 48, P, P, s) == SHAPE
+    assert lib.mxfp4_tile(P, P, 2, -3, 64, P, P, s) == SHAPE
+    assert lib.mxfp4_tile(None, P, 2, 64, 64, P, P, s) == NULL
+    assert lib.mxfp4_tile(P, P, 2, 64, 64, P, None, s) == NULL
+    assert lib.mxfp4_tile(P, P + 8, 2, 64, 64, P, P, s) == ALIGN
+    assert lib.mxfp4_tile(P, P, 0, 64, 64, None, None, s) == OK  # nothing to tile: no-op
+    assert lib.mxfp4_tile(P, P, 2, 0, 64, None, None, s) == OK
+
+
 def _layer(**kw):
-    d = dict(E=4, H=64, I=64, top_k=2, param_dtype=1, reserved0=0, gate_up_blocks=P, gate_up_scales=P,
+    d = dict(E=4, H=64, I=64, top_k=2, param_dtype=1, weight_layout=0, gate_up_blocks=P, gate_up_scales=P,
              gate_up_bias=P, down_blocks=P, down_scales=P, down_bias=P, router_w=P, router_b=P)
     d.update(kw)
     return B.Layer(**d)
@@ -86,6 +111,7 @@ def _fwd(lib, layer, T=8, opts=None, x=P, out=P, ws=P, ws_bytes=1 << 30):
     (dict(top_k=5), SHAPE),         # > E
     (dict(E=16, top_k=9), SHAPE),   # > 8
     (dict(param_dtype=3), DTYPE),
+    (dict(weight_layout=2), VALUE),
     (dict(gate_up_blocks=None), NULL),
     (dict(router_b=None), NULL),
     (dict(down_scales=P + 1), ALIGN),

@@ -131,3 +131,22 @@ def test_pack_unpack_roundtrip_20b_gate_up(dev):
     hb, hs = W.torch_to_array(b2), W.torch_to_array(s2)
     assert np.array_equal(hb[canon], b[canon]) and np.array_equal(hs[canon], s[canon])
     assert (~canon).sum() > 0  # non-canonical blocks exist and were re-encoded
+
+
+@pytest.mark.parametrize("mats,rows,nb", [(1, 16, 4), (2, 70, 3), (3, 130, 9), (2, 5760, 90), (4, 2880, 90)])
+def test_tile_matches_layout_reference(dev, mats, rows, nb):
+    """mxfp4_tile is bit-exact against the tiled order's definition, ragged
+    rows and chunks included, and at the 20b gate_up / down shapes."""
+    import torch
+    import mxfp4_quantized_moe_amd as mx
+    from tests import tiled_layout as TL
+
+    note(f"tile mats={mats} rows={rows} nb={nb}")
+    rng = np.random.default_rng(mats * 1000 + rows + nb)
+    blocks = rng.integers(0, 256, (mats, rows, nb, 16), dtype=np.uint8)
+    scales = rng.integers(0, 256, (mats, rows, nb), dtype=np.uint8)
+    tb, ts = mx.mxfp4_tile(W.array_to_torch(blocks, dev), W.array_to_torch(scales, dev))
+    torch.cuda.synchronize()
+    rb, rs = TL.tile(blocks, scales)
+    assert np.array_equal(W.torch_to_array(tb), rb)
+    assert np.array_equal(W.torch_to_array(ts), rs)

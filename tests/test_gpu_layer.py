@@ -25,11 +25,13 @@ def dev():
     return device()
 
 
-def run_gpu(case, dev, x_scale=1.0, h_scale=1.0, want_route=True):
+def run_gpu(case, dev, x_scale=1.0, h_scale=1.0, want_route=True, layout="rows"):
     import torch
     import mxfp4_quantized_moe_amd as mx
 
     wts = W.layer_to_torch(case.layer, dev)
+    if layout == "tiled":
+        wts = wts.tiled()
     x = W.array_to_torch(case.x, dev)
     T, k = case.T, case.layer.top_k
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -86,22 +88,24 @@ def test_tiny_f32(dev):
     check_layer(case, res, tol=1e-4)
 
 
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
 @pytest.mark.parametrize("T", [1, 8, 64])
-def test_decode_20b(dev, T):
+def test_decode_20b(dev, T, layout):
     case = W.decode_20b(T=T)
-    note(case.name)
-    res, _, _ = run_gpu(case, dev)
+    note(f"{case.name} {layout}")
+    res, _, _ = run_gpu(case, dev, layout=layout)
     check_perm(case, res["route"])
     check_layer(case, res)
 
 
-def test_prefill_120b_full_size(dev):
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_prefill_120b_full_size(dev, layout):
     """T=4096 at the 120b shape: routing and grouping for every token, the
     layer output on 12 tokens spread over the batch (the oracle computes
     them one by one; tokens are independent)."""
     case = W.prefill_120b()
-    note(case.name)
-    res, _, _ = run_gpu(case, dev)
+    note(f"{case.name} {layout}")
+    res, _, _ = run_gpu(case, dev, layout=layout)
     check_perm(case, res["route"])
     counts = res["route"][2]
     assert counts.max() > 3 * counts.mean()  # the router bias skews expert load
@@ -109,13 +113,14 @@ def test_prefill_120b_full_size(dev):
     check_layer(case, res, sample=sample)
 
 
-def test_fp8_20b_full_size(dev):
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_fp8_20b_full_size(dev, layout):
     """W-MXFP4 A-FP8 at T=2048: static scales from the 256-token calibration
     batch (the oracle's values, fed to both sides), output on 12 tokens."""
     case = W.fp8_20b()
     s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
-    note(f"{case.name} s_x={s_x} s_h={s_h}")
-    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False)
+    note(f"{case.name} {layout} s_x={s_x} s_h={s_h}")
+    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False, layout=layout)
     sample = np.linspace(0, case.T - 1, 12).astype(int)
     check_layer(case, res, sample=sample, x_scale=s_x, h_scale=s_h)
 
@@ -144,15 +149,17 @@ def test_fp8_calibration_scales(dev):
     (12, 3, 128, 96, 3, 5, "f32"),       # top_k = E
     (13, 1, 64, 32, 1, 9, "bf16"),       # a single expert
     (14, 16, 256, 128, 8, 40, "bf16"),   # top_k = 8
-    (15, 4, 64, 96, 2, 300, "bf16"),     # prefill kernels, R = 192 < one 256-row stripe
+    (15, 4, 64, 96, 2, 300, "bf16"),     # prefill kernels, R = 192 < one 512-row stripe
     (16, 6, 160, 352, 2, 777, "bf16"),   # prefill: ragged token tiles, K/32 = 5 and 11
     (17, 2, 32, 32, 1, 200, "bf16"),     # smallest dims through prefill
     (18, 4, 64, 64, 2, 130, "f32"),      # fp32 with more than 64 tokens per expert
+    (19, 4, 96, 544, 2, 600, "bf16"),    # prefill: gate_up R = 1088 (2 stripes + a ragged third)
 ])
-def test_small_shapes(dev, seed, E, H, I, k, T, act):
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_small_shapes(dev, seed, E, H, I, k, T, act, layout):
     case = W.small_case(seed, E, H, I, k, T, act_dtype=act)
-    note(case.name)
-    res, _, _ = run_gpu(case, dev)
+    note(f"{case.name} {layout}")
+    res, _, _ = run_gpu(case, dev, layout=layout)
     check_perm(case, res["route"])
     check_layer(case, res, tol=1e-4 if act == "f32" else None)
 
@@ -161,11 +168,12 @@ def test_small_shapes(dev, seed, E, H, I, k, T, act):
     (20, 4, 64, 64, 2, 16),     # decode-shaped
     (21, 4, 96, 160, 2, 400),   # prefill-shaped with partial chunks
 ])
-def test_small_fp8(dev, seed, E, H, I, k, T):
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_small_fp8(dev, seed, E, H, I, k, T, layout):
     case = W.small_case(seed, E, H, I, k, T, act_dtype="bf16", fp8=True)
     s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
-    note(f"{case.name} fp8")
-    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False)
+    note(f"{case.name} fp8 {layout}")
+    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False, layout=layout)
     check_layer(case, res, x_scale=s_x, h_scale=s_h)
 
 
