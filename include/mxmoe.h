@@ -178,7 +178,9 @@ typedef struct {
    * FP8 quantisation of x, gate_up + SwiGLU, down, combine) and the last one
    * after the combine, so stage i takes elapsed(event i, event i+1).  A
    * stage that does not run records its event at the same point as the
-   * next.  NULL records nothing. */
+   * next.  NULL records nothing, and a NULL entry skips that one event:
+   * each record takes a few microseconds of stream time, so a caller timing
+   * one stage passes only the two handles around it. */
   void* const* stage_events;
 } mxmoe_fwd_opts_t;
 

@@ -305,7 +305,7 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* const* ev = o->stage_events;
-  auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
+  auto mark = [&](int i) { return ev && ev[i] ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   if (mark(0) != hipSuccess) return MXMOE_ERR_HIP;
   hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
                              nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr);

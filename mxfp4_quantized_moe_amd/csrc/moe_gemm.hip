@@ -39,8 +39,17 @@
 
 namespace mxmoe {
 
-constexpr int kDecodeRowTiles = 1;  // 16 weight rows per decode workgroup
-constexpr int kDecodeChunkBuf = 6;  // 128-K chunks in flight per wave
+// Decode tile: row tiles of 16 weight rows per workgroup, and 128-K chunks
+// whose weight loads each wave keeps in flight.  Overridable at build time
+// for sweeps.
+#ifndef MXMOE_DECODE_ROW_TILES
+#define MXMOE_DECODE_ROW_TILES 1
+#endif
+#ifndef MXMOE_DECODE_CHUNKS
+#define MXMOE_DECODE_CHUNKS 6
+#endif
+constexpr int kDecodeRowTiles = MXMOE_DECODE_ROW_TILES;
+constexpr int kDecodeChunkBuf = MXMOE_DECODE_CHUNKS;
 
 // ------------------------------------------------------------ operands
 
@@ -325,11 +334,13 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
         const int64_t p = row_start + j;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          f32x4_t s = red[0][rt][nt][lane];
-          s += red[1][rt][nt][lane];
-          s += red[2][rt][nt][lane];
-          s += red[3][rt][nt][lane];
-          store_rows<ACT, PHASE>(a, e, rbase + 16 * rt + 4 * g, p, s[0], s[1], s[2], s[3]);
+          if (rbase + 16 * rt < a.R) {  // R is a multiple of 16
+            f32x4_t s = red[0][rt][nt][lane];
+            s += red[1][rt][nt][lane];
+            s += red[2][rt][nt][lane];
+            s += red[3][rt][nt][lane];
+            store_rows<ACT, PHASE>(a, e, rbase + 16 * rt + 4 * g, p, s[0], s[1], s[2], s[3]);
+          }
         }
       }
     }
@@ -673,7 +684,7 @@ static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
       gemm_prefill_kernel<ACT, PHASE, TILED><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
     }
   } else {
-    const unsigned gx = unsigned(a.R / (16 * kDecodeRowTiles));
+    const unsigned gx = unsigned((a.R + 16 * kDecodeRowTiles - 1) / (16 * kDecodeRowTiles));
     gemm_decode_kernel<ACT, PHASE, TILED><<<dim3(gx, unsigned(a.max_active)), dim3(256), 0, stream>>>(a);
   }
 }

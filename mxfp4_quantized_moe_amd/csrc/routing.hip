@@ -17,71 +17,77 @@ namespace mxmoe {
 
 // ------------------------------------------------------------------ router
 //
-// One workgroup (4 waves) per 16 tokens.  The logits^T tile (E x 16) is an
-// MFMA product with A = W_r rows (experts) and B = x rows (tokens); the 4
-// waves split the contracting dimension into interleaved 128-wide chunks and
-// their partial sums are added in a fixed order in LDS, so the logits are
-// deterministic.  Inside a chunk, lane group g (lanes 16g..16g+15) of the
+// One workgroup per 16 tokens.  The logits^T tile (E x 16) is an MFMA
+// product with A = W_r rows (experts) and B = x rows (tokens); the KW waves
+// of the workgroup split the contracting dimension into interleaved
+// 128-wide chunks and their partial sums are added in a fixed order in LDS,
+// so the logits are deterministic.  KW = 4 when there are many token
+// groups; a decode-sized batch (few groups) uses 16 waves so that the chain
+// of dependent weight loads per wave stays short.  Inside a chunk, lane group g (lanes 16g..16g+15) of the
 // MFMA covers K = 128c + 32g + [0, 32): the same permutation of K is applied
 // to both operands, which leaves the dot products unchanged.
 
 constexpr int kRouteTokens = 16;
-constexpr int kMaxRowTiles = 16;  // E <= 256
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  extern __shared__ float part[];  // [4][16][E]
+// RG row tiles of 16 experts have their loads issued together, NG groups
+// cover E <= 16 * RG * NG.
+template <bool BF16, int RG, int NG, int KW>
+__global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
+  extern __shared__ float part[];  // [KW][16][E]
+  constexpr int EB = BF16 ? 2 : 4;          // bytes per element of x and W_r
+  constexpr int XL = BF16 ? 4 : 8;          // 16-byte loads per lane per row and chunk
+  constexpr int MRT = RG * NG;              // row tiles held in registers
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int E = a.E, H = a.H;
   const int t0 = blockIdx.x * kRouteTokens;
   const int tok = t0 + r16;
-  const bool tok_ok = tok < a.T;
   const int nrt = (E + 15) >> 4;
   const int nchunks = (H + 127) >> 7;
+  const uint32_t row_bytes = uint32_t(H) * EB;
+  // range-checked windows: lanes past T or E, and K past H, read zeros
+  const rsrc_t xs = make_rsrc(a.x, uint32_t(a.T) * row_bytes);
+  const rsrc_t wsrc = make_rsrc(a.w_r, uint32_t(E) * row_bytes);
+  const uint32_t xrow = tok < a.T ? uint32_t(tok) * row_bytes : kOOB;
 
-  f32x4_t acc[kMaxRowTiles];
+  f32x4_t acc[MRT];
 #pragma unroll
-  for (int rt = 0; rt < kMaxRowTiles; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < MRT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = wave; c < nchunks; c += 4) {
+  for (int c = wave; c < nchunks; c += KW) {
     const int kb = 128 * c + 32 * g;  // start of this lane group's 32 K values
-    const bool k_ok = kb < H;
-    if constexpr (BF16) {
-      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + int64_t(tok) * H + kb;
-      const uint16_t* wr = static_cast<const uint16_t*>(a.w_r);
+    const uint32_t kofs = kb < H ? uint32_t(kb) * EB : kOOB;
+    // every load of the chunk is issued before its first MFMA
+    uint4 xq[XL];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint4 bq = make_uint4(0, 0, 0, 0);
-        if (tok_ok && k_ok) bq = *reinterpret_cast<const uint4*>(xr + 8 * s);
-        bf16x8_t b = __builtin_bit_cast(bf16x8_t, bq);
+    for (int s = 0; s < XL; ++s) xq[s] = buf_load_b128(xs, oob_add(xrow, oob_add(kofs, 16u * s)));
 #pragma unroll
-        for (int rt = 0; rt < kMaxRowTiles; ++rt) {
-          if (rt < nrt) {
-            const int e = rt * 16 + r16;
-            uint4 aq = make_uint4(0, 0, 0, 0);
-            if (e < E && k_ok) aq = *reinterpret_cast<const uint4*>(wr + int64_t(e) * H + kb + 8 * s);
-            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aq), b, acc[rt], 0, 0, 0);
-          }
+    for (int grp = 0; grp < NG; ++grp) {
+      if (grp * RG < nrt) {  // uniform across the workgroup
+        uint4 wq[RG][XL];
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          const int e = (grp * RG + r) * 16 + r16;
+          const uint32_t wrow = e < E ? uint32_t(e) * row_bytes : kOOB;
+#pragma unroll
+          for (int s = 0; s < XL; ++s) wq[r][s] = buf_load_b128(wsrc, oob_add(wrow, oob_add(kofs, 16u * s)));
         }
-      }
-    } else {
-      const float* xr = static_cast<const float*>(a.x) + int64_t(tok) * H + kb;
-      const float* wr = static_cast<const float*>(a.w_r);
 #pragma unroll
-      for (int s4 = 0; s4 < 8; ++s4) {
-        float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tok_ok && k_ok) bq = *reinterpret_cast<const float4*>(xr + 4 * s4);
+        for (int r = 0; r < RG; ++r) {
+          f32x4_t& ac = acc[grp * RG + r];
+          if constexpr (BF16) {
 #pragma unroll
-        for (int rt = 0; rt < kMaxRowTiles; ++rt) {
-          if (rt < nrt) {
-            const int e = rt * 16 + r16;
-            float4 aq = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < E && k_ok) aq = *reinterpret_cast<const float4*>(wr + int64_t(e) * H + kb + 4 * s4);
-            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.x, bq.x, acc[rt], 0, 0, 0);
-            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.y, bq.y, acc[rt], 0, 0, 0);
-            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.z, bq.z, acc[rt], 0, 0, 0);
-            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.w, bq.w, acc[rt], 0, 0, 0);
+            for (int s = 0; s < XL; ++s)
+              ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wq[r][s]),
+                                                           __builtin_bit_cast(bf16x8_t, xq[s]), ac, 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int s = 0; s < XL; ++s) {
+              ac = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(wq[r][s].x), __uint_as_float(xq[s].x), ac, 0, 0, 0);
+              ac = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(wq[r][s].y), __uint_as_float(xq[s].y), ac, 0, 0, 0);
+              ac = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(wq[r][s].z), __uint_as_float(xq[s].z), ac, 0, 0, 0);
+              ac = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(wq[r][s].w), __uint_as_float(xq[s].w), ac, 0, 0, 0);
+            }
           }
         }
       }
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   // rt*16 + 4g + i for token r16
   float* mine = part + (wave * kRouteTokens + r16) * E;
 #pragma unroll
-  for (int rt = 0; rt < kMaxRowTiles; ++rt) {
+  for (int rt = 0; rt < MRT; ++rt) {
     if (rt < nrt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -103,19 +109,16 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
   const int tile = kRouteTokens * E;
-  for (int j = threadIdx.x; j < tile; j += 256) {
+  for (int j = threadIdx.x; j < tile; j += 64 * KW) {
     const int e = j % E;
     float s = part[j];
-    s += part[tile + j];
-    s += part[2 * tile + j];
-    s += part[3 * tile + j];
+    for (int w = 1; w < KW; ++w) s += part[w * tile + j];
     part[j] = s + load_param(a.b_r, e, a.act_bf16);
   }
   __syncthreads();
 
-  // top-k + softmax: wave w handles tokens 4w .. 4w+3 of the tile
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tl = wave * 4 + tt;
+  // top-k + softmax: wave w handles tokens w, w + KW, ... of the tile
+  for (int tl = wave; tl < kRouteTokens; tl += KW) {
     const int t = t0 + tl;
     if (t >= a.T) break;
     const float* lg = part + tl * E;
@@ -182,14 +185,37 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   }
 }
 
+template <bool BF16, int KW>
+static void launch_route_typed(const RouteArgs& a, unsigned grid, hipStream_t stream) {
+  const size_t lds = size_t(KW) * kRouteTokens * a.E * sizeof(float);
+  const dim3 g(grid), b(64 * KW);
+  // register tiles sized to E (fp32 operands take twice the registers)
+  if (a.E <= 32)
+    route_kernel<BF16, 2, 1, KW><<<g, b, lds, stream>>>(a);
+  else if (a.E <= 64)
+    route_kernel<BF16, 4, 1, KW><<<g, b, lds, stream>>>(a);
+  else if (a.E <= 128)
+    route_kernel<BF16, (BF16 ? 8 : 4), (BF16 ? 1 : 2), KW><<<g, b, lds, stream>>>(a);
+  else if constexpr (KW == 4)  // E > 128 always takes 4 waves (LDS bound)
+    route_kernel<BF16, 4, 4, KW><<<g, b, lds, stream>>>(a);
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   const unsigned grid = unsigned((a.T + kRouteTokens - 1) / kRouteTokens);
-  const size_t lds = size_t(4) * kRouteTokens * a.E * sizeof(float);
-  if (a.act_bf16)
-    route_kernel<true><<<dim3(grid), dim3(256), lds, stream>>>(a);
-  else
-    route_kernel<false><<<dim3(grid), dim3(256), lds, stream>>>(a);
+  // few token groups: more waves split K (shorter chains of dependent
+  // loads per wave); many groups: 4 waves each, several groups per CU.
+  // The LDS of the partial logits, KW x 16 x E floats, stays <= 64 KB.
+  if (grid < 64 && a.E <= 64) {
+    if (a.act_bf16) launch_route_typed<true, 16>(a, grid, stream);
+    else launch_route_typed<false, 16>(a, grid, stream);
+  } else if (grid < 64 && a.E <= 128) {
+    if (a.act_bf16) launch_route_typed<true, 8>(a, grid, stream);
+    else launch_route_typed<false, 8>(a, grid, stream);
+  } else {
+    if (a.act_bf16) launch_route_typed<true, 4>(a, grid, stream);
+    else launch_route_typed<false, 4>(a, grid, stream);
+  }
   return hipGetLastError();
 }
 

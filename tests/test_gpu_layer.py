@@ -154,6 +154,9 @@ def test_fp8_calibration_scales(dev):
     (17, 2, 32, 32, 1, 200, "bf16"),     # smallest dims through prefill
     (18, 4, 64, 64, 2, 130, "f32"),      # fp32 with more than 64 tokens per expert
     (19, 4, 96, 544, 2, 600, "bf16"),    # prefill: gate_up R = 1088 (2 stripes + a ragged third)
+    (22, 100, 64, 64, 4, 20, "bf16"),    # router: 65 <= E <= 128 with few tokens (8 K-splitting waves)
+    (23, 256, 64, 32, 8, 40, "bf16"),    # router: E = 256 (largest), top_k = 8
+    (24, 200, 96, 64, 3, 70, "f32"),     # router: fp32 with E > 128
 ])
 @pytest.mark.parametrize("layout", ["rows", "tiled"])
 def test_small_shapes(dev, seed, E, H, I, k, T, act, layout):
