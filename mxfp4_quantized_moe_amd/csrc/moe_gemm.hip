@@ -445,12 +445,18 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
 
-  // XCD-aware remap: hardware places workgroup b on XCD b % 8
-  const int G = gridDim.x;  // multiple of 8
-  const int item = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  // Work items (token tile, row stripe), stripe fastest.  The grid is sized
+  // for the most tiles a routing can produce; the valid items are the first
+  // nvalid.  Hardware places workgroup b on XCD b % 8, so XCD x takes the
+  // x-th eighth of the valid items, in order: every XCD gets an even share
+  // and the stripes of one token tile run on one XCD, sharing its L2.
   const int nstripes = (a.R + kPrefillRows - 1) / kPrefillRows;
+  const int nvalid = a.tile_off[a.E] * nstripes;
+  const int per_xcd = (nvalid + 7) >> 3;
+  const int idx = blockIdx.x >> 3;
+  const int item = (blockIdx.x & 7) * per_xcd + idx;
+  if (idx >= per_xcd || item >= nvalid) return;
   const int tile = item / nstripes, stripe = item - tile * nstripes;
-  if (tile >= a.tile_off[a.E]) return;
   const int4 ti = a.tiles[tile];  // {expert, first sorted row, tokens}
   const int e = ti.x, row_start = ti.y, ntok = ti.z;
   const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
@@ -675,6 +681,249 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
 }
 
 // =====================================================================
+// Prefill-shaped GEMM on the tiled weight order.
+//
+// Same workgroup tile as above (kPrefillRows rows x 128 tokens, 8 waves of
+// 64 rows x 128 tokens), but a wave's weight rows are its own, so they skip
+// LDS: each chunk's four 1 KB pieces (already in MFMA lane order) and its
+// scale dword load straight into registers.  Only the token tile, which
+// all 8 waves read, goes through LDS (buffer-to-LDS DMA), which leaves room
+// for S stages: S-1 chunks of weights and tokens stay in flight while one
+// is computed.
+// =====================================================================
+
+// (FP8 token fragments take twice the registers of bf16 ones: one stage
+// fewer keeps that variant free of spills)
+#ifndef MXMOE_PREFILL_TILED_STAGES
+#define MXMOE_PREFILL_TILED_STAGES 3
+#endif
+#ifndef MXMOE_PREFILL_TILED_STAGES_FP8
+#define MXMOE_PREFILL_TILED_STAGES_FP8 2
+#endif
+
+template <int ACT, int PHASE>
+__global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_tiled_kernel(GemmArgs a) {
+  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "prefill path takes bf16 or fp8 activations");
+  static_assert(kPrefillTokens == 128, "eight 16-token sub-tiles per tile");
+  static_assert(kPrefillRows == 512, "8 waves of 4 row tiles: one scale group per wave");
+  constexpr int RT = 4, S = ACT == ACT_BF16 ? MXMOE_PREFILL_TILED_STAGES : MXMOE_PREFILL_TILED_STAGES_FP8;
+  constexpr int EB = ACT == ACT_BF16 ? 2 : 1;
+  constexpr int KB = 128 * EB;                  // bytes of one token row per chunk
+  constexpr int PPR = KB / 16;                  // 16-byte pieces per token row (16 or 8)
+  constexpr int TPL = 64 / PPR;                 // tokens per 1 KB B load (4 or 8)
+  constexpr int NBL = 128 / TPL;                // B loads per chunk (32 or 16)
+  constexpr int BLOADS = NBL / 8;               // B loads per wave per chunk (4 or 2)
+  constexpr int B_BYTES = 128 * KB;             // B stage
+  constexpr int LOADS = RT + 1 + BLOADS;        // VMEM instructions per wave per chunk
+  static_assert(S >= 2 && S <= 4, "2..4 stages");
+  static_assert((S - 2) * LOADS < 64, "vmcnt range");
+  __shared__ __align__(16) uint8_t sB0[B_BYTES], sB1[B_BYTES], sB2[S > 2 ? B_BYTES : 16], sB3[S > 3 ? B_BYTES : 16];
+  auto stage_b = [&](auto uc) -> uint8_t* {
+    constexpr int u = decltype(uc)::value;
+    if constexpr (u == 0) return sB0;
+    else if constexpr (u == 1) return sB1;
+    else if constexpr (u == 2) return sB2;
+    else return sB3;
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+
+  // Work items (token tile, row stripe), stripe fastest.  The grid is sized
+  // for the most tiles a routing can produce; the valid items are the first
+  // nvalid.  Hardware places workgroup b on XCD b % 8, so XCD x takes the
+  // x-th eighth of the valid items, in order: every XCD gets an even share
+  // and the stripes of one token tile run on one XCD, sharing its L2.
+  const int nstripes = (a.R + kPrefillRows - 1) / kPrefillRows;
+  const int nvalid = a.tile_off[a.E] * nstripes;
+  const int per_xcd = (nvalid + 7) >> 3;
+  const int idx = blockIdx.x >> 3;
+  const int item = (blockIdx.x & 7) * per_xcd + idx;
+  if (idx >= per_xcd || item >= nvalid) return;
+  const int tile = item / nstripes, stripe = item - tile * nstripes;
+  const int4 ti = a.tiles[tile];  // {expert, first sorted row, tokens}
+  const int e = ti.x, row_start = ti.y, ntok = ti.z;
+  const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
+  const int nb = a.nb, K = nb * 32;
+  const WBuf wb = expert_weights<true>(a, e);
+  const int nc = wb.nc;
+  const int grow = stripe * kPrefillRows + wave * (16 * RT);  // first row of this wave
+  const int t0 = grow >> 4;                                   // its first row tile (a scale group start)
+  const int rt_active = max(0, min(RT, (a.R - grow) >> 4));
+  const bool busy = rt_active > 0;  // wave-uniform
+  const bool wok = t0 < wb.rt4;
+  const uint32_t row_bytes = uint32_t(K) * EB;
+  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
+  const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
+
+  // B DMA: the 128 tokens are NBL loads of TPL tokens; wave w carries loads
+  // BLOADS*w .. BLOADS*w + BLOADS-1; lane i carries token TPL*load + i/PPR,
+  // piece slot i%PPR, XOR-swizzled by token.
+  // (clast: the last chunk whose part of this piece lies inside K)
+  uint32_t boff[BLOADS];
+  int clast[BLOADS];
+#pragma unroll
+  for (int jj = 0; jj < BLOADS; ++jj) {
+    const int tok = TPL * (BLOADS * wave + jj) + lane / PPR;
+    const int slot = lane % PPR;
+    const int p = ACT == ACT_BF16 ? (slot ^ (tok & 15)) : (slot ^ ((tok >> 1) & 7));
+    clast[jj] = (K - 1 - p * (16 / EB)) >> 7;
+    const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
+    boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
+  }
+  uint4 aq[S][RT];   // weight pieces per stage
+  uint32_t sw[S];    // scale dword per stage
+
+  auto issue = [&](int c, auto stc) __attribute__((always_inline)) {
+    constexpr int u = decltype(stc)::value;
+    const bool cok = c < nc && wok;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      aq[u][rt] = buf_load_b128(wb.blk, cok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
+    sw[u] = buf_load_b32(wb.sc, cok ? uint32_t(((t0 >> 2) * nc + c) * 256 + lane * 4) : kOOB);
+    uint8_t* stb = stage_b(stc);
+#pragma unroll
+    for (int jj = 0; jj < BLOADS; ++jj) {
+      const bool kok = c <= clast[jj];
+      dma16(bsrc, oob_add(boff[jj], kok ? uint32_t(c) * KB : kOOB), stb + (BLOADS * wave + jj) * 1024);
+    }
+  };
+
+  auto barrier = [&]() __attribute__((always_inline)) {
+    order_point();
+    __builtin_amdgcn_s_barrier();
+    order_point();
+  };
+
+  auto main_loop = [&](auto ntc) __attribute__((always_inline)) {
+    constexpr int NA = decltype(ntc)::value;  // 1 .. 8 active sub-tiles
+    f32x4_t acc[RT][NA];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](auto stc) __attribute__((always_inline)) {
+      constexpr int u = decltype(stc)::value;
+      if (busy) {
+        const uint8_t* sb = stage_b(stc);
+        uint32_t ascb[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) ascb[rt] = (sw[u] >> (((t0 + rt) & 3) * 8)) & 0xFFu;
+        if constexpr (ACT == ACT_BF16) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            bf16x8_t b[NA];
+#pragma unroll
+            for (int nt = 0; nt < NA; ++nt)
+              b[nt] = *reinterpret_cast<const bf16x8_t*>(sb + ((nt * 16 + r16) * 16 + ((4 * g + st) ^ r16)) * 16);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              const bf16x8_t av = fp4x8_to_bf16x8(dword(aq[u][rt], st), e8m0_as_scale_operand(ascb[rt]));
+#pragma unroll
+              for (int nt = 0; nt < NA; ++nt)
+                acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nt], acc[rt][nt], 0, 0, 0);
+            }
+          }
+        } else {
+          i32x8_t b[NA];
+          const int sw8 = (r16 >> 1) & 7;
+#pragma unroll
+          for (int nt = 0; nt < NA; ++nt) {
+            const uint8_t* rowp = sb + (nt * 16 + r16) * 128;
+            const uint4 p0 = *reinterpret_cast<const uint4*>(rowp + (g ^ sw8) * 16);
+            const uint4 p1 = *reinterpret_cast<const uint4*>(rowp + ((4 + g) ^ sw8) * 16);
+            b[nt] = i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const uint4 q = aq[u][rt];
+            const i32x8_t av = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
+#pragma unroll
+            for (int nt = 0; nt < NA; ++nt)
+              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b[nt], acc[rt][nt], 4, 0, 0,
+                                                                             int(ascb[rt]), 0, 127);
+          }
+        }
+      }
+    };
+
+    // prologue: chunks 0 .. S-2 in flight, issued in chunk order
+    order_point();
+    issue(0, IC<0>{});
+    order_point();
+    if constexpr (S > 2) { issue(1, IC<1>{}); order_point(); }
+    if constexpr (S > 3) { issue(2, IC<2>{}); order_point(); }
+
+    // iteration c: wait for chunk c, barrier (its tokens have landed for
+    // every wave, and chunk c-1's stage is free), refill that stage with
+    // chunk c+S-1, compute chunk c.  Every iteration issues the same loads
+    // (chunks past the end read zeros), so the wait count is fixed.
+    auto iteration = [&](int c, auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;  // c % S
+      wait_vmcnt<(S - 2) * LOADS>();
+      barrier();
+      issue(c + S - 1, IC<(u + S - 1) % S>{});
+      order_point();
+      compute(IC<u>{});
+    };
+    int c0 = 0;
+    for (; c0 + S <= nc; c0 += S) {
+      iteration(c0 + 0, IC<0>{});
+      iteration(c0 + 1, IC<1>{});
+      if constexpr (S > 2) iteration(c0 + 2, IC<2 % S>{});
+      if constexpr (S > 3) iteration(c0 + 3, IC<3 % S>{});
+    }
+    if (c0 + 0 < nc) iteration(c0 + 0, IC<0>{});
+    if (c0 + 1 < nc) iteration(c0 + 1, IC<1 % S>{});
+    if constexpr (S > 3) if (c0 + 2 < nc) iteration(c0 + 2, IC<2 % S>{});
+    wait_vmcnt<0>();
+    // Never true (slot counts are non-negative).  It keeps every weight
+    // prefetch live: the vmcnt waits count loads, so none may be dropped as
+    // dead even when its chunk lies past the end.
+    if (a.n_slots < 0) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int d = 0; d < S; ++d) x ^= aq[d][0].x ^ aq[d][1].y ^ aq[d][2].z ^ aq[d][3].w ^ sw[d];
+      static_cast<uint32_t*>(a.out)[0] = x;
+    }
+
+    // bias of this lane's 4 output rows per row tile (raw bf16 bits)
+    const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (rt < rt_active) {
+        const int r0 = grow + 16 * rt + 4 * g;
+        const uint2 q = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, uint32_t(r0) * 2u, 0, 0));
+#pragma unroll
+        for (int nt = 0; nt < NA; ++nt) {
+          const int j = nt * 16 + r16;
+          if (j < ntok) {
+            const f32x4_t v = acc[rt][nt];
+            store_rows_biased<ACT, PHASE>(a, grow + 16 * rt + 4 * g, row_start + j,
+                                          v[0] * a.acc_scale + __uint_as_float(q.x << 16),
+                                          v[1] * a.acc_scale + __uint_as_float(q.x & 0xFFFF0000u),
+                                          v[2] * a.acc_scale + __uint_as_float(q.y << 16),
+                                          v[3] * a.acc_scale + __uint_as_float(q.y & 0xFFFF0000u));
+          }
+        }
+      }
+    }
+  };
+  switch (na) {
+    case 1: main_loop(IC<1>{}); break;
+    case 2: main_loop(IC<2>{}); break;
+    case 3: main_loop(IC<3>{}); break;
+    case 4: main_loop(IC<4>{}); break;
+    case 5: main_loop(IC<5>{}); break;
+    case 6: main_loop(IC<6>{}); break;
+    case 7: main_loop(IC<7>{}); break;
+    default: main_loop(IC<8>{}); break;
+  }
+}
+
+// =====================================================================
 // Decode-shaped GEMM on the tiled weight order (bf16 and FP8 activations).
 //
 // Bound by streaming the routed experts' packed weights.  A workgroup owns
@@ -867,7 +1116,10 @@ static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
       const int nstripes = (a.R + kPrefillRows - 1) / kPrefillRows;
       int64_t items = int64_t(a.max_tiles) * nstripes;
       items = (items + 7) / 8 * 8;
-      gemm_prefill_kernel<ACT, PHASE, TILED><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
+      if constexpr (TILED)
+        gemm_prefill_tiled_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
+      else
+        gemm_prefill_kernel<ACT, PHASE, TILED><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
     }
   } else if constexpr (TILED && ACT != ACT_F32) {
     const unsigned gx = unsigned((a.R + 63) / 64);  // row groups
