@@ -20,17 +20,12 @@ constexpr int MAX_TOPK_DEV = 8;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// float -> bfloat16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
 
-// Two floats -> packed bf16 pair (lo in bits 0..15).
+// Two floats -> packed bf16 pair (lo in bits 0..15), rounded to nearest
+// even by the hardware conversion (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // An e8m0 scale byte as the float whose exponent field is that byte; the
@@ -114,7 +109,7 @@ __device__ __forceinline__ float clamped_swiglu(float gate, float up) {
   // gate <= 7, up in [-7, 7], h = (up + 1) * gate * sigmoid(1.702 * gate)
   float g = __builtin_fminf(gate, 7.0f);
   float u = __builtin_fminf(__builtin_fmaxf(up, -7.0f), 7.0f);
-  float sig = 1.0f / (1.0f + __expf(-1.702f * g));
+  float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g));  // v_rcp_f32 (1 ulp)
   return (u + 1.0f) * g * sig;
 }
 
