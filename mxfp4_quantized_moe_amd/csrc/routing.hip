@@ -359,8 +359,125 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) {
   }
 }
 
+// Expert-parallel grouping for large batches: workgroup e handles expert e.
+// Every workgroup builds the full histogram in LDS (integer counts, order
+// free) and scans it, which gives all offsets without a second launch; it
+// then writes the entries of its own expert: offsets, count, tile range and
+// tiles, its slot in the active list, and the stable positions of its
+// slots.  For those, each wave takes a contiguous range of slots, counts its
+// matches with ballots, takes a prefix over the waves, and sweeps the range
+// again writing positions in slot order.
+__global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(PermuteArgs a) {
+  __shared__ int cnt[256];
+  __shared__ int s_off, s_toff, s_act;
+  __shared__ int wsum[kPermWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, N = a.n_slots, me = blockIdx.x;
+
+  for (int e = tid; e < 256; e += kPermThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int s = tid; s < N; s += kPermThreads) {
+    int e = a.idx[s];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // each lane scans 4 consecutive experts
+    int c[4], tsum = 0, csum = 0, act = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      c[j] = e < E ? cnt[e] : 0;
+      csum += c[j];
+      tsum += (c[j] + kPrefillTokens - 1) / kPrefillTokens;
+      act += c[j] > 0;
+    }
+    int ctot, ttot, atot;
+    int cbase = wave_excl_scan(csum, lane, &ctot);
+    int tbase = wave_excl_scan(tsum, lane, &ttot);
+    int abase = wave_excl_scan(act, lane, &atot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      if (e == me) {
+        s_off = cbase;
+        s_toff = tbase;
+        s_act = abase;
+      }
+      cbase += c[j];
+      tbase += (c[j] + kPrefillTokens - 1) / kPrefillTokens;
+      abase += c[j] > 0;
+    }
+    if (me == 0 && lane == 0) {
+      a.offsets[E] = ctot;
+      a.tile_off[E] = ttot;
+      a.active[0] = atot;
+      if (a.offsets_out) a.offsets_out[E] = ctot;
+    }
+  }
+  __syncthreads();
+  const int c_me = cnt[me], off_me = s_off, toff_me = s_toff;
+  if (tid == 0) {
+    a.offsets[me] = off_me;
+    a.counts[me] = c_me;
+    a.tile_off[me] = toff_me;
+    if (a.counts_out) a.counts_out[me] = c_me;
+    if (a.offsets_out) a.offsets_out[me] = off_me;
+    if (c_me > 0) a.active[1 + s_act] = me;
+  }
+  for (int j = tid; j * kPrefillTokens < c_me; j += kPermThreads)
+    a.tiles[toff_me + j] = make_int4(me, off_me + j * kPrefillTokens, min(kPrefillTokens, c_me - j * kPrefillTokens), 0);
+
+  // stable positions of this expert's slots
+  const int per_wave = ((N + kPermWaves - 1) / kPermWaves + 63) & ~63;
+  const int s0 = wave * per_wave, s1 = min(N, s0 + per_wave);
+  int mine = 0;
+  for (int b = s0; b < s1; b += 64) {
+    const int s = b + lane;
+    int key = -1;
+    if (s < s1) {
+      key = a.idx[s];
+      key = key < 0 ? 0 : (key >= E ? E - 1 : key);
+    }
+    mine += __popcll(__ballot(key == me));
+  }
+  if (lane == 0) wsum[wave] = mine;
+  __syncthreads();
+  int run = off_me;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b = s0; b < s1; b += 64) {
+    const int s = b + lane;
+    int key = -1;
+    if (s < s1) {
+      key = a.idx[s];
+      key = key < 0 ? 0 : (key >= E ? E - 1 : key);
+    }
+    const uint64_t m = __ballot(key == me);
+    if (key == me) {
+      const int p = run + __popcll(m & lt_mask);
+      a.sorted[p] = s;
+      a.sorted_tok[p] = s / a.top_k;
+      a.pos[s] = p;
+    }
+    run += __popcll(m);
+  }
+}
+
+// Batches up to this many slots use the single-workgroup kernel (one
+// launch-latency-bound pass); larger ones the expert-parallel kernel, which
+// reads the expert ids three times per workgroup.
+constexpr int kPermSmall = 2048;
+constexpr int kPermLarge = 1 << 20;
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
-  permute_kernel<<<dim3(1), dim3(kPermThreads), 0, stream>>>(a);
+  if (a.n_slots == 0) return hipSuccess;
+  if (a.n_slots > kPermSmall && a.n_slots <= kPermLarge)
+    permute_by_expert_kernel<<<dim3(unsigned(a.E)), dim3(kPermThreads), 0, stream>>>(a);
+  else
+    permute_kernel<<<dim3(1), dim3(kPermThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 

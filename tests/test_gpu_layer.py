@@ -157,6 +157,8 @@ def test_fp8_calibration_scales(dev):
     (22, 100, 64, 64, 4, 20, "bf16"),    # router: 65 <= E <= 128 with few tokens (8 K-splitting waves)
     (23, 256, 64, 32, 8, 40, "bf16"),    # router: E = 256 (largest), top_k = 8
     (24, 200, 96, 64, 3, 70, "f32"),     # router: fp32 with E > 128
+    (25, 8, 64, 32, 2, 3000, "bf16"),    # grouping: > 2048 slots (one workgroup per expert)
+    (26, 256, 64, 32, 8, 600, "bf16"),   # grouping: > 2048 slots over 256 experts
 ])
 @pytest.mark.parametrize("layout", ["rows", "tiled"])
 def test_small_shapes(dev, seed, E, H, I, k, T, act, layout):
