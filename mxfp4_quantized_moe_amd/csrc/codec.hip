@@ -11,42 +11,65 @@ namespace mxmoe {
 
 // ---------------------------------------------------------------- unpack
 //
-// HBM-bound: 17 bytes in, 64 (bf16) or 128 (fp32) bytes out per block.  Each
-// thread owns one 16-byte block: one 128-bit load, one scale byte, sixteen
-// packed hardware conversions (exact for every byte and scale, including
-// s = 0 -> 2^-127, s = 255 -> NaN and overflow -> Inf), and four or eight
-// 128-bit stores.  Consecutive lanes own consecutive blocks, so the loads
-// and the wave's stores each cover one contiguous span.
+// HBM-bound: 17 bytes in, 64 (bf16) or 128 (fp32) bytes out per block.  The
+// decode is the packed hardware conversion (exact for every byte and scale,
+// including s = 0 -> 2^-127, s = 255 -> NaN and overflow -> Inf).  fp32
+// output: each thread owns one 16-byte block (one 128-bit load, one scale
+// byte, eight 128-bit stores).
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void unpack_kernel(const u32x4_t* __restrict__ blocks,
-                                                     const uint8_t* __restrict__ scales,
-                                                     void* __restrict__ out, int64_t nblocks) {
+__global__ __launch_bounds__(256) void unpack_f32_kernel(const u32x4_t* __restrict__ blocks,
+                                                         const uint8_t* __restrict__ scales,
+                                                         f32x4_t* __restrict__ out, int64_t nblocks) {
   int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= nblocks) return;
   const u32x4_t w = __builtin_nontemporal_load(blocks + i);
   const float sc = e8m0_as_scale_operand(scales[i]);
-  if constexpr (OUT_BF16) {
-    u32x4_t* o = static_cast<u32x4_t*>(out) + i * 4;
+  f32x4_t* o = out + i * 8;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      u32x4_t r;
-      r[0] = fp4x2_to_bf16x2<0>(w[d], sc);
-      r[1] = fp4x2_to_bf16x2<1>(w[d], sc);
-      r[2] = fp4x2_to_bf16x2<2>(w[d], sc);
-      r[3] = fp4x2_to_bf16x2<3>(w[d], sc);
-      __builtin_nontemporal_store(r, o + d);
+  for (int d = 0; d < 4; ++d) {
+    const f32x2_t a = fp4x2_to_f32x2<0>(w[d], sc);
+    const f32x2_t b = fp4x2_to_f32x2<1>(w[d], sc);
+    const f32x2_t c = fp4x2_to_f32x2<2>(w[d], sc);
+    const f32x2_t e = fp4x2_to_f32x2<3>(w[d], sc);
+    __builtin_nontemporal_store(f32x4_t{a[0], a[1], b[0], b[1]}, o + 2 * d);
+    __builtin_nontemporal_store(f32x4_t{c[0], c[1], e[0], e[1]}, o + 2 * d + 1);
+  }
+}
+
+// bf16 output with whole-wave stores: a wave owns 64 consecutive blocks
+// (1 KB in, 4 KB out).  Store d of lane l writes output bytes
+// [1 KB * d + 16 l, +16), which is quarter l % 4 of block 16 d + l / 4: the 8
+// values of dword l % 4 of that block.  So each of the four dword loads of a
+// lane is part of one contiguous 256-byte wave read, and each 16-byte store
+// part of one contiguous 1 KB wave write.
+__global__ __launch_bounds__(256) void unpack_bf16_kernel(const uint32_t* __restrict__ blocks,
+                                                          const uint8_t* __restrict__ scales,
+                                                          u32x4_t* __restrict__ out, int64_t nblocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b0 = ((int64_t(blockIdx.x) * 256 + threadIdx.x) >> 6) * 64;
+  const int q = lane & 3;
+  uint32_t w[4];
+  float sc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int64_t blk = b0 + 16 * d + (lane >> 2);
+    w[d] = 0;
+    sc[d] = 0.f;
+    if (blk < nblocks) {
+      w[d] = __builtin_nontemporal_load(blocks + blk * 4 + q);
+      sc[d] = e8m0_as_scale_operand(scales[blk]);
     }
-  } else {
-    f32x4_t* o = static_cast<f32x4_t*>(out) + i * 8;
+  }
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const f32x2_t a = fp4x2_to_f32x2<0>(w[d], sc);
-      const f32x2_t b = fp4x2_to_f32x2<1>(w[d], sc);
-      const f32x2_t c = fp4x2_to_f32x2<2>(w[d], sc);
-      const f32x2_t e = fp4x2_to_f32x2<3>(w[d], sc);
-      __builtin_nontemporal_store(f32x4_t{a[0], a[1], b[0], b[1]}, o + 2 * d);
-      __builtin_nontemporal_store(f32x4_t{c[0], c[1], e[0], e[1]}, o + 2 * d + 1);
+  for (int d = 0; d < 4; ++d) {
+    const int64_t blk = b0 + 16 * d + (lane >> 2);
+    if (blk < nblocks) {
+      u32x4_t r;
+      r[0] = fp4x2_to_bf16x2<0>(w[d], sc[d]);
+      r[1] = fp4x2_to_bf16x2<1>(w[d], sc[d]);
+      r[2] = fp4x2_to_bf16x2<2>(w[d], sc[d]);
+      r[3] = fp4x2_to_bf16x2<3>(w[d], sc[d]);
+      __builtin_nontemporal_store(r, out + blk * 4 + q);
     }
   }
 }
@@ -56,11 +79,11 @@ hipError_t launch_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t n
   if (nblocks == 0) return hipSuccess;
   int64_t grid = (nblocks + 255) / 256;
   if (out_bf16)
-    unpack_kernel<true><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(reinterpret_cast<const u32x4_t*>(blocks), scales,
-                                                                       out, nblocks);
+    unpack_bf16_kernel<<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(reinterpret_cast<const uint32_t*>(blocks), scales,
+                                                                      static_cast<u32x4_t*>(out), nblocks);
   else
-    unpack_kernel<false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(reinterpret_cast<const u32x4_t*>(blocks), scales,
-                                                                        out, nblocks);
+    unpack_f32_kernel<<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(reinterpret_cast<const u32x4_t*>(blocks), scales,
+                                                                     static_cast<f32x4_t*>(out), nblocks);
   return hipGetLastError();
 }
 
