@@ -59,7 +59,7 @@ Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8)
   w.xq = take(fp8 ? size_t(T) * size_t(H) : 0);
   const size_t hb = fp8 ? 1 : (act_dtype == MXMOE_BF16 ? 2 : 4);
   w.h = take(slots * size_t(I) * hb);
-  w.y = take(slots * size_t(H) * 4);
+  w.y = take(slots * size_t(H) * (act_dtype == MXMOE_BF16 ? 2 : 4));  // Y: bf16 with bf16 activations
   w.total = o;
   return w;
 }
@@ -333,7 +333,8 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
   if ((e = launch_moe_gemm(g1, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
   if (mark(5) != hipSuccess) return MXMOE_ERR_HIP;
   CombineArgs ca{};
-  ca.Y = at<float>(ws, w.y);
+  ca.Y = at<void>(ws, w.y);
+  ca.y_bf16 = act != ACT_F32;
   ca.pos = at<int32_t>(ws, w.pos);
   ca.wts = at<float>(ws, w.wts);
   ca.out = out;

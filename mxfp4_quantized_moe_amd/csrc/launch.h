@@ -83,7 +83,7 @@ struct GemmArgs {
   const int32_t* active;      // (E+1)
   const int32_t* tile_off;    // (E+1)
   const int4* tiles;          // prefill tile table
-  void* out;                  // phase 0: h (T*k, R/2) act storage; phase 1: Y (T*k, R) fp32
+  void* out;                  // phase 0: h (T*k, R/2) act storage; phase 1: Y (T*k, R), fp32 or bf16 (act != fp32)
   float acc_scale;            // fp8: the static scale of the B operand; else 1
   float out_inv_scale;        // phase 0 fp8: 1 / h_scale
   int max_active;             // grid bound: min(E, T*k)
@@ -93,7 +93,8 @@ struct GemmArgs {
 hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream);
 
 struct CombineArgs {
-  const float* Y;        // (T*k, H) fp32 in sorted order
+  const void* Y;         // (T*k, H) in sorted order: bf16 (y_bf16) or fp32
+  int y_bf16;
   const int32_t* pos;    // (T*k)
   const float* wts;      // (T, k)
   void* out;             // (T, H) act dtype

@@ -136,7 +136,9 @@ __device__ __forceinline__ uint32_t act_row_offset(const GemmArgs& a, int phase,
 // ------------------------------------------------------------ epilogue
 
 // Store rows r0 .. r0+3 of one token (sorted row p), bias already added:
-// gate_up applies the SwiGLU and writes h, down writes Y.
+// gate_up applies the SwiGLU and writes h, down writes Y (bf16 when the
+// activations are bf16, its only reader being the combine, which sums the
+// k rows of a token in fp32; fp32 in the fp32 mode).
 template <int ACT, int PHASE>
 __device__ __forceinline__ void store_rows_biased(const GemmArgs& a, int r0, int64_t p, float v0, float v1, float v2,
                                                   float v3) {
@@ -154,8 +156,10 @@ __device__ __forceinline__ void store_rows_biased(const GemmArgs& a, int r0, int
       const uint32_t q = pack_e4m3x4(h0 * a.out_inv_scale, h1 * a.out_inv_scale, 0.f, 0.f);
       *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.out) + o) = uint16_t(q & 0xFFFFu);
     }
-  } else {
+  } else if constexpr (ACT == ACT_F32) {
     *reinterpret_cast<float4*>(static_cast<float*>(a.out) + p * a.R + r0) = make_float4(v0, v1, v2, v3);
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + p * a.R + r0) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
   }
 }
 
@@ -1156,9 +1160,12 @@ hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream) 
 // ----------------------------------------------------------------- combine
 //
 // out_t = sum_j w[t, j] * Y[pos[t*k + j]] in the order j = 0 .. k-1 (fp32),
-// one workgroup per token, four columns per thread.
+// one workgroup per token; each thread takes 8 columns of bf16 Y (one
+// 16-byte load per row) or 4 of fp32 Y.
 
+template <bool Y_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int CPT = Y_BF16 ? 8 : 4;  // columns per thread
   const int t = blockIdx.x;
   const int k = a.top_k;
   int64_t rows[MAX_TOPK_DEV];
@@ -1172,29 +1179,51 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       w[j] = a.wts[int64_t(t) * k + j];
     }
   }
-  for (int c = threadIdx.x * 4; c < a.H; c += 256 * 4) {
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = threadIdx.x * CPT; c < a.H; c += 256 * CPT) {
+    float s[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) s[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < MAX_TOPK_DEV; ++j) {
       if (j < k) {
-        const float4 y = *reinterpret_cast<const float4*>(a.Y + rows[j] + c);
-        s.x += w[j] * y.x;
-        s.y += w[j] * y.y;
-        s.z += w[j] * y.z;
-        s.w += w[j] * y.w;
+        if constexpr (Y_BF16) {
+          const uint4 y = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Y) + rows[j] + c);
+          const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s[2 * i] += w[j] * __uint_as_float(yw[i] << 16);
+            s[2 * i + 1] += w[j] * __uint_as_float(yw[i] & 0xFFFF0000u);
+          }
+        } else {
+          const float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.Y) + rows[j] + c);
+          s[0] += w[j] * y.x;
+          s[1] += w[j] * y.y;
+          s[2] += w[j] * y.z;
+          s[3] += w[j] * y.w;
+        }
       }
     }
     const int64_t o = int64_t(t) * a.H + c;
-    if (a.out_bf16)
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
-    else
-      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = s;
+    if (a.out_bf16) {
+      if constexpr (CPT == 8)
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + o) =
+            make_uint4(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7]));
+      else
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPT; i += 4)
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o + i) = make_float4(s[i], s[i + 1], s[i + 2], s[i + 3]);
+    }
   }
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  combine_kernel<<<dim3(unsigned(a.T)), dim3(256), 0, stream>>>(a);
+  if (a.y_bf16)
+    combine_kernel<true><<<dim3(unsigned(a.T)), dim3(256), 0, stream>>>(a);
+  else
+    combine_kernel<false><<<dim3(unsigned(a.T)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
