@@ -970,6 +970,11 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_tiled_kernel(GemmArgs a) {
   const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
   const int nj = (nc - wave + 3) >> 2;  // chunks of this wave (0 when nc <= wave)
   const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
+  // bias of the 4 output rows this lane stores (row tile t0 + wave, rows
+  // 4g .. 4g+3), fetched before the K loop as raw bf16 bits
+  const int r0 = 16 * (t0 + wave) + 4 * g;
+  const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
+  const uint2 biasq = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, r0 < a.R ? uint32_t(r0) * 2u : kOOB, 0, 0));
 
   // up to 32 tokens per pass over the weights (registers bound the tile)
   for (int tg = 0; tg < n_e; tg += 32) {
@@ -1095,13 +1100,15 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_tiled_kernel(GemmArgs a) {
         for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt][nt];
         __syncthreads();
         const int j = tg + nt * 16 + r16;
-        const int r0 = 16 * (t0 + wave) + 4 * g;
         if (j < n_e && r0 < a.R) {
           f32x4_t sum = red[0][wave][lane];
           sum += red[1][wave][lane];
           sum += red[2][wave][lane];
           sum += red[3][wave][lane];
-          store_rows<ACT, PHASE>(a, e, r0, row_start + j, sum[0], sum[1], sum[2], sum[3]);
+          store_rows_biased<ACT, PHASE>(a, r0, row_start + j, sum[0] * a.acc_scale + __uint_as_float(biasq.x << 16),
+                                        sum[1] * a.acc_scale + __uint_as_float(biasq.x & 0xFFFF0000u),
+                                        sum[2] * a.acc_scale + __uint_as_float(biasq.y << 16),
+                                        sum[3] * a.acc_scale + __uint_as_float(biasq.y & 0xFFFF0000u));
         }
         __syncthreads();
       }

@@ -28,6 +28,10 @@ namespace mxmoe {
 // to both operands, which leaves the dot products unchanged.
 
 constexpr int kRouteTokens = 16;
+// K-splitting waves per 16-token group for large batches (sweep knob)
+#ifndef MXMOE_ROUTE_KW_LARGE
+#define MXMOE_ROUTE_KW_LARGE 8
+#endif
 
 // RG row tiles of 16 experts have their loads issued together, NG groups
 // cover E <= 16 * RG * NG.
@@ -204,12 +208,18 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   const unsigned grid = unsigned((a.T + kRouteTokens - 1) / kRouteTokens);
   // few token groups: more waves split K (shorter chains of dependent
-  // loads per wave); many groups: 4 waves each, several groups per CU.
+  // loads per wave); many groups: 8 waves each up to E = 128.
   // The LDS of the partial logits, KW x 16 x E floats, stays <= 64 KB.
   if (grid < 64 && a.E <= 64) {
     if (a.act_bf16) launch_route_typed<true, 16>(a, grid, stream);
     else launch_route_typed<false, 16>(a, grid, stream);
   } else if (grid < 64 && a.E <= 128) {
+    if (a.act_bf16) launch_route_typed<true, 8>(a, grid, stream);
+    else launch_route_typed<false, 8>(a, grid, stream);
+  } else if (MXMOE_ROUTE_KW_LARGE == 16 && a.E <= 64) {
+    if (a.act_bf16) launch_route_typed<true, 16>(a, grid, stream);
+    else launch_route_typed<false, 16>(a, grid, stream);
+  } else if (MXMOE_ROUTE_KW_LARGE >= 8 && a.E <= 128) {
     if (a.act_bf16) launch_route_typed<true, 8>(a, grid, stream);
     else launch_route_typed<false, 8>(a, grid, stream);
   } else {
