@@ -687,36 +687,50 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
 // =====================================================================
 // Prefill-shaped GEMM on the tiled weight order.
 //
-// Same workgroup tile as above (kPrefillRows rows x 128 tokens, 8 waves of
-// 64 rows x 128 tokens), but a wave's weight rows are its own, so they skip
-// LDS: each chunk's four 1 KB pieces (already in MFMA lane order) and its
-// scale dword load straight into registers.  Only the token tile, which
-// all 8 waves read, goes through LDS (buffer-to-LDS DMA), which leaves room
-// for S stages: S-1 chunks of weights and tokens stay in flight while one
-// is computed.
+// Workgroup tile = kTiledRows weight rows x 128 tokens of one expert, K in
+// 128-wide chunks, one wave per 64 rows (4 row tiles, one scale group) x
+// all 128 tokens.  A wave's weight rows are its own, so they skip LDS: each
+// chunk's four 1 KB pieces (already in MFMA lane order) and its scale dword
+// load straight into registers.  Only the token tile, which all waves read,
+// goes through LDS (buffer-to-LDS DMA) in an S-stage ring: S-1 chunks of
+// weights and tokens stay in flight while one is computed, and one barrier
+// per chunk publishes a landed stage and frees the one computed last.
+// 256-row workgroups (4 waves, 64 KB of LDS) run two per CU: each one's
+// per-chunk barrier and refill bubble is covered by the other's MFMAs,
+// which outweighs the doubled token-tile reads from L2 (measured against
+// one 512-row, three-stage workgroup per CU).
 // =====================================================================
 
-// (FP8 token fragments take twice the registers of bf16 ones: one stage
-// fewer keeps that variant free of spills)
+// Rows per workgroup (64 per wave) of the tiled-order kernel.
+#ifndef MXMOE_PREFILL_TILED_ROWS
+#define MXMOE_PREFILL_TILED_ROWS 256
+#endif
+constexpr int kTiledRows = MXMOE_PREFILL_TILED_ROWS;
+constexpr int kTiledWaves = kTiledRows / 64;
+constexpr int kTiledThreads = 64 * kTiledWaves;
+
+// LDS stages of the token tile for bf16 and FP8 activations (build-time
+// knobs for sweeps; registers, not LDS, bound them at this tile size).
 #ifndef MXMOE_PREFILL_TILED_STAGES
-#define MXMOE_PREFILL_TILED_STAGES 3
+#define MXMOE_PREFILL_TILED_STAGES 2
 #endif
 #ifndef MXMOE_PREFILL_TILED_STAGES_FP8
 #define MXMOE_PREFILL_TILED_STAGES_FP8 2
 #endif
 
 template <int ACT, int PHASE>
-__global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_tiled_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefill_tiled_kernel(GemmArgs a) {
   static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "prefill path takes bf16 or fp8 activations");
   static_assert(kPrefillTokens == 128, "eight 16-token sub-tiles per tile");
-  static_assert(kPrefillRows == 512, "8 waves of 4 row tiles: one scale group per wave");
+  static_assert(kTiledRows % 64 == 0, "waves of 4 row tiles: one scale group per wave");
   constexpr int RT = 4, S = ACT == ACT_BF16 ? MXMOE_PREFILL_TILED_STAGES : MXMOE_PREFILL_TILED_STAGES_FP8;
   constexpr int EB = ACT == ACT_BF16 ? 2 : 1;
   constexpr int KB = 128 * EB;                  // bytes of one token row per chunk
   constexpr int PPR = KB / 16;                  // 16-byte pieces per token row (16 or 8)
   constexpr int TPL = 64 / PPR;                 // tokens per 1 KB B load (4 or 8)
   constexpr int NBL = 128 / TPL;                // B loads per chunk (32 or 16)
-  constexpr int BLOADS = NBL / 8;               // B loads per wave per chunk (4 or 2)
+  constexpr int BLOADS = NBL / kTiledWaves;     // B loads per wave per chunk
+  static_assert(NBL % kTiledWaves == 0, "B loads split evenly over the waves");
   constexpr int B_BYTES = 128 * KB;             // B stage
   constexpr int LOADS = RT + 1 + BLOADS;        // VMEM instructions per wave per chunk
   static_assert(S >= 2 && S <= 4, "2..4 stages");
@@ -739,7 +753,7 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_tiled_kernel(Gem
   // nvalid.  Hardware places workgroup b on XCD b % 8, so XCD x takes the
   // x-th eighth of the valid items, in order: every XCD gets an even share
   // and the stripes of one token tile run on one XCD, sharing its L2.
-  const int nstripes = (a.R + kPrefillRows - 1) / kPrefillRows;
+  const int nstripes = (a.R + kTiledRows - 1) / kTiledRows;
   const int nvalid = a.tile_off[a.E] * nstripes;
   const int per_xcd = (nvalid + 7) >> 3;
   const int idx = blockIdx.x >> 3;
@@ -752,7 +766,7 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_tiled_kernel(Gem
   const int nb = a.nb, K = nb * 32;
   const WBuf wb = expert_weights<true>(a, e);
   const int nc = wb.nc;
-  const int grow = stripe * kPrefillRows + wave * (16 * RT);  // first row of this wave
+  const int grow = stripe * kTiledRows + wave * (16 * RT);  // first row of this wave
   const int t0 = grow >> 4;                                   // its first row tile (a scale group start)
   const int rt_active = max(0, min(RT, (a.R - grow) >> 4));
   const bool busy = rt_active > 0;  // wave-uniform
@@ -1124,11 +1138,11 @@ template <int ACT, int PHASE, bool TILED>
 static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
   if (prefill) {
     if constexpr (ACT != ACT_F32) {
-      const int nstripes = (a.R + kPrefillRows - 1) / kPrefillRows;
+      const int nstripes = TILED ? (a.R + kTiledRows - 1) / kTiledRows : (a.R + kPrefillRows - 1) / kPrefillRows;
       int64_t items = int64_t(a.max_tiles) * nstripes;
       items = (items + 7) / 8 * 8;
       if constexpr (TILED)
-        gemm_prefill_tiled_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
+        gemm_prefill_tiled_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kTiledThreads), 0, stream>>>(a);
       else
         gemm_prefill_kernel<ACT, PHASE, TILED><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);
     }
