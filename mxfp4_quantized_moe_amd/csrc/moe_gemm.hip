@@ -845,23 +845,33 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
             }
           }
         } else {
-          i32x8_t b[NA];
+          // token fragments double-buffered by hand (sub-tile nt+1 is read
+          // before sub-tile nt's MFMAs; the order points keep the compiler
+          // from hoisting all of them, which would cost 8 registers each)
           const int sw8 = (r16 >> 1) & 7;
-#pragma unroll
-          for (int nt = 0; nt < NA; ++nt) {
+          auto load_b = [&](int nt) __attribute__((always_inline)) {
             const uint8_t* rowp = sb + (nt * 16 + r16) * 128;
             const uint4 p0 = *reinterpret_cast<const uint4*>(rowp + (g ^ sw8) * 16);
             const uint4 p1 = *reinterpret_cast<const uint4*>(rowp + ((4 + g) ^ sw8) * 16);
-            b[nt] = i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
-          }
+            return i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
+          };
+          i32x8_t av[RT];
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
             const uint4 q = aq[u][rt];
-            const i32x8_t av = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
+            av[rt] = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
+          }
+          i32x8_t bcur = load_b(0);
 #pragma unroll
-            for (int nt = 0; nt < NA; ++nt)
-              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b[nt], acc[rt][nt], 4, 0, 0,
+          for (int nt = 0; nt < NA; ++nt) {
+            i32x8_t bnext = bcur;
+            if (nt + 1 < NA) bnext = load_b(nt + 1);
+            order_point();
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[rt], bcur, acc[rt][nt], 4, 0, 0,
                                                                              int(ascb[rt]), 0, 127);
+            bcur = bnext;
           }
         }
       }
