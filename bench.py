@@ -23,6 +23,7 @@ Workloads (synthetic, seeded; see workloads/):
   fp8_20b_t2048        W-MXFP4 A-FP8, gpt-oss-20b shape, T=2048
   tiny                 E=4, top-2, H=I=64, T=8, fp32
   unpack_20b           mxfp4_unpack of the 20b expert tensors to bf16 (GB/s)
+  linear_t4096_k2880_n5760  weight-only MXFP4 dense layer y = x W^T + b, bf16
 """
 from __future__ import annotations
 
@@ -319,6 +320,54 @@ def bench_unpack(args, dev):
                          "frac": gbps / PEAK["hbm_GBps"], "traffic": measured_traffic("unpack_20b", "unpack_kernel")}}
 
 
+def bench_linear(args, dev):
+    """The weight-only MXFP4 dense layer: tokens/s and the GEMM's TFLOP/s
+    (HIP events around each call on the stream it runs on)."""
+    import numpy as np
+    import torch
+
+    import mxfp4_quantized_moe_amd as mx
+    import workloads as W
+
+    T, K, N = 4096, 2880, 5760
+    case = W.linear_case(0, T, K, N, "bf16", True)
+    lin = mx.MXFP4Linear(W.array_to_torch(case.blocks, dev), W.array_to_torch(case.scales, dev), N, K,
+                         W.array_to_torch(case.bias, dev))
+    if args.layout == "tiled":
+        lin = lin.tiled()
+    wbytes = lin.blocks.numel() + lin.scales.numel()
+    copies = min(64, -(-int(1.0e9) // wbytes) + 1) if args.copies is None else args.copies
+    lins = [lin] + [mx.MXFP4Linear(lin.blocks.clone(), lin.scales.clone(), N, K, lin.bias, lin.layout)
+                    for _ in range(copies - 1)]
+    x = W.array_to_torch(case.x, dev)
+    out = torch.empty((T, N), dtype=x.dtype, device=dev)
+    ws = torch.empty(max(mx.mxfp4_linear_workspace_bytes(T, N, x.dtype), 256), dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        lins[i % copies](x, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        lins[i % copies](x, out=out, workspace=ws)
+        ends[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    call_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
+    fl = 2 * T * K * N
+    achieved = fl / call_s / 1e12
+    return {"metric": "MXFP4 dense linear tokens/s", "value": T * args.steps / (t1 - t0), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded random MXFP4 weight and bf16 activations)",
+            "config": {"workload": f"linear_t{T}_k{K}_n{N}", "T": T, "K": K, "N": N, "weight_layout": args.layout,
+                       "weight_copies": copies},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK["bf16_TFLOPs"], "unit": "TFLOP/s",
+                         "frac": achieved / PEAK["bf16_TFLOPs"], "kernel": "gemm_prefill_tiled_kernel<phase 1>",
+                         "algorithmic": f"{fl} flop per call", "traffic": None}}
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
@@ -363,6 +412,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "unpack_20b":
         res = bench_unpack(args, dev)
+    elif args.workload == "linear_t4096_k2880_n5760":
+        res = bench_linear(args, dev)
     else:
         res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)

@@ -59,7 +59,7 @@ typedef enum {
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* mxmoe_status_string(int32_t status);
 
-/* Interface version, bumped on any ABI change (currently 2). */
+/* Interface version, bumped on any ABI change (currently 3). */
 int32_t mxmoe_version(void);
 
 /*
@@ -143,6 +143,29 @@ mxmoe_status_t mxfp4_tiled_bytes(int64_t mats, int64_t rows, int64_t k, int64_t*
  */
 mxmoe_status_t mxfp4_tile(const uint8_t* blocks, const uint8_t* scales, int64_t mats, int64_t rows, int64_t k,
                           uint8_t* tiled_blocks, uint8_t* tiled_scales, void* stream);
+
+/*
+ * mxfp4_linear — a weight-only MXFP4 dense layer, y = x W^T + b, with the
+ * (N, K) weight stored as MXFP4 and dequantised in registers as the GEMM
+ * consumes it (KerasFormers "mxfp4" page, "As a quantize_model scheme": a
+ * Dense kernel kept packed and dequantised on the fly, its contracting
+ * dimension a multiple of 32; the bias stays full precision).
+ *
+ *   x        : (T, K) in act_dtype (MXMOE_BF16 or MXMOE_F32).
+ *   w_blocks, w_scales : the weight as one (rows N, k K) MXFP4 matrix in
+ *              weight_layout order (MXMOE_LAYOUT_ROWS: (N, K/32, 16) and
+ *              (N, K/32); MXMOE_LAYOUT_TILED: the outputs of mxfp4_tile
+ *              with mats = 1).
+ *   bias     : (N,) in act_dtype, or NULL for none.
+ *   out      : (T, N) in act_dtype, accumulated in fp32 and rounded once.
+ *   workspace: mxfp4_linear_workspace_bytes(T, N, act_dtype) bytes.
+ * Errors: K or N not a positive multiple of 32, T < 0 -> MXMOE_ERR_SHAPE;
+ * otherwise as moe_mxfp4_forward.  T == 0 is a no-op.
+ */
+size_t mxfp4_linear_workspace_bytes(int64_t T, int64_t N, int32_t act_dtype);
+mxmoe_status_t mxfp4_linear(const void* x, int64_t T, int64_t K, const uint8_t* w_blocks, const uint8_t* w_scales,
+                            int32_t weight_layout, const void* bias, int64_t N, int32_t act_dtype, void* out,
+                            void* workspace, size_t ws_bytes, void* stream);
 
 /* One MoE layer's parameters, all device pointers (see the file header). */
 typedef struct {

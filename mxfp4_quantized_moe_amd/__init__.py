@@ -9,12 +9,15 @@ from .binding import (  # noqa: F401
     LAYOUT_TILED,
     LIB_PATH,
     MoEWeights,
+    MXFP4Linear,
     MxmoeError,
     alloc_workspace,
     load_library,
     moe_mxfp4_calibrate_fp8,
     moe_mxfp4_forward,
     moe_mxfp4_route,
+    mxfp4_linear,
+    mxfp4_linear_workspace_bytes,
     mxfp4_pack,
     mxfp4_tile,
     mxfp4_tiled_bytes,

@@ -41,6 +41,8 @@ EXPORTED = (
     "mxfp4_pack",
     "mxfp4_tiled_bytes",
     "mxfp4_tile",
+    "mxfp4_linear_workspace_bytes",
+    "mxfp4_linear",
     "moe_mxfp4_workspace_bytes",
     "moe_mxfp4_forward",
     "moe_mxfp4_route",
@@ -113,6 +115,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_tiled_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.mxfp4_tile.restype = i32
     lib.mxfp4_tile.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.mxfp4_linear_workspace_bytes.restype = sz
+    lib.mxfp4_linear_workspace_bytes.argtypes = [i64, i64, i32]
+    lib.mxfp4_linear.restype = i32
+    lib.mxfp4_linear.argtypes = [vp, i64, i64, vp, vp, i32, vp, i64, i32, vp, vp, sz, vp]
     lib.moe_mxfp4_workspace_bytes.restype = sz
     lib.moe_mxfp4_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i64, ctypes.POINTER(FwdOpts)]
     lib.moe_mxfp4_forward.restype = i32
@@ -201,6 +207,56 @@ def mxfp4_tile(blocks: torch.Tensor, scales: torch.Tensor):
     _check(load_library().mxfp4_tile(_ptr(blocks), _ptr(scales), mats, rows, nb * 32, _ptr(tb), _ptr(ts),
                                      _stream(blocks.device)))
     return tb, ts
+
+
+# ----------------------------------------------------------- dense layer
+
+
+@dataclass
+class MXFP4Linear:
+    """A weight-only MXFP4 dense layer y = x W^T + b (see include/mxmoe.h).
+    blocks/scales: (N, K/32, 16) / (N, K/32) in row order, or the flat
+    outputs of mxfp4_tile with layout LAYOUT_TILED."""
+
+    blocks: torch.Tensor
+    scales: torch.Tensor
+    N: int
+    K: int
+    bias: Optional[torch.Tensor] = None  # (N,) in the activation dtype
+    layout: int = LAYOUT_ROWS
+
+    @staticmethod
+    def from_rows(blocks: torch.Tensor, scales: torch.Tensor, bias: Optional[torch.Tensor] = None) -> "MXFP4Linear":
+        return MXFP4Linear(blocks, scales, int(blocks.shape[0]), int(blocks.shape[1]) * 32, bias)
+
+    def tiled(self) -> "MXFP4Linear":
+        if self.layout == LAYOUT_TILED:
+            return self
+        tb, ts = mxfp4_tile(self.blocks.reshape(1, self.N, self.K // 32, 16), self.scales.reshape(1, self.N, self.K // 32))
+        return MXFP4Linear(tb, ts, self.N, self.K, self.bias, LAYOUT_TILED)
+
+    def __call__(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        return mxfp4_linear(x, self, out=out, workspace=workspace)
+
+
+def mxfp4_linear_workspace_bytes(T: int, N: int, act_dtype: torch.dtype) -> int:
+    return int(load_library().mxfp4_linear_workspace_bytes(T, N, _dtype_code(act_dtype)))
+
+
+def mxfp4_linear(x: torch.Tensor, layer: MXFP4Linear, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x W^T + b for x (T, K) in bf16 or fp32; returns (T, N)."""
+    T = int(x.shape[0])
+    if out is None:
+        out = torch.empty((T, layer.N), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        n = mxfp4_linear_workspace_bytes(T, layer.N, x.dtype)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    _check(load_library().mxfp4_linear(_ptr(x), T, int(x.shape[1]), _ptr(layer.blocks), _ptr(layer.scales),
+                                       layer.layout, _ptr(layer.bias), layer.N, _dtype_code(x.dtype), _ptr(out),
+                                       _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
 
 
 # ----------------------------------------------------------------- layer

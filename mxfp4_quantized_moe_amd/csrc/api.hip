@@ -231,7 +231,7 @@ const char* mxmoe_status_string(int32_t s) {
   }
 }
 
-int32_t mxmoe_version(void) { return 2; }
+int32_t mxmoe_version(void) { return 3; }
 
 mxmoe_status_t mxfp4_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t rows, int64_t k, void* out,
                             int32_t out_dtype, void* stream) {
@@ -386,6 +386,103 @@ mxmoe_status_t moe_mxfp4_calibrate_fp8(const mxmoe_layer_t* L, const void* x, in
   if (launch_amax_bf16(static_cast<const uint16_t*>(x), T * L->H, slots, s) != hipSuccess) return MXMOE_ERR_HIP;
   if (launch_amax_bf16(at<uint16_t>(ws, w.h), T * L->top_k * L->I, slots + 1, s) != hipSuccess) return MXMOE_ERR_HIP;
   return hip_status(launch_calib_finish(slots, scales_out, s));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------- dense layer
+
+namespace {
+
+struct LinearWorkspace {
+  size_t offsets, active, tile_off, tiles, bias, total;
+};
+
+LinearWorkspace linear_layout(int64_t T, int64_t N, int act_dtype) {
+  LinearWorkspace w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  w.offsets = take(2 * 4);
+  w.active = take(2 * 4);
+  w.tile_off = take(2 * 4);
+  w.tiles = take(size_t((T + kPrefillTokens - 1) / kPrefillTokens) * 16 + 16);
+  w.bias = take(size_t(N) * (act_dtype == MXMOE_BF16 ? 2 : 4));
+  w.total = o;
+  return w;
+}
+
+mxmoe_status_t check_linear(int64_t T, int64_t K, int64_t N, int32_t act_dtype, int32_t layout) {
+  if (T < 0 || K <= 0 || N <= 0 || K % 32 != 0 || N % 32 != 0 || K > kMaxDim || N > kMaxDim) return MXMOE_ERR_SHAPE;
+  if (T > kMaxSlots) return MXMOE_ERR_SHAPE;
+  if (act_dtype != MXMOE_F32 && act_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
+  if (layout != MXMOE_LAYOUT_ROWS && layout != MXMOE_LAYOUT_TILED) return MXMOE_ERR_VALUE;
+  // 32-bit buffer windows over x, out and the weight (both orders)
+  if (T * K * 4 > kMaxWindow || T * N * 4 > kMaxWindow) return MXMOE_ERR_SHAPE;
+  int64_t bb, sb;
+  tiled_sizes(1, N, K, &bb, &sb);
+  if (bb > kMaxWindow || N * K / 2 > kMaxWindow) return MXMOE_ERR_SHAPE;
+  return MXMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mxfp4_linear_workspace_bytes(int64_t T, int64_t N, int32_t act_dtype) {
+  if (T < 0 || N <= 0 || N > kMaxDim || T > kMaxSlots) return 0;
+  if (act_dtype != MXMOE_F32 && act_dtype != MXMOE_BF16) return 0;
+  return linear_layout(T, N, act_dtype).total;
+}
+
+mxmoe_status_t mxfp4_linear(const void* x, int64_t T, int64_t K, const uint8_t* w_blocks, const uint8_t* w_scales,
+                            int32_t weight_layout, const void* bias, int64_t N, int32_t act_dtype, void* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  mxmoe_status_t st = check_linear(T, K, N, act_dtype, weight_layout);
+  if (st != MXMOE_OK) return st;
+  if (T == 0) return MXMOE_OK;
+  if (!x || !w_blocks || !w_scales || !out || !ws) return MXMOE_ERR_NULL;
+  const void* ptrs[] = {x, w_blocks, w_scales, out, ws, bias};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MXMOE_ERR_ALIGN;
+  const LinearWorkspace w = linear_layout(T, N, act_dtype);
+  if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ebytes = act_dtype == MXMOE_BF16 ? 2 : 4;
+  if (launch_linear_setup(int(T), at<int32_t>(ws, w.offsets), at<int32_t>(ws, w.active), at<int32_t>(ws, w.tile_off),
+                          at<int4>(ws, w.tiles), bias ? nullptr : at<void>(ws, w.bias), int(N), ebytes, s) != hipSuccess)
+    return MXMOE_ERR_HIP;
+  // the down-projection epilogue of the grouped GEMM (bias added, no
+  // SwiGLU), over the token rows in order
+  GemmArgs g{};
+  g.act = act_dtype == MXMOE_BF16 ? ACT_BF16 : ACT_F32;
+  g.phase = 1;
+  g.wblk = w_blocks;
+  g.wsc = w_scales;
+  g.tiled = weight_layout == MXMOE_LAYOUT_TILED;
+  g.bias = bias ? bias : at<void>(ws, w.bias);
+  g.bias_bf16 = act_dtype == MXMOE_BF16;
+  g.R = int(N);
+  g.nb = int(K / 32);
+  g.top_k = 1;
+  g.E = 1;
+  g.bsrc = x;
+  g.b_rows = T;
+  g.offsets = at<int32_t>(ws, w.offsets);
+  g.active = at<int32_t>(ws, w.active);
+  g.tile_off = at<int32_t>(ws, w.tile_off);
+  g.tiles = at<int4>(ws, w.tiles);
+  g.out = out;
+  g.acc_scale = 1.0f;
+  g.out_inv_scale = 1.0f;
+  g.max_active = 1;
+  g.max_tiles = int((T + kPrefillTokens - 1) / kPrefillTokens);
+  g.n_slots = int(T);
+  const bool prefill = g.act != ACT_F32 && T > 16;
+  return hip_status(launch_moe_gemm(g, prefill, s));
 }
 
 }  // extern "C"

@@ -92,6 +92,12 @@ struct GemmArgs {
 };
 hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream);
 
+// The routing tables of a dense layer seen as one expert with all T tokens
+// (offsets, active list, prefill tiles) and, if zero_bias is set, N zero
+// bias values of zero_bias_bytes each.
+hipError_t launch_linear_setup(int T, int32_t* offsets, int32_t* active, int32_t* tile_off, int4* tiles,
+                               void* zero_bias, int N, int zero_bias_bytes, hipStream_t stream);
+
 struct CombineArgs {
   const void* Y;         // (T*k, H) in sorted order: bf16 (y_bf16) or fp32
   int y_bf16;

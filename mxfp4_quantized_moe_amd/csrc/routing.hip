@@ -512,6 +512,42 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint4* __restrict_
   q[i] = make_uint2(pack_e4m3x4(f[0], f[1], f[2], f[3]), pack_e4m3x4(f[4], f[5], f[6], f[7]));
 }
 
+// ------------------------------------------------------------- dense layer
+//
+// A dense layer runs through the grouped GEMMs as one expert that every
+// token routes to once: expert 0 owns sorted rows 0 .. T-1 (the token rows
+// themselves), in ceil(T / kPrefillTokens) prefill tiles.
+
+__global__ __launch_bounds__(256) void linear_setup_kernel(int T, int32_t* offsets, int32_t* active, int32_t* tile_off,
+                                                           int4* tiles, void* zero_bias, int N, int zero_bias_bytes) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int ntiles = (T + kPrefillTokens - 1) / kPrefillTokens;
+  if (i == 0) {
+    offsets[0] = 0;
+    offsets[1] = T;
+    active[0] = 1;
+    active[1] = 0;
+    tile_off[0] = 0;
+    tile_off[1] = ntiles;
+  }
+  if (i < ntiles) tiles[i] = make_int4(0, i * kPrefillTokens, min(kPrefillTokens, T - i * kPrefillTokens), 0);
+  if (zero_bias && i < N) {
+    if (zero_bias_bytes == 2)
+      static_cast<uint16_t*>(zero_bias)[i] = 0;
+    else
+      static_cast<float*>(zero_bias)[i] = 0.f;
+  }
+}
+
+hipError_t launch_linear_setup(int T, int32_t* offsets, int32_t* active, int32_t* tile_off, int4* tiles,
+                               void* zero_bias, int N, int zero_bias_bytes, hipStream_t stream) {
+  const int ntiles = (T + kPrefillTokens - 1) / kPrefillTokens;
+  const int n = ntiles > N ? ntiles : N;
+  linear_setup_kernel<<<dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream>>>(T, offsets, active, tile_off, tiles,
+                                                                               zero_bias, N, zero_bias_bytes);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8_t* q, hipStream_t stream) {
   const int64_t n8 = n / 8;  // n is a multiple of 32
   if (n8 == 0) return hipSuccess;

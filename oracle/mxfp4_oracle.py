@@ -74,6 +74,7 @@ __all__ = [
     "fp8_quant_dequant",
     "calibrate_fp8",
     "routing_margin",
+    "mxfp4_linear",
 ]
 
 # ---------------------------------------------------------------------------
@@ -421,6 +422,26 @@ def moe_forward(
         return out, dict(idx=idx, w=w, logits=logits, counts=counts, offsets=offsets,
                          sorted_slots=sorted_slots, slot_pos=slot_pos, h=h_all, Y=Y)
     return out
+
+
+def mxfp4_linear(x: np.ndarray, blocks: np.ndarray, scales: np.ndarray, bias, act_dtype: str) -> np.ndarray:
+    """A weight-only MXFP4 dense layer (KerasFormers "mxfp4" page, "As a
+    quantize_model scheme": a Dense kernel is stored as MXFP4 blocks and
+    scales, dequantised on the fly, and must have a contracting dimension
+    that is a multiple of 32; the bias keeps full precision as in the
+    GPT-OSS experts of the next section).
+
+    y = x W^T + b in float64, W = mxfp4_unpack(blocks, scales) (N, K).
+    x: (T, K) in act_dtype storage; bias: (N,) in act_dtype storage or None.
+    Returns (T, N) float64, unrounded."""
+    xf = widen(x, act_dtype)
+    if xf.ndim != 2 or blocks.ndim != 3 or xf.shape[1] != blocks.shape[1] * 32:
+        raise ValueError("x (T, K) and blocks (N, K/32, 16) must agree on K")
+    W = mxfp4_unpack(blocks, scales)
+    y = xf @ W.T
+    if bias is not None:
+        y = y + widen(bias, act_dtype)
+    return y
 
 
 def moe_forward_dense(layer, x: np.ndarray, act_dtype: str) -> np.ndarray:

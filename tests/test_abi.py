@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(B.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mxmoe_version() == 2
+    assert lib.mxmoe_version() == 3
     for s in range(9):
         assert lib.mxmoe_status_string(s)
 
@@ -155,8 +155,12 @@ def test_workspace_bytes_grows_with_tokens(lib):
     a = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 64, ctypes.byref(o))
     b = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 4096, ctypes.byref(o))
     assert 0 < a < b
-    # dominated by the per-slot intermediate h (bf16) and Y (fp32)
-    assert b >= 4096 * 4 * (2880 * 2 + 2880 * 4)
+    # dominated by the per-slot intermediate h and the expert outputs Y (both
+    # bf16 with bf16 activations)
+    assert b >= 4096 * 4 * (2880 * 2 + 2880 * 2)
+    f = lib.moe_mxfp4_workspace_bytes(ctypes.byref(_layer(E=32, H=2880, I=2880, top_k=4, param_dtype=0)), 4096,
+                                      ctypes.byref(_opts(act_dtype=0)))
+    assert f >= 4096 * 4 * (2880 * 4 + 2880 * 4)  # fp32 activations: fp32 h and Y
 
 
 def test_route_and_calibrate_validation(lib):
@@ -190,3 +194,25 @@ def test_binding_has_no_cpu_fallback(tmp_path):
             B.load_library(str(tmp_path / "nope.so"))
     finally:
         B._lib = saved
+
+
+def test_linear_validation(lib):
+    s = None
+
+    def call(x=P, T=8, K=64, wb=P, wsc=P, layout=0, bias=None, N=64, act=1, out=P, ws=P, ws_bytes=1 << 20):
+        return lib.mxfp4_linear(x, T, K, wb, wsc, layout, bias, N, act, out, ws, ws_bytes, s)
+
+    assert call(K=48) == SHAPE        # contracting dim not a multiple of 32 ("a clear error")
+    assert call(K=0) == SHAPE
+    assert call(N=40) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert call(act=3) == DTYPE
+    assert call(layout=5) == VALUE
+    assert call(wb=None) == NULL
+    assert call(x=P + 2) == ALIGN
+    assert call(bias=P + 8) == ALIGN
+    assert call(T=0, x=None, out=None, ws=None) == OK  # empty batch: no-op
+    need = lib.mxfp4_linear_workspace_bytes(8, 64, 1)
+    assert need > 0
+    assert call(ws_bytes=need - 1) == WS
+    assert lib.mxfp4_linear_workspace_bytes(8, 64, 7) == 0

@@ -472,3 +472,44 @@ def test_fp8_mode_error_is_fp8_sized():
     q = O.moe_forward(case.layer, case.x, "bf16", fp8=True, x_scale=s_x, h_scale=s_h)
     rel = np.max(np.abs(q - ref)) / np.max(np.abs(ref))
     assert 1e-3 < rel < 0.15  # e4m3 has 3 mantissa bits: a few percent, not zero
+
+
+# ------------------------------------------------------------ dense MXFP4 linear
+
+
+def test_linear_exact_integer_closed_form():
+    """Grid weights at scale byte 127 (value 1) times small integer inputs:
+    every product and sum is an exact multiple of 1/2, so y is the int64
+    product of the doubled weights with x, halved, plus an integer bias."""
+    rng = np.random.default_rng(7)
+    T, K, N = 9, 96, 40
+    codes = rng.integers(0, 16, size=(N, K))
+    twice = np.array([0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12], dtype=np.int64)  # 2 x e2m1 value
+    nib = codes.reshape(N, K // 32, 16, 2)
+    blocks = (nib[..., 0] | (nib[..., 1] << 4)).astype(np.uint8)
+    scales = np.full((N, K // 32), 127, dtype=np.uint8)
+    x = rng.integers(-8, 9, size=(T, K)).astype(np.float32)
+    b = rng.integers(-5, 6, size=N).astype(np.float32)
+    y = O.mxfp4_linear(x, blocks, scales, b, "f32")
+    exact = (x.astype(np.int64) @ twice[codes].T) / 2.0 + b
+    assert np.array_equal(y, exact)
+    assert np.array_equal(O.mxfp4_linear(x, blocks, scales, None, "f32"), exact - b)
+
+
+def test_linear_rejects_mismatched_k():
+    blocks = np.zeros((4, 2, 16), dtype=np.uint8)
+    scales = np.zeros((4, 2), dtype=np.uint8)
+    with pytest.raises(ValueError):
+        O.mxfp4_linear(np.zeros((3, 48), np.float32), blocks, scales, None, "f32")
+
+
+def test_linear_is_the_down_projection_of_the_layer():
+    """With one expert, top-1 and the identity router weight of 1, the
+    layer's down step is this linear on h: check the linear against the
+    layer's own parts (Y = h W_d^T + b_d) on a tiny random layer."""
+    case = W.small_case(3, 1, 64, 32, 1, 5, act_dtype="f32")
+    out, parts = O.moe_forward(case.layer, case.x, "f32", return_parts=True)
+    L = case.layer
+    y = O.mxfp4_linear(parts["h"].astype(np.float32), L.down_blocks[0], L.down_scales[0], L.down_bias[0], "f32")
+    assert np.allclose(y, parts["Y"], rtol=1e-6, atol=1e-6)
+    assert np.allclose(out, parts["Y"])  # top-1 of one expert: weight 1

@@ -196,6 +196,30 @@ def unpack_20b(seed: int = 0, E: int = 32, H: int = 2880, I: int = 2880) -> Unpa
     return UnpackCase(f"unpack_20b_e{E}", [(gub, gus), (db, ds)])
 
 
+@dataclass
+class LinearCase:
+    name: str
+    x: np.ndarray        # (T, K) in act_dtype storage
+    blocks: np.ndarray   # (N, K/32, 16) uint8
+    scales: np.ndarray   # (N, K/32) uint8
+    bias: Optional[np.ndarray]  # (N,) in act_dtype storage
+    act_dtype: str
+
+
+def linear_case(seed: int, T: int, K: int, N: int, act_dtype: str = BF16, bias: bool = True,
+                scale_lo: int = 120, scale_hi: int = 126) -> LinearCase:
+    """A weight-only MXFP4 dense layer and its input.  Draw order: blocks,
+    scales, bias, x; distributions as the expert weights (nibbles uniform,
+    scales on [lo, hi]), bias N(0, 0.01), x N(0, 1)."""
+    assert K % 32 == 0
+    rng = np.random.default_rng(seed)
+    blocks = rng.integers(0, 256, size=(N, K // 32, 16), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, size=(N, K // 32), dtype=np.uint8)
+    b = _real(rng, (N,), 0.01, act_dtype) if bias else None
+    x = _real(rng, (T, K), 1.0, act_dtype)
+    return LinearCase(f"linear_s{seed}_t{T}_k{K}_n{N}_{act_dtype}", x, blocks, scales, b, act_dtype)
+
+
 def random_weights(seed: int, rows: int, k: int, std: float = 1.0, dtype: str = F32) -> np.ndarray:
     """A dense weight matrix to be packed (pack parity cases)."""
     rng = np.random.default_rng(seed)
