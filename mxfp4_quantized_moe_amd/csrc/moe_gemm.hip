@@ -790,6 +790,17 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
     boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
   }
+  // The workgroup's kTiledRows bias values go to LDS by one DMA of wave 0,
+  // issued before every chunk load: the first chunk's wait covers it and the
+  // first barrier publishes it, so the epilogue finds it without a memory
+  // round trip (lanes past the stripe read zeros).
+  __shared__ __align__(16) uint8_t sBias[1024];
+  static_assert(kTiledRows * 2 <= 1024, "one DMA covers the stripe's bias");
+  if (wave == 0) {
+    const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
+    const int r = stripe * kTiledRows + 8 * lane;
+    dma16(br, (8 * lane < kTiledRows && r < a.R) ? uint32_t(r) * 2u : kOOB, sBias);
+  }
   uint4 aq[S][RT];   // weight pieces per stage
   uint32_t sw[S];    // scale dword per stage
 
@@ -917,13 +928,11 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
       static_cast<uint32_t*>(a.out)[0] = x;
     }
 
-    // bias of this lane's 4 output rows per row tile (raw bf16 bits)
-    const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if (rt < rt_active) {
-        const int r0 = grow + 16 * rt + 4 * g;
-        const uint2 q = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, uint32_t(r0) * 2u, 0, 0));
+        // bias of this lane's 4 output rows (raw bf16 bits)
+        const uint2 q = *reinterpret_cast<const uint2*>(sBias + 2 * (wave * 16 * RT + 16 * rt + 4 * g));
 #pragma unroll
         for (int nt = 0; nt < NA; ++nt) {
           const int j = nt * 16 + r16;
