@@ -21,11 +21,13 @@ namespace mxmoe {
 // product with A = W_r rows (experts) and B = x rows (tokens); the KW waves
 // of the workgroup split the contracting dimension into interleaved
 // 128-wide chunks and their partial sums are added in a fixed order in LDS,
-// so the logits are deterministic.  KW = 4 when there are many token
-// groups; a decode-sized batch (few groups) uses 16 waves so that the chain
-// of dependent weight loads per wave stays short.  Inside a chunk, lane group g (lanes 16g..16g+15) of the
-// MFMA covers K = 128c + 32g + [0, 32): the same permutation of K is applied
-// to both operands, which leaves the dot products unchanged.
+// so the logits are deterministic.  KW = 8 when there are many token groups
+// (E <= 128); a decode-sized batch (few groups) uses up to 16 waves so that
+// the chain of dependent weight loads per wave stays short.  In MFMA step s
+// of a chunk, lane group g (lanes 16g .. 16g+15) holds K = 128c + 32s + 8g
+// .. +8 (bf16), so the lane groups of a row read adjacent bytes: any
+// permutation of K applied to both operands leaves the dot products
+// unchanged.
 
 constexpr int kRouteTokens = 16;
 // K-splitting waves per 16-token group for large batches (sweep knob)
@@ -59,12 +61,20 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
   for (int rt = 0; rt < MRT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int c = wave; c < nchunks; c += KW) {
-    const int kb = 128 * c + 32 * g;  // start of this lane group's 32 K values
-    const uint32_t kofs = kb < H ? uint32_t(kb) * EB : kOOB;
+    // load s of lane group g covers K = 128c + (32s + 8g) .. +8 (bf16) or
+    // 128c + (16s + 4g) .. +4 (fp32): the four lane groups of a row read 64
+    // contiguous bytes per instruction.  Each step's K range is a multiple
+    // of 16 long and H of 32, so a step lies wholly inside or outside H.
+    uint32_t kofs[XL];
+#pragma unroll
+    for (int s = 0; s < XL; ++s) {
+      const int k0 = 128 * c + (BF16 ? 32 : 16) * s;
+      kofs[s] = k0 < H ? uint32_t(k0 + (BF16 ? 8 : 4) * g) * EB : kOOB;
+    }
     // every load of the chunk is issued before its first MFMA
     uint4 xq[XL];
 #pragma unroll
-    for (int s = 0; s < XL; ++s) xq[s] = buf_load_b128(xs, oob_add(xrow, oob_add(kofs, 16u * s)));
+    for (int s = 0; s < XL; ++s) xq[s] = buf_load_b128(xs, oob_add(xrow, kofs[s]));
 #pragma unroll
     for (int grp = 0; grp < NG; ++grp) {
       if (grp * RG < nrt) {  // uniform across the workgroup
@@ -74,7 +84,7 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
           const int e = (grp * RG + r) * 16 + r16;
           const uint32_t wrow = e < E ? uint32_t(e) * row_bytes : kOOB;
 #pragma unroll
-          for (int s = 0; s < XL; ++s) wq[r][s] = buf_load_b128(wsrc, oob_add(wrow, oob_add(kofs, 16u * s)));
+          for (int s = 0; s < XL; ++s) wq[r][s] = buf_load_b128(wsrc, oob_add(wrow, kofs[s]));
         }
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
