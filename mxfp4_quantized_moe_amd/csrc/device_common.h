@@ -16,6 +16,21 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // Largest top_k the kernels handle (the ABI limit).
 constexpr int MAX_TOPK_DEV = 8;
 
+// Compiler-only ordering point for memory operations (emits nothing).  It
+// keeps the compiler from sinking loads towards their first use, so a batch
+// of loads is in flight together, and from moving a load across an explicit
+// vmcnt wait that counts the loads of one pipeline stage.
+__device__ __forceinline__ void order_point() { __asm__ __volatile__("" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  order_point();
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  order_point();
+}
+
 // ---------------------------------------------------------------- scalars
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }

@@ -390,20 +390,6 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, const uint8_t* lds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_dst), 16, off, 0, 0, 0);
 }
 
-// Compiler-only ordering point for memory operations (emits nothing).  The
-// explicit vmcnt waits count loads per chunk, so the compiler must not mix
-// the loads of two chunks or move a load across a wait.
-__device__ __forceinline__ void order_point() { __asm__ __volatile__("" ::: "memory"); }
-
-// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  order_point();
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  order_point();
-}
-
 template <int ACT, int PHASE, bool TILED>
 __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs a) {
   static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "prefill path takes bf16 or fp8 activations");

@@ -24,10 +24,22 @@ namespace mxmoe {
 // so the logits are deterministic.  KW = 8 when there are many token groups
 // (E <= 128); a decode-sized batch (few groups) uses up to 16 waves so that
 // the chain of dependent weight loads per wave stays short.  In MFMA step s
-// of a chunk, lane group g (lanes 16g .. 16g+15) holds K = 128c + 32s + 8g
-// .. +8 (bf16), so the lane groups of a row read adjacent bytes: any
-// permutation of K applied to both operands leaves the dot products
-// unchanged.
+// of chunk c, lane group g (lanes 16g .. 16g+15) holds K = 128c + 32s + 8g
+// .. +8 (bf16): any permutation of K applied to both operands leaves the
+// dot products unchanged.  All loads of a row-tile group are in flight before its first
+// MFMA (a scheduling barrier): left to itself the scheduler hoists each MFMA
+// up to its load and waits there, which serialises one L2 round trip per row
+// tile and step.
+//
+// The loads themselves are coalesced: in load s of a row tile, lane l reads
+// row l/4 at K granule (16 bytes) 4s + l%4, so each lane quad reads 64
+// contiguous bytes of one row (one cache access instead of four).  A lane
+// transpose through ds_bpermute (destination lane 16g + r takes source lane
+// 4r + g) then gives every lane the MFMA fragment described above.
+//
+// Partial logits sit in LDS as [wave][row tile][g][token][i] (accumulator
+// element i of lane (g, token) is expert 16*rt + 4g + i), so the 16 lanes of
+// one lane group store 256 contiguous bytes.
 
 constexpr int kRouteTokens = 16;
 // K-splitting waves per 16-token group for large batches (sweep knob)
@@ -37,17 +49,155 @@ constexpr int kRouteTokens = 16;
 
 // RG row tiles of 16 experts have their loads issued together, NG groups
 // cover E <= 16 * RG * NG.
+// ------------------------------------------------------ top-k selection
+//
+// Order of the experts: larger logit first, the lower index first among
+// equal logits (a NaN logit counts as -inf).  Both parts sit in one 64-bit
+// key that compares as an unsigned integer: the high word is the logit
+// mapped onto uint32 in the same order (-0 taken as +0, which ties with it
+// anyway), the low word is ~expert.  Key 0 ranks below every expert.
+//
+// Each of the L lanes of a token keeps the KM best keys of its strided
+// share of the logits as a sorted list; the lists are then merged pairwise,
+// log2(L) times, until every lane holds the KM best of all E.  Merging two
+// sorted lists A, B of disjoint experts: C[j] = max(A[j], B[KM-1-j]) is the
+// KM best of the union as a bitonic sequence, which a bitonic merge network
+// sorts.  Pairing: DPP row rotations by 1, 2, 4, 8 inside a 16-lane row
+// (lane i then holds lanes i..i-15 of its row, each merge combining disjoint
+// sets), then lane XOR 16 and 32 across rows.
+
+__device__ __forceinline__ uint64_t expert_key(float x, int e) {
+  x = (x != x) ? -INFINITY : (x == 0.f ? 0.f : x);
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t(o) << 32) | uint32_t(~uint32_t(e));
+}
+
+__device__ __forceinline__ float key_logit(uint64_t k) {
+  const uint32_t o = uint32_t(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ int key_expert(uint64_t k) { return int(~uint32_t(k)); }
+
+template <int KM>
+__device__ __forceinline__ void list_insert(uint64_t (&l)[KM], uint64_t x) {
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const uint64_t hi = l[j] > x ? l[j] : x;
+    x = l[j] > x ? x : l[j];
+    l[j] = hi;
+  }
+}
+
+template <int KM>
+__device__ __forceinline__ void list_merge(uint64_t (&l)[KM], const uint64_t (&p)[KM]) {
+#pragma unroll
+  for (int j = 0; j < KM; ++j) l[j] = l[j] > p[KM - 1 - j] ? l[j] : p[KM - 1 - j];
+#pragma unroll
+  for (int st = KM / 2; st >= 1; st >>= 1) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if ((j & st) == 0) {
+        const uint64_t a0 = l[j], a1 = l[j + st];
+        l[j] = a0 > a1 ? a0 : a1;
+        l[j + st] = a0 > a1 ? a1 : a0;
+      }
+    }
+  }
+}
+
+// the key of lane (i - R) mod 16 of this lane's 16-lane row
+template <int R>
+__device__ __forceinline__ uint64_t row_rotated(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(x)), 0x120 + R, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(x >> 32)), 0x120 + R, 0xF, 0xF, false);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+template <int R, int KM>
+__device__ __forceinline__ void merge_rotated(uint64_t (&l)[KM]) {
+  uint64_t p[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) p[j] = row_rotated<R>(l[j]);
+  list_merge<KM>(l, p);
+}
+
+template <int KM>
+__device__ __forceinline__ void merge_xor(uint64_t (&l)[KM], int mask) {
+  uint64_t p[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(l[j])), mask));
+    const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(l[j] >> 32)), mask));
+    p[j] = (uint64_t(hi) << 32) | lo;
+  }
+  list_merge<KM>(l, p);
+}
+
+// Top-k of token t's logits (lg[256*(e/16) + 64*((e/4)%4) + e%4] for expert
+// e) by the L lanes of its group, then the softmax over those k; the first
+// k lanes of the group write the outputs.
+template <int KM, int L>
+__device__ __forceinline__ void topk_softmax(const RouteArgs& a, const float* lg, int t) {
+  static_assert(L == 16 || L == 32 || L == 64, "a token's lanes are whole 16-lane rows");
+  const int q = threadIdx.x % L;
+  uint64_t l[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) l[j] = 0;
+  for (int e = q; e < a.E; e += L) list_insert<KM>(l, expert_key(lg[256 * (e >> 4) + 64 * ((e >> 2) & 3) + (e & 3)], e));
+  merge_rotated<1, KM>(l);
+  merge_rotated<2, KM>(l);
+  merge_rotated<4, KM>(l);
+  merge_rotated<8, KM>(l);
+  if constexpr (L >= 32) merge_xor<KM>(l, 16);
+  if constexpr (L >= 64) merge_xor<KM>(l, 32);
+
+  const float m = key_logit(l[0]);
+  float den = 0.f;
+  float ex[KM];
+#pragma unroll
+  for (int kk = 0; kk < KM; ++kk) {
+    ex[kk] = kk < a.top_k ? expf(key_logit(l[kk]) - m) : 0.f;
+    den += ex[kk];
+  }
+#pragma unroll
+  for (int kk = 0; kk < KM; ++kk) {
+    if (kk < a.top_k && q == kk) {
+      const float w = ex[kk] / den;
+      const int64_t o = int64_t(t) * a.top_k + kk;
+      const int e = key_expert(l[kk]);
+      a.idx[o] = e;
+      a.wts[o] = w;
+      if (a.idx_out) a.idx_out[o] = e;
+      if (a.wts_out) a.wts_out[o] = w;
+    }
+  }
+}
+
+// The 16 bytes of source lane (perm / 4), for every lane.
+__device__ __forceinline__ uint4 lane_permute(uint4 v, int perm) {
+  return make_uint4(uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(v.x))),
+                    uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(v.y))),
+                    uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(v.z))),
+                    uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(v.w))));
+}
+
 template <bool BF16, int RG, int NG, int KW>
 __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
   extern __shared__ float part[];  // [KW][16][E]
+  __shared__ float sbias[256];     // b_r, read before the contraction
+  constexpr int kLanesPerToken = 4 * KW;
   constexpr int EB = BF16 ? 2 : 4;          // bytes per element of x and W_r
   constexpr int XL = BF16 ? 4 : 8;          // 16-byte loads per lane per row and chunk
   constexpr int MRT = RG * NG;              // row tiles held in registers
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
+  const int g = lane >> 4, r16 = lane & 15;  // MFMA fragment position
+  const int lrow = lane >> 2, lq = lane & 3;  // coalesced load position
+  const int perm = (4 * r16 + g) * 4;         // bpermute byte index
   const int E = a.E, H = a.H;
   const int t0 = blockIdx.x * kRouteTokens;
-  const int tok = t0 + r16;
+  const int tok = t0 + lrow;
   const int nrt = (E + 15) >> 4;
   const int nchunks = (H + 127) >> 7;
   const uint32_t row_bytes = uint32_t(H) * EB;
@@ -56,20 +206,22 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
   const rsrc_t wsrc = make_rsrc(a.w_r, uint32_t(E) * row_bytes);
   const uint32_t xrow = tok < a.T ? uint32_t(tok) * row_bytes : kOOB;
 
+  for (int e = threadIdx.x; e < E; e += 64 * KW) sbias[e] = load_param(a.b_r, e, a.act_bf16);
+
   f32x4_t acc[MRT];
 #pragma unroll
   for (int rt = 0; rt < MRT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int c = wave; c < nchunks; c += KW) {
-    // load s of lane group g covers K = 128c + (32s + 8g) .. +8 (bf16) or
-    // 128c + (16s + 4g) .. +4 (fp32): the four lane groups of a row read 64
-    // contiguous bytes per instruction.  Each step's K range is a multiple
-    // of 16 long and H of 32, so a step lies wholly inside or outside H.
+    // after the transpose, step s of lane group g covers K = 128c + (32s +
+    // 8g) .. +8 (bf16) or 128c + (16s + 4g) .. +4 (fp32).  Each step's K
+    // range is a multiple of 16 long and H of 32, so a step lies wholly
+    // inside or outside H.
     uint32_t kofs[XL];
 #pragma unroll
     for (int s = 0; s < XL; ++s) {
       const int k0 = 128 * c + (BF16 ? 32 : 16) * s;
-      kofs[s] = k0 < H ? uint32_t(k0 + (BF16 ? 8 : 4) * g) * EB : kOOB;
+      kofs[s] = k0 < H ? uint32_t(k0 + (BF16 ? 8 : 4) * lq) * EB : kOOB;
     }
     // every load of the chunk is issued before its first MFMA
     uint4 xq[XL];
@@ -78,14 +230,26 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
 #pragma unroll
     for (int grp = 0; grp < NG; ++grp) {
       if (grp * RG < nrt) {  // uniform across the workgroup
+        // the previous group's MFMAs stay ahead of this group's loads
+        if (grp > 0) __builtin_amdgcn_sched_barrier(0);
         uint4 wq[RG][XL];
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
-          const int e = (grp * RG + r) * 16 + r16;
+          const int e = (grp * RG + r) * 16 + lrow;
           const uint32_t wrow = e < E ? uint32_t(e) * row_bytes : kOOB;
 #pragma unroll
           for (int s = 0; s < XL; ++s) wq[r][s] = buf_load_b128(wsrc, oob_add(wrow, kofs[s]));
         }
+        // neither loads nor MFMAs cross this point
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp == 0) {
+#pragma unroll
+          for (int s = 0; s < XL; ++s) xq[s] = lane_permute(xq[s], perm);
+        }
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int s = 0; s < XL; ++s) wq[r][s] = lane_permute(wq[r][s], perm);
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
           f32x4_t& ac = acc[grp * RG + r];
@@ -108,110 +272,50 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
     }
   }
 
-  // partial logits: accumulator element i of row tile rt is expert
-  // rt*16 + 4g + i for token r16
-  float* mine = part + (wave * kRouteTokens + r16) * E;
+  // partial logits of this wave (experts past E hold zeros: their W_r rows
+  // read as zero)
+  const int tile = kRouteTokens * 16 * nrt;
+  float* mine = part + wave * tile + 64 * g + 4 * r16;
 #pragma unroll
-  for (int rt = 0; rt < MRT; ++rt) {
-    if (rt < nrt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = rt * 16 + 4 * g + i;
-        if (e < E) mine[e] = acc[rt][i];
-      }
-    }
-  }
+  for (int rt = 0; rt < MRT; ++rt)
+    if (rt < nrt) *reinterpret_cast<f32x4_t*>(mine + 256 * rt) = acc[rt];
   __syncthreads();
-  const int tile = kRouteTokens * E;
+  // fixed-order sum over the waves, plus the bias
   for (int j = threadIdx.x; j < tile; j += 64 * KW) {
-    const int e = j % E;
-    float s = part[j];
-    for (int w = 1; w < KW; ++w) s += part[w * tile + j];
-    part[j] = s + load_param(a.b_r, e, a.act_bf16);
+    const int e = 16 * (j >> 8) + 4 * ((j >> 6) & 3) + (j & 3);
+    if (e < E) {
+      float s = part[j];
+      for (int w = 1; w < KW; ++w) s += part[w * tile + j];
+      part[j] = s + sbias[e];
+    }
   }
   __syncthreads();
 
-  // top-k + softmax: wave w handles tokens w, w + KW, ... of the tile
-  for (int tl = wave; tl < kRouteTokens; tl += KW) {
-    const int t = t0 + tl;
-    if (t >= a.T) break;
-    const float* lg = part + tl * E;
-    float v[4];
-    unsigned picked = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      float x = e < E ? lg[e] : -INFINITY;
-      v[j] = (x != x) ? -INFINITY : x;  // a NaN logit ranks lowest
-    }
-    float sel_v[MAX_TOPK_DEV];
-    int sel_i[MAX_TOPK_DEV];
-#pragma unroll
-    for (int kk = 0; kk < MAX_TOPK_DEV; ++kk) {
-      sel_v[kk] = -INFINITY;
-      sel_i[kk] = 0;
-      if (kk < a.top_k) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = lane + 64 * j;
-          if (e < E && !((picked >> j) & 1u)) {
-            if (v[j] > bv || (v[j] == bv && e < bi)) {
-              bv = v[j];
-              bi = e;
-            }
-          }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          const float ov = __shfl_xor(bv, off);
-          const int oi = __shfl_xor(bi, off);
-          if (ov > bv || (ov == bv && oi < bi)) {
-            bv = ov;
-            bi = oi;
-          }
-        }
-        sel_v[kk] = bv;
-        sel_i[kk] = bi;
-        if ((bi & 63) == lane) picked |= 1u << (bi >> 6);
-      }
-    }
-    const float m = sel_v[0];
-    float den = 0.f;
-    float ex[MAX_TOPK_DEV];
-#pragma unroll
-    for (int kk = 0; kk < MAX_TOPK_DEV; ++kk) {
-      ex[kk] = kk < a.top_k ? expf(sel_v[kk] - m) : 0.f;
-      den += ex[kk];
-    }
-#pragma unroll
-    for (int kk = 0; kk < MAX_TOPK_DEV; ++kk) {
-      if (kk < a.top_k && lane == kk) {
-        const float w = ex[kk] / den;
-        const int64_t o = int64_t(t) * a.top_k + kk;
-        a.idx[o] = sel_i[kk];
-        a.wts[o] = w;
-        if (a.idx_out) a.idx_out[o] = sel_i[kk];
-        if (a.wts_out) a.wts_out[o] = w;
-      }
-    }
+  // top-k + softmax: 4*KW lanes per token, all 16 tokens at once
+  const int tl = threadIdx.x / kLanesPerToken;
+  if (t0 + tl < a.T) {
+    if (a.top_k <= 4) topk_softmax<4, kLanesPerToken>(a, part + 4 * tl, t0 + tl);
+    else topk_softmax<MAX_TOPK_DEV, kLanesPerToken>(a, part + 4 * tl, t0 + tl);
   }
 }
 
 template <bool BF16, int KW>
 static void launch_route_typed(const RouteArgs& a, unsigned grid, hipStream_t stream) {
-  const size_t lds = size_t(KW) * kRouteTokens * a.E * sizeof(float);
+  const size_t lds = size_t(KW) * kRouteTokens * ((a.E + 15) & ~15) * sizeof(float);
   const dim3 g(grid), b(64 * KW);
   // register tiles sized to E (fp32 operands take twice the registers)
   if (a.E <= 32)
     route_kernel<BF16, 2, 1, KW><<<g, b, lds, stream>>>(a);
-  else if (a.E <= 64)
-    route_kernel<BF16, 4, 1, KW><<<g, b, lds, stream>>>(a);
-  else if (a.E <= 128)
-    route_kernel<BF16, (BF16 ? 8 : 4), (BF16 ? 1 : 2), KW><<<g, b, lds, stream>>>(a);
-  else if constexpr (KW == 4)  // E > 128 always takes 4 waves (LDS bound)
-    route_kernel<BF16, 4, 4, KW><<<g, b, lds, stream>>>(a);
+  else if constexpr (BF16 || KW <= 8) {  // fp32 past E = 32: at most 8 waves (registers)
+    if (a.E <= 64)
+      route_kernel<BF16, 4, 1, KW><<<g, b, lds, stream>>>(a);
+    else if constexpr (KW <= 8) {  // E > 64 takes at most 8 waves (LDS bound)
+      if (a.E <= 128)
+        route_kernel<BF16, (BF16 ? 8 : 4), (BF16 ? 1 : 2), KW><<<g, b, lds, stream>>>(a);
+      else if constexpr (KW == 4)  // E > 128 always takes 4 waves
+        route_kernel<BF16, 4, 4, KW><<<g, b, lds, stream>>>(a);
+    }
+  }
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
@@ -219,14 +323,17 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const unsigned grid = unsigned((a.T + kRouteTokens - 1) / kRouteTokens);
   // few token groups: more waves split K (shorter chains of dependent
   // loads per wave); many groups: 8 waves each up to E = 128.
-  // The LDS of the partial logits, KW x 16 x E floats, stays <= 64 KB.
-  if (grid < 64 && a.E <= 64) {
+  // The LDS of the partial logits, KW x 16 x E floats (E rounded up to a
+  // multiple of 16), stays <= 64 KB.
+  // 16 waves take E <= 64 (bf16) or E <= 32 (fp32: twice the registers).
+  const int e16 = a.act_bf16 ? 64 : 32;
+  if (grid < 64 && a.E <= e16) {
     if (a.act_bf16) launch_route_typed<true, 16>(a, grid, stream);
     else launch_route_typed<false, 16>(a, grid, stream);
   } else if (grid < 64 && a.E <= 128) {
     if (a.act_bf16) launch_route_typed<true, 8>(a, grid, stream);
     else launch_route_typed<false, 8>(a, grid, stream);
-  } else if (MXMOE_ROUTE_KW_LARGE == 16 && a.E <= 64) {
+  } else if (MXMOE_ROUTE_KW_LARGE == 16 && a.E <= e16) {
     if (a.act_bf16) launch_route_typed<true, 16>(a, grid, stream);
     else launch_route_typed<false, 16>(a, grid, stream);
   } else if (MXMOE_ROUTE_KW_LARGE >= 8 && a.E <= 128) {

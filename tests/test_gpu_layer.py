@@ -159,6 +159,7 @@ def test_fp8_calibration_scales(dev):
     (24, 200, 96, 64, 3, 70, "f32"),     # router: fp32 with E > 128
     (25, 8, 64, 32, 2, 3000, "bf16"),    # grouping: > 2048 slots (one workgroup per expert)
     (26, 256, 64, 32, 8, 600, "bf16"),   # grouping: > 2048 slots over 256 experts
+    (27, 48, 160, 64, 4, 40, "f32"),     # router: fp32 with 32 < E <= 64 and few tokens (8 waves)
 ])
 @pytest.mark.parametrize("layout", ["rows", "tiled"])
 def test_small_shapes(dev, seed, E, H, I, k, T, act, layout):
