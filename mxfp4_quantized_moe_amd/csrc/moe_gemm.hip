@@ -97,6 +97,18 @@ __device__ __forceinline__ WBuf expert_weights(const GemmArgs& a, int e) {
 // lane group read 16 distinct bank groups.
 __device__ __forceinline__ int piece_slot(int r, int b) { return r * 4 + (b ^ ((r >> 2) & 3)); }
 
+// Position of 16-byte piece p (K = 8p .. 8p+7 of the chunk) in the 256-byte
+// LDS row of token tok, bf16 token tiles.  gfx950 serves ds_read_b128 16
+// lanes at a time against 64 banks of 4 bytes; the 16 lanes of a group are
+// the 4-lane blocks of one half-wave whose lane bits 2..4 have the same
+// parity (measured with SQ_LDS_BANK_CONFLICT over lane patterns chosen to
+// tell the candidate groupings apart), and a group is conflict-free when its
+// 16 slots are distinct modulo 16.  In MFMA step st lane (g, r) reads piece
+// 4g + st of token r; XOR-ing the piece with the token's low 4 bits rotated
+// by 2 makes every group conflict-free for all four steps (checked for all
+// of them against that grouping).
+__device__ __forceinline__ int bf16_piece_pos(int tok, int p) { return p ^ (((tok << 2) | ((tok >> 2) & 3)) & 15); }
+
 // Block `block` of weight row `row`; zero when either is out of range.
 __device__ __forceinline__ AFrag load_a(const WBuf& w, int row, int block) {
   const bool ok = row < w.R && block < w.nb;
@@ -371,7 +383,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
 //     group read 16 different bank groups.  Scale bytes go to registers
 //     (one aligned dword per row tile).
 //   * B (activations): 64 gathered token rows of the chunk, pieces
-//     XOR-swizzled by token the same way.
+//     XOR-swizzled by token (bf16_piece_pos for bf16).
 // Each wave decodes its own weight rows into bf16 registers right before
 // the MFMAs; a wave whose rows all lie past the matrix skips its MFMAs, so
 // a partial last row stripe costs little.  The work list is (token tile, row stripe) with the stripe
@@ -485,7 +497,7 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   for (int jj = 0; jj < BLOADS; ++jj) {
     const int tok = TPL * (BLOADS * wave + jj) + lane / PPR;
     const int slot = lane % PPR;
-    const int p = ACT == ACT_BF16 ? (slot ^ (tok & 15)) : (slot ^ ((tok >> 1) & 7));
+    const int p = ACT == ACT_BF16 ? bf16_piece_pos(tok, slot) : (slot ^ ((tok >> 1) & 7));
     bpiece[jj] = p;
     const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
     boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
@@ -570,7 +582,7 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
             bf16x8_t b[NA];
 #pragma unroll
             for (int nt = 0; nt < NA; ++nt)
-              b[nt] = *reinterpret_cast<const bf16x8_t*>(sb + ((nt * 16 + r16) * 16 + ((4 * g + st) ^ r16)) * 16);
+              b[nt] = *reinterpret_cast<const bf16x8_t*>(sb + ((nt * 16 + r16) * 16 + bf16_piece_pos(r16, 4 * g + st)) * 16);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
               const bf16x8_t av = fp4x8_to_bf16x8(dword(aq[rt], st), e8m0_as_scale_operand(ascb[rt]));
@@ -763,7 +775,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
 
   // B DMA: the 128 tokens are NBL loads of TPL tokens; wave w carries loads
   // BLOADS*w .. BLOADS*w + BLOADS-1; lane i carries token TPL*load + i/PPR,
-  // piece slot i%PPR, XOR-swizzled by token.
+  // piece slot i%PPR, XOR-swizzled by token (bf16_piece_pos for bf16).
   // (clast: the last chunk whose part of this piece lies inside K)
   uint32_t boff[BLOADS];
   int clast[BLOADS];
@@ -771,7 +783,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   for (int jj = 0; jj < BLOADS; ++jj) {
     const int tok = TPL * (BLOADS * wave + jj) + lane / PPR;
     const int slot = lane % PPR;
-    const int p = ACT == ACT_BF16 ? (slot ^ (tok & 15)) : (slot ^ ((tok >> 1) & 7));
+    const int p = ACT == ACT_BF16 ? bf16_piece_pos(tok, slot) : (slot ^ ((tok >> 1) & 7));
     clast[jj] = (K - 1 - p * (16 / EB)) >> 7;
     const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
     boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
@@ -832,7 +844,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
             bf16x8_t b[NA];
 #pragma unroll
             for (int nt = 0; nt < NA; ++nt)
-              b[nt] = *reinterpret_cast<const bf16x8_t*>(sb + ((nt * 16 + r16) * 16 + ((4 * g + st) ^ r16)) * 16);
+              b[nt] = *reinterpret_cast<const bf16x8_t*>(sb + ((nt * 16 + r16) * 16 + bf16_piece_pos(r16, 4 * g + st)) * 16);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
               const bf16x8_t av = fp4x8_to_bf16x8(dword(aq[u][rt], st), e8m0_as_scale_operand(ascb[rt]));
