@@ -104,6 +104,8 @@ def make_case(name: str):
         return W.decode_20b(T=int(name.rsplit("t", 1)[1]))
     if name == "fp8_20b_t2048":
         return W.fp8_20b()
+    if name.startswith("bf16_20b_t"):
+        return W.bf16_20b(T=int(name.rsplit("t", 1)[1]))
     if name == "tiny":
         return W.tiny()
     raise SystemExit(f"unknown workload {name}")
@@ -114,11 +116,13 @@ def layer_bytes(layer) -> int:
                                   layer.down_scales, layer.down_bias))
 
 
-def expert_gemm_bytes(case, phase: int, n_active: int) -> int:
+def expert_gemm_bytes(case, phase: int, n_active: int, dense: bool = False) -> int:
     """Algorithmic HBM bytes of one grouped-GEMM launch: the routed experts'
-    packed weights, scales and biases once, the activations in and out once."""
+    packed weights, scales and biases once, the activations in and out once
+    (rows per token: top_k routed, E dense)."""
     L = case.layer
-    H, I, k, T = L.H, L.I, L.top_k, case.T
+    H, I, T = L.H, L.I, case.T
+    k = L.E if dense else L.top_k
     pb = 2 if L.param_dtype == "bf16" else 4
     ab = 1 if case.fp8 else (2 if case.act_dtype == "bf16" else 4)
     if phase == 0:
@@ -128,14 +132,15 @@ def expert_gemm_bytes(case, phase: int, n_active: int) -> int:
     return n_active * w + T * k * I * ab + T * k * H * 4
 
 
-def expert_gemm_flops(case, phase: int) -> int:
+def expert_gemm_flops(case, phase: int, dense: bool = False) -> int:
     L = case.layer
-    slots = case.T * L.top_k
+    slots = case.T * (L.E if dense else L.top_k)
     return 2 * slots * (2 * L.I) * L.H if phase == 0 else 2 * slots * L.H * L.I
 
 
-def cpu_baseline(case, budget_s: float):
-    """The oracle as it stands on a bounded token slice of the workload."""
+def cpu_baseline(case, budget_s: float, dense: bool = False):
+    """The oracle as it stands on a bounded token slice of the workload (its
+    all-experts forward for the dense path)."""
     import numpy as np
 
     import oracle as O
@@ -163,7 +168,10 @@ def cpu_baseline(case, budget_s: float):
             break
         sub = W.MoECase(case.name, case.layer, case.x[rows].copy(), case.act_dtype, case.fp8, case.x_calib)
         t0 = time.perf_counter()
-        O.moe_forward(sub.layer, sub.x, sub.act_dtype, **scales)
+        if dense and not case.fp8:
+            O.moe_forward_dense(sub.layer, sub.x, sub.act_dtype)
+        else:
+            O.moe_forward(sub.layer, sub.x, sub.act_dtype, **scales)
         elapsed += time.perf_counter() - t0
         done += rows.size
         if elapsed >= budget_s or done >= case.T:
@@ -171,7 +179,8 @@ def cpu_baseline(case, budget_s: float):
         n = min(n * 2, case.T - done)
     return {"value": done / elapsed, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {done} of {case.T} tokens of {case.name}, float64 NumPy ({blas}), "
-                      f"{elapsed:.1f} s, slices of doubling size each dequantising their routed experts"}
+                      f"{elapsed:.1f} s, slices of doubling size each dequantising "
+                      f"{'every expert' if dense and not case.fp8 else 'their routed experts'}"}
 
 
 # ------------------------------------------------------------ main legs
@@ -193,7 +202,8 @@ def bench_layer(args, dev):
         torch.cuda.synchronize()
     x = W.array_to_torch(case.x, dev)
     _, _, counts, _, _, _ = mx.moe_mxfp4_route(w0, x)
-    n_active = int((W.torch_to_array(counts) > 0).sum())
+    dense = args.path == "dense"
+    n_active = L.E if dense else int((W.torch_to_array(counts) > 0).sum())
     # identical weight copies: enough that a copy's routed experts were last
     # read more than 1 GB of traffic ago (past the 256 MB Infinity Cache)
     per_step = n_active * layer_bytes(L) // L.E
@@ -208,8 +218,9 @@ def bench_layer(args, dev):
         sc = mx.moe_mxfp4_calibrate_fp8(weights[0], W.array_to_torch(case.x_calib, dev))
         s = W.torch_to_array(sc)
         fp8_kw = dict(fp8=True, x_scale=float(s[0]), h_scale=float(s[1]))
-    ws = mx.alloc_workspace(weights[0], T, x.dtype, case.fp8)
+    ws = mx.alloc_workspace(weights[0], T, x.dtype, case.fp8, dense)
     out = torch.empty_like(x)
+    fp8_kw["dense"] = dense
 
     # a plain copy of known size: the reference point that scales the HBM
     # byte counters of a profiled run (bytes moved = 2 x 256 MiB)
@@ -249,15 +260,16 @@ def bench_layer(args, dev):
 
     # dominant kernel: the gate_up grouped GEMM (2/3 of the flops, 2/3 of the weight bytes)
     gu_s = float(gu_ms.mean()) * 1e-3
-    decode_shaped = T * L.top_k <= 16 * min(L.E, T * L.top_k) or case.act_dtype == "f32"
+    rows = T * (L.E if dense else L.top_k)
+    decode_shaped = rows <= 16 * min(L.E, rows) or case.act_dtype == "f32"
     if decode_shaped:
-        byts = expert_gemm_bytes(case, 0, n_active)
+        byts = expert_gemm_bytes(case, 0, n_active, dense)
         achieved = byts / gu_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_GBps"], "unit": "GB/s",
                 "frac": achieved / PEAK["hbm_GBps"]}
         algo = f"{byts} B per launch ({n_active} routed experts)"
     else:
-        fl = expert_gemm_flops(case, 0)
+        fl = expert_gemm_flops(case, 0, dense)
         peak = PEAK["fp8_TFLOPs"] if case.fp8 else PEAK["bf16_TFLOPs"]
         achieved = fl / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
@@ -281,13 +293,14 @@ def bench_layer(args, dev):
         "config": {"workload": case.name, "E": L.E, "top_k": L.top_k, "H": L.H, "I": L.I, "T": T,
                    "act": "fp8" if case.fp8 else case.act_dtype, "weight_layout": args.layout,
                    "weight_copies": copies,
+                   "expert_path": args.path,
                    "routed_experts": n_active},
         "roofline": roof,
         "stages_us": {name: float(v * 1e3) for name, v in zip(STAGES, avg)},
         "stages_note": "separate untimed pass with all stage events (each record adds a few us)",
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, dense)
     return res
 
 
@@ -391,6 +404,8 @@ def main():
     ap.add_argument("--copies", type=int, default=None, help="weight copies cycled through (default: >= 1 GB apart)")
     ap.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
                     help="expert weight order: tiled by mxfp4_tile at load (default) or the checkpoint row order")
+    ap.add_argument("--path", choices=("routed", "dense"), default="routed",
+                    help="experts per token: the routed top_k, or all of them (dense all-experts path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     args = ap.parse_args()

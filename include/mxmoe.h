@@ -59,7 +59,7 @@ typedef enum {
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* mxmoe_status_string(int32_t status);
 
-/* Interface version, bumped on any ABI change (currently 3). */
+/* Interface version, bumped on any ABI change (currently 4). */
 int32_t mxmoe_version(void);
 
 /*
@@ -205,7 +205,21 @@ typedef struct {
    * each record takes a few microseconds of stream time, so a caller timing
    * one stage passes only the two handles around it. */
   void* const* stage_events;
+  int32_t expert_path;   /* mxmoe_path_t: which experts each token passes through */
 } mxmoe_fwd_opts_t;
+
+/* Experts evaluated by the forward. */
+typedef enum {
+  /* each token through its top_k experts only (grouped by expert) */
+  MXMOE_PATH_ROUTED = 0,
+  /* every token through every expert, then the same top_k combine: the
+   * dense all-experts path of the KerasFormers "mxfp4" page ("As GPT-OSS's
+   * native format"), which its long prefills take when cheaper.  The output
+   * equals the routed path's up to the fp32 summation order inside the
+   * GEMMs (E/top_k times the GEMM work; rows T*E must fit the 32-bit
+   * buffer windows, else MXMOE_ERR_SHAPE). */
+  MXMOE_PATH_DENSE = 1
+} mxmoe_path_t;
 
 /* Number of handles stage_events points to. */
 #define MXMOE_STAGE_EVENTS 7
@@ -238,6 +252,10 @@ size_t moe_mxfp4_workspace_bytes(const mxmoe_layer_t* layer, int64_t T, const mx
  * and both GEMMs run on scaled MXFP4 x FP8 matrix instructions with fp32
  * accumulation; the router still reads the unquantised x.
  *
+ * With expert_path = MXMOE_PATH_DENSE the two GEMMs run over all T*E
+ * (expert, token) pairs, row e*T + t, and the combine reads the top_k rows
+ * the router chose; the router and the combine are the routed path's.
+ *
  * The result is deterministic: identical inputs give identical bits.
  */
 mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* layer, const void* x, int64_t T, void* out,
@@ -256,7 +274,8 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* layer, const void* x, int6
  *                 expert, ascending slot id within an expert
  *   pos_out     : (T*top_k,) int32 row of each flat slot in sorted_out
  * Any of the five outputs may be NULL.  opts->act_dtype gives x's dtype;
- * the FP8 fields are ignored.  Workspace as for moe_mxfp4_forward.
+ * the FP8 fields and expert_path are ignored (the grouping is the routed
+ * one).  Workspace as for moe_mxfp4_forward.
  */
 mxmoe_status_t moe_mxfp4_route(const mxmoe_layer_t* layer, const void* x, int64_t T,
                                const mxmoe_fwd_opts_t* opts, int32_t* idx_out, float* w_out,

@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     MoEWeights,
     MXFP4Linear,
     MxmoeError,
+    PATH_DENSE,
+    PATH_ROUTED,
     alloc_workspace,
     load_library,
     moe_mxfp4_calibrate_fp8,

@@ -84,8 +84,12 @@ class FwdOpts(ctypes.Structure):
         ("topk_idx_out", ctypes.c_void_p),
         ("topk_w_out", ctypes.c_void_p),
         ("stage_events", ctypes.c_void_p),
+        ("expert_path", ctypes.c_int32),
     ]
 
+
+# mxmoe_path_t
+PATH_ROUTED, PATH_DENSE = 0, 1
 
 STAGE_EVENTS = 7
 STAGES = ("router", "grouping", "quant_fp8", "gate_up_swiglu", "down", "combine")
@@ -312,41 +316,47 @@ class MoEWeights:
 
 
 def _opts(act_dtype: torch.dtype, fp8: bool, x_scale: float, h_scale: float, idx_out=None, w_out=None,
-          stage_events=None) -> FwdOpts:
+          stage_events=None, dense: bool = False) -> FwdOpts:
     return FwdOpts(act_dtype=_dtype_code(act_dtype), fp8_act=1 if fp8 else 0, x_scale=x_scale, h_scale=h_scale,
                    topk_idx_out=_ptr(idx_out), topk_w_out=_ptr(w_out),
-                   stage_events=ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None)
+                   stage_events=ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None,
+                   expert_path=PATH_DENSE if dense else PATH_ROUTED)
 
 
-def workspace_bytes(layer: MoEWeights, T: int, act_dtype: torch.dtype, fp8: bool = False) -> int:
+def workspace_bytes(layer: MoEWeights, T: int, act_dtype: torch.dtype, fp8: bool = False,
+                    dense: bool = False) -> int:
     d = layer.descriptor()
-    o = _opts(act_dtype, fp8, 1.0, 1.0)
+    o = _opts(act_dtype, fp8, 1.0, 1.0, dense=dense)
     n = load_library().moe_mxfp4_workspace_bytes(ctypes.byref(d), T, ctypes.byref(o))
     if n == 0 and T > 0:
         raise MxmoeError(3, "invalid layer or token count")
     return int(n)
 
 
-def alloc_workspace(layer: MoEWeights, T: int, act_dtype: torch.dtype, fp8: bool = False) -> torch.Tensor:
-    n = workspace_bytes(layer, T, act_dtype, fp8)
+def alloc_workspace(layer: MoEWeights, T: int, act_dtype: torch.dtype, fp8: bool = False,
+                    dense: bool = False) -> torch.Tensor:
+    n = workspace_bytes(layer, T, act_dtype, fp8, dense)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=layer.router_w.device)
 
 
 def moe_mxfp4_forward(layer: MoEWeights, x: torch.Tensor, fp8: bool = False, x_scale: float = 1.0,
                       h_scale: float = 1.0, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, topk_idx_out: Optional[torch.Tensor] = None,
-                      topk_w_out: Optional[torch.Tensor] = None, stage_events=None) -> torch.Tensor:
-    """The routed MXFP4 MoE layer on x (T, H); returns out (T, H).
+                      topk_w_out: Optional[torch.Tensor] = None, stage_events=None,
+                      dense: bool = False) -> torch.Tensor:
+    """The MXFP4 MoE layer on x (T, H); returns out (T, H).
 
+    dense: every token through every expert (MXMOE_PATH_DENSE) instead of
+    its top_k; the combine is the same.
     stage_events: optional ctypes array of STAGE_EVENTS hipEvent_t handles
     (see include/mxmoe.h) recorded around the stages on the current stream."""
     T = int(x.shape[0])
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
-        workspace = alloc_workspace(layer, T, x.dtype, fp8)
+        workspace = alloc_workspace(layer, T, x.dtype, fp8, dense)
     d = layer.descriptor()
-    o = _opts(x.dtype, fp8, x_scale, h_scale, topk_idx_out, topk_w_out, stage_events)
+    o = _opts(x.dtype, fp8, x_scale, h_scale, topk_idx_out, topk_w_out, stage_events, dense)
     _check(load_library().moe_mxfp4_forward(ctypes.byref(d), _ptr(x), T, _ptr(out), ctypes.byref(o),
                                             _ptr(workspace), workspace.numel(), _stream(x.device)))
     return out

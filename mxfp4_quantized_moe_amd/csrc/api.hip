@@ -34,10 +34,16 @@ struct Workspace {
   size_t idx, wts, counts, offsets, active, tile_off, tiles, sorted, sorted_tok, pos, calib, xq, h, y, total;
 };
 
-// Byte offsets of the forward's scratch buffers inside the caller's workspace.
-Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8) {
+// Rows of the two GEMMs: the T*k routed (token, expert) pairs, or all T*E
+// of them on the dense path.
+int64_t gemm_rows(const mxmoe_layer_t* L, int64_t T, bool dense) { return T * (dense ? L->E : L->top_k); }
+
+// Byte offsets of the forward's scratch buffers inside the caller's workspace
+// (`rows` = GEMM rows, T*k routed or T*E dense).
+Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8, int64_t rows) {
   Workspace w{};
   const size_t slots = size_t(T) * size_t(k);
+  const size_t grows = size_t(rows);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -50,16 +56,16 @@ Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8)
   w.offsets = take(size_t(E + 1) * 4);
   w.active = take(size_t(E + 1) * 4);
   w.tile_off = take(size_t(E + 1) * 4);
-  const size_t active_max = slots < size_t(E) ? slots : size_t(E);
-  w.tiles = take((slots + kPrefillTokens - 1) / kPrefillTokens * 16 + active_max * 16);
+  const size_t active_max = grows < size_t(E) ? grows : size_t(E);
+  w.tiles = take((grows + kPrefillTokens - 1) / kPrefillTokens * 16 + active_max * 16);
   w.sorted = take(slots * 4);
-  w.sorted_tok = take(slots * 4);
+  w.sorted_tok = take(grows * 4);
   w.pos = take(slots * 4);
   w.calib = take(16);
   w.xq = take(fp8 ? size_t(T) * size_t(H) : 0);
   const size_t hb = fp8 ? 1 : (act_dtype == MXMOE_BF16 ? 2 : 4);
-  w.h = take(slots * size_t(I) * hb);
-  w.y = take(slots * size_t(H) * (act_dtype == MXMOE_BF16 ? 2 : 4));  // Y: bf16 with bf16 activations
+  w.h = take(grows * size_t(I) * hb);
+  w.y = take(grows * size_t(H) * (act_dtype == MXMOE_BF16 ? 2 : 4));  // Y: bf16 with bf16 activations
   w.total = o;
   return w;
 }
@@ -94,6 +100,7 @@ mxmoe_status_t check_opts(const mxmoe_layer_t* L, const mxmoe_fwd_opts_t* o, boo
       if (!std::isfinite(1.0f / o->x_scale) || !std::isfinite(1.0f / o->h_scale)) return MXMOE_ERR_VALUE;
     }
   }
+  if (use_fp8 && o->expert_path != MXMOE_PATH_ROUTED && o->expert_path != MXMOE_PATH_DENSE) return MXMOE_ERR_VALUE;
   if (o->topk_idx_out && !aligned16(o->topk_idx_out)) return MXMOE_ERR_ALIGN;
   if (o->topk_w_out && !aligned16(o->topk_w_out)) return MXMOE_ERR_ALIGN;
   return MXMOE_OK;
@@ -103,10 +110,10 @@ mxmoe_status_t check_opts(const mxmoe_layer_t* L, const mxmoe_fwd_opts_t* o, boo
 // through 32-bit range-checked buffer windows below 2^31 bytes.
 constexpr int64_t kMaxWindow = (int64_t(1) << 31) - 1;
 
-mxmoe_status_t check_tokens(const mxmoe_layer_t* L, int64_t T) {
+mxmoe_status_t check_tokens(const mxmoe_layer_t* L, int64_t T, bool dense = false) {
   if (T < 0) return MXMOE_ERR_SHAPE;
-  if (T * int64_t(L->top_k) > kMaxSlots) return MXMOE_ERR_SHAPE;
-  const int64_t slots = T * L->top_k;
+  if (T * int64_t(dense ? L->E : L->top_k) > kMaxSlots) return MXMOE_ERR_SHAPE;
+  const int64_t slots = gemm_rows(L, T, dense);
   if (T * int64_t(L->H) * 4 > kMaxWindow || slots * int64_t(L->I) * 4 > kMaxWindow) return MXMOE_ERR_SHAPE;
   if (int64_t(2) * L->I * L->H / 2 > kMaxWindow) return MXMOE_ERR_SHAPE;
   int64_t bb, sb;  // one expert's tiled gate_up (the larger of the two matrices)
@@ -127,7 +134,8 @@ T* at(void* base, size_t off) {
 // Router + grouping into the workspace; optional copies for the caller.
 hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act_dtype, const Workspace& w,
                        void* ws, int32_t* idx_out, float* w_out, int32_t* counts_out, int32_t* offsets_out,
-                       int32_t* sorted_buf, int32_t* pos_buf, hipStream_t s, hipEvent_t mid = nullptr) {
+                       int32_t* sorted_buf, int32_t* pos_buf, hipStream_t s, hipEvent_t mid = nullptr,
+                       bool dense = false) {
   RouteArgs ra{};
   ra.x = x;
   ra.w_r = L->router_w;
@@ -144,6 +152,21 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   hipError_t e = launch_route(ra, s);
   if (e != hipSuccess) return e;
   if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
+  if (dense) {
+    DenseGroupArgs da{};
+    da.idx = ra.idx;
+    da.T = int(T);
+    da.E = L->E;
+    da.top_k = L->top_k;
+    da.counts = at<int32_t>(ws, w.counts);
+    da.offsets = at<int32_t>(ws, w.offsets);
+    da.sorted_tok = at<int32_t>(ws, w.sorted_tok);
+    da.pos = at<int32_t>(ws, w.pos);
+    da.active = at<int32_t>(ws, w.active);
+    da.tile_off = at<int32_t>(ws, w.tile_off);
+    da.tiles = at<int4>(ws, w.tiles);
+    return launch_dense_group(da, s);
+  }
   PermuteArgs pa{};
   pa.idx = ra.idx;
   pa.n_slots = int(T * L->top_k);
@@ -162,7 +185,8 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   return launch_permute(pa, s);
 }
 
-GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t T, int act, int phase) {
+GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t T, int act, int phase,
+                   bool dense = false) {
   GemmArgs g{};
   g.act = act;
   g.phase = phase;
@@ -175,7 +199,7 @@ GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t
   g.active = at<int32_t>(ws, w.active);
   g.tile_off = at<int32_t>(ws, w.tile_off);
   g.tiles = at<int4>(ws, w.tiles);
-  const int64_t slots = T * L->top_k;
+  const int64_t slots = gemm_rows(L, T, dense);
   g.n_slots = int(slots);
   g.max_active = int(slots < L->E ? slots : L->E);
   g.max_tiles = int((slots + kPrefillTokens - 1) / kPrefillTokens + g.max_active);
@@ -205,9 +229,9 @@ GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t
 
 // Decode-shaped kernels while experts see few tokens on average; the
 // LDS-staged MFMA tiles beyond that.
-bool use_prefill(const mxmoe_layer_t* L, int64_t T, int act) {
+bool use_prefill(const mxmoe_layer_t* L, int64_t T, int act, bool dense = false) {
   if (act == ACT_F32) return false;
-  const int64_t slots = T * L->top_k;
+  const int64_t slots = gemm_rows(L, T, dense);
   const int64_t active = slots < L->E ? slots : L->E;
   return slots > 16 * active;
 }
@@ -231,7 +255,7 @@ const char* mxmoe_status_string(int32_t s) {
   }
 }
 
-int32_t mxmoe_version(void) { return 3; }
+int32_t mxmoe_version(void) { return 4; }
 
 mxmoe_status_t mxfp4_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t rows, int64_t k, void* out,
                             int32_t out_dtype, void* stream) {
@@ -285,9 +309,12 @@ mxmoe_status_t mxfp4_tile(const uint8_t* blocks, const uint8_t* scales, int64_t 
 }
 
 size_t moe_mxfp4_workspace_bytes(const mxmoe_layer_t* L, int64_t T, const mxmoe_fwd_opts_t* o) {
-  if (check_layer(L) != MXMOE_OK || !o || check_tokens(L, T) != MXMOE_OK) return 0;
+  if (check_layer(L) != MXMOE_OK || !o) return 0;
+  if (o->expert_path != MXMOE_PATH_ROUTED && o->expert_path != MXMOE_PATH_DENSE) return 0;
+  const bool dense = o->expert_path == MXMOE_PATH_DENSE;
+  if (check_tokens(L, T, dense) != MXMOE_OK) return 0;
   if (o->act_dtype != MXMOE_F32 && o->act_dtype != MXMOE_BF16) return 0;
-  return layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, o->fp8_act == 1).total;
+  return layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, o->fp8_act == 1, gemm_rows(L, T, dense)).total;
 }
 
 mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t T, void* out,
@@ -295,12 +322,13 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
   mxmoe_status_t st = check_layer(L);
   if (st != MXMOE_OK) return st;
   if ((st = check_opts(L, o, true)) != MXMOE_OK) return st;
-  if ((st = check_tokens(L, T)) != MXMOE_OK) return st;
+  const bool dense = o->expert_path == MXMOE_PATH_DENSE;
+  if ((st = check_tokens(L, T, dense)) != MXMOE_OK) return st;
   if (T == 0) return MXMOE_OK;
   if (!x || !out || !ws) return MXMOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return MXMOE_ERR_ALIGN;
   const bool fp8 = o->fp8_act == 1;
-  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, fp8);
+  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, fp8, gemm_rows(L, T, dense));
   if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -308,7 +336,7 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
   auto mark = [&](int i) { return ev && ev[i] ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   if (mark(0) != hipSuccess) return MXMOE_ERR_HIP;
   hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
-                             nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr);
+                             nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr, dense);
   if (e != hipSuccess) return MXMOE_ERR_HIP;
   if (mark(2) != hipSuccess) return MXMOE_ERR_HIP;
   const int act = fp8 ? ACT_FP8 : (o->act_dtype == MXMOE_BF16 ? ACT_BF16 : ACT_F32);
@@ -319,8 +347,8 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
     if (e != hipSuccess) return MXMOE_ERR_HIP;
   }
   if (mark(3) != hipSuccess) return MXMOE_ERR_HIP;
-  const bool prefill = use_prefill(L, T, act);
-  GemmArgs g0 = gemm_args(L, w, ws, T, act, 0);
+  const bool prefill = use_prefill(L, T, act, dense);
+  GemmArgs g0 = gemm_args(L, w, ws, T, act, 0, dense);
   g0.bsrc = fp8 ? at<void>(ws, w.xq) : x;
   if (fp8) {
     g0.acc_scale = o->x_scale;
@@ -328,7 +356,7 @@ mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t 
   }
   if ((e = launch_moe_gemm(g0, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
   if (mark(4) != hipSuccess) return MXMOE_ERR_HIP;
-  GemmArgs g1 = gemm_args(L, w, ws, T, act, 1);
+  GemmArgs g1 = gemm_args(L, w, ws, T, act, 1, dense);
   if (fp8) g1.acc_scale = o->h_scale;
   if ((e = launch_moe_gemm(g1, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
   if (mark(5) != hipSuccess) return MXMOE_ERR_HIP;
@@ -358,7 +386,7 @@ mxmoe_status_t moe_mxfp4_route(const mxmoe_layer_t* L, const void* x, int64_t T,
   const void* outs[] = {x, ws, idx_out, w_out, counts_out, offsets_out, sorted_out, pos_out};
   for (const void* p : outs)
     if (p && !aligned16(p)) return MXMOE_ERR_ALIGN;
-  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, o->fp8_act == 1);
+  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, o->fp8_act == 1, gemm_rows(L, T, false));
   if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
   return hip_status(run_routing(L, x, T, o->act_dtype, w, ws, idx_out, w_out, counts_out, offsets_out, sorted_out,
                                 pos_out, static_cast<hipStream_t>(stream)));
@@ -373,7 +401,7 @@ mxmoe_status_t moe_mxfp4_calibrate_fp8(const mxmoe_layer_t* L, const void* x, in
   if (T < 1) return MXMOE_ERR_SHAPE;
   if (!x || !scales_out || !ws) return MXMOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(scales_out) || !aligned16(ws)) return MXMOE_ERR_ALIGN;
-  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, MXMOE_BF16, false);
+  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, MXMOE_BF16, false, gemm_rows(L, T, false));
   if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = run_routing(L, x, T, MXMOE_BF16, w, ws, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s);

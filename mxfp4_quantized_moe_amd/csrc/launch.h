@@ -63,6 +63,22 @@ struct PermuteArgs {
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 
+// Grouping of the dense all-experts path: rows e*T + t for every expert e
+// and token t (sorted_tok, offsets, counts, active, tiles), and the row of
+// each routed slot, pos[t*k + j] = idx[t*k + j] * T + t.
+struct DenseGroupArgs {
+  const int32_t* idx;   // (T*k) routed experts
+  int T, E, top_k;
+  int32_t* counts;      // (E)
+  int32_t* offsets;     // (E+1)
+  int32_t* sorted_tok;  // (T*E)
+  int32_t* pos;         // (T*k)
+  int32_t* active;      // (E+1)
+  int32_t* tile_off;    // (E+1)
+  int4* tiles;          // (E * ceil(T / kPrefillTokens))
+};
+hipError_t launch_dense_group(const DenseGroupArgs& a, hipStream_t stream);
+
 // FP8 static quantisation of a (rows, cols) bf16 tensor to e4m3 codes.
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8_t* q, hipStream_t stream);
 

@@ -665,6 +665,47 @@ hipError_t launch_linear_setup(int T, int32_t* offsets, int32_t* active, int32_t
   return hipGetLastError();
 }
 
+// ---------------------------------------------------- dense all-experts
+//
+// Grouping of the dense path: row e*T + t is token t for expert e, every
+// expert active with all T tokens; the combine finds slot (t, j) at row
+// idx[t, j] * T + t.
+
+__global__ __launch_bounds__(256) void dense_group_kernel(DenseGroupArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int T = a.T, E = a.E;
+  const int64_t rows = int64_t(T) * E;
+  const int ntiles = (T + kPrefillTokens - 1) / kPrefillTokens;
+  if (i < rows) a.sorted_tok[i] = int(i % T);
+  if (i < int64_t(T) * a.top_k) {
+    int e = a.idx[i];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    a.pos[i] = e * T + int(i / a.top_k);
+  }
+  if (i <= E) {
+    a.offsets[i] = int(i) * T;
+    a.tile_off[i] = int(i) * ntiles;
+    if (i < E) {
+      a.counts[i] = T;
+      a.active[1 + i] = int(i);
+    } else {
+      a.active[0] = E;
+    }
+  }
+  if (i < int64_t(E) * ntiles) {
+    const int e = int(i / ntiles), q = int(i % ntiles);
+    a.tiles[i] = make_int4(e, e * T + q * kPrefillTokens, min(kPrefillTokens, T - q * kPrefillTokens), 0);
+  }
+}
+
+hipError_t launch_dense_group(const DenseGroupArgs& a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const int64_t rows = int64_t(a.T) * a.E;
+  const int64_t n = rows > a.E + 1 ? rows : a.E + 1;
+  dense_group_kernel<<<dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8_t* q, hipStream_t stream) {
   const int64_t n8 = n / 8;  // n is a multiple of 32
   if (n8 == 0) return hipSuccess;

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(B.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mxmoe_version() == 3
+    assert lib.mxmoe_version() == 4
     for s in range(9):
         assert lib.mxmoe_status_string(s)
 
@@ -147,6 +147,26 @@ def test_forward_token_and_workspace_validation(lib):
     need8 = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 8, ctypes.byref(_opts(fp8_act=1)))
     assert need8 > need - 8 * 64 * 2 * 1
     assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(_layer(H=40)), 8, ctypes.byref(_opts())) == 0
+
+
+def test_dense_path_validation(lib):
+    L = _layer(E=32, H=2880, I=2880, top_k=4)
+    assert _fwd(lib, _layer(), opts=_opts(expert_path=2)) == VALUE
+    assert _fwd(lib, _layer(), opts=_opts(expert_path=-1)) == VALUE
+    routed = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 64, ctypes.byref(_opts()))
+    dense = lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 64, ctypes.byref(_opts(expert_path=1)))
+    # h and Y for all T*E (expert, token) rows instead of T*k
+    assert dense >= routed + 64 * (32 - 4) * (2880 * 2 + 2880 * 2)
+    assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 64, ctypes.byref(_opts(expert_path=3))) == 0
+    # T*E rows of h beyond the 32-bit buffer window: the dense path refuses
+    # a long prefill over many experts that the routed path takes
+    big = _layer(E=128, H=2880, I=2880, top_k=4)
+    assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(big), 4096, ctypes.byref(_opts())) > 0
+    assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(big), 4096, ctypes.byref(_opts(expert_path=1))) == 0
+    assert _fwd(lib, big, T=4096, opts=_opts(expert_path=1)) == SHAPE
+    # routing only: the grouping is always the routed one
+    assert lib.moe_mxfp4_route(ctypes.byref(big), P, 4096, ctypes.byref(_opts(expert_path=7)), None, None, None,
+                               None, None, None, P, 0, None) == WS
 
 
 def test_workspace_bytes_grows_with_tokens(lib):

@@ -25,7 +25,7 @@ def dev():
     return device()
 
 
-def run_gpu(case, dev, x_scale=1.0, h_scale=1.0, want_route=True, layout="rows"):
+def run_gpu(case, dev, x_scale=1.0, h_scale=1.0, want_route=True, layout="rows", dense=False):
     import torch
     import mxfp4_quantized_moe_amd as mx
 
@@ -37,7 +37,7 @@ def run_gpu(case, dev, x_scale=1.0, h_scale=1.0, want_route=True, layout="rows")
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     out = mx.moe_mxfp4_forward(wts, x, fp8=case.fp8, x_scale=x_scale, h_scale=h_scale, topk_idx_out=idx,
-                               topk_w_out=w)
+                               topk_w_out=w, dense=dense)
     torch.cuda.synchronize()
     res = dict(out=W.torch_to_array(out), idx=W.torch_to_array(idx), w=W.torch_to_array(w))
     if want_route:

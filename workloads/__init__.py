@@ -134,6 +134,16 @@ def decode_20b(T: int = 64, seed: int = 0) -> MoECase:
     return MoECase(f"gpt_oss_20b_decode_t{T}", layer, x, BF16)
 
 
+def bf16_20b(T: int, seed: int = 0) -> MoECase:
+    """The 20b layer of decode_20b (same generator and seed) with T bf16
+    tokens ~N(0, 1): the routed/dense crossover sweep over T."""
+    assert T >= 1
+    rng = np.random.default_rng(seed)
+    layer = make_layer(rng, 32, 2880, 2880, 4, BF16, 120, 126, 0.01, 0.02, 0.01)
+    x = _real(rng, (T, 2880), 1.0, BF16)
+    return MoECase(f"gpt_oss_20b_bf16_t{T}", layer, x, BF16)
+
+
 def prefill_120b(T: int = 4096, seed: int = 0) -> MoECase:
     """gpt-oss-120b-shaped prefill: E=128, top-4, H=I=2880, T=4096, bf16.
 
