@@ -741,6 +741,18 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     else if constexpr (u == 2) return sB2;
     else return sB3;
   };
+  // bf16 tiles of at most 64 tokens run a deeper ring in the same LDS: four
+  // stages of 64 token rows (16 KB) in sB0 and sB1, so three chunks are in
+  // flight while one is computed.  A short tile's few MFMAs cannot cover a
+  // chunk's load latency with one chunk ahead.
+  constexpr int SS = 4;                          // stages of a small tile
+  constexpr int SBLOADS = BLOADS / 2;            // its B loads per wave per chunk
+  static_assert(SS * (B_BYTES / 2) <= 2 * B_BYTES, "small stages fit in sB0 and sB1");
+  static_assert((SS - 2) * (RT + 1 + SBLOADS) < 64, "vmcnt range");
+  auto stage_small = [&](auto uc) -> uint8_t* {
+    constexpr int u = decltype(uc)::value;
+    return (u < 2 ? sB0 : sB1) + (u & 1) * (B_BYTES / 2);
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -773,21 +785,6 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
   const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
 
-  // B DMA: the 128 tokens are NBL loads of TPL tokens; wave w carries loads
-  // BLOADS*w .. BLOADS*w + BLOADS-1; lane i carries token TPL*load + i/PPR,
-  // piece slot i%PPR, XOR-swizzled by token (bf16_piece_pos for bf16).
-  // (clast: the last chunk whose part of this piece lies inside K)
-  uint32_t boff[BLOADS];
-  int clast[BLOADS];
-#pragma unroll
-  for (int jj = 0; jj < BLOADS; ++jj) {
-    const int tok = TPL * (BLOADS * wave + jj) + lane / PPR;
-    const int slot = lane % PPR;
-    const int p = ACT == ACT_BF16 ? bf16_piece_pos(tok, slot) : (slot ^ ((tok >> 1) & 7));
-    clast[jj] = (K - 1 - p * (16 / EB)) >> 7;
-    const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
-    boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
-  }
   // The workgroup's kTiledRows bias values go to LDS by one DMA of wave 0,
   // issued before every chunk load: the first chunk's wait covers it and the
   // first barrier publishes it, so the epilogue finds it without a memory
@@ -799,32 +796,58 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     const int r = stripe * kTiledRows + 8 * lane;
     dma16(br, (8 * lane < kTiledRows && r < a.R) ? uint32_t(r) * 2u : kOOB, sBias);
   }
-  uint4 aq[S][RT];   // weight pieces per stage
-  uint32_t sw[S];    // scale dword per stage
-
-  auto issue = [&](int c, auto stc) __attribute__((always_inline)) {
-    constexpr int u = decltype(stc)::value;
-    const bool cok = c < nc && wok;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      aq[u][rt] = buf_load_b128(wb.blk, cok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
-    sw[u] = buf_load_b32(wb.sc, cok ? uint32_t(((t0 >> 2) * nc + c) * 256 + lane * 4) : kOOB);
-    uint8_t* stb = stage_b(stc);
-#pragma unroll
-    for (int jj = 0; jj < BLOADS; ++jj) {
-      const bool kok = c <= clast[jj];
-      dma16(bsrc, oob_add(boff[jj], kok ? uint32_t(c) * KB : kOOB), stb + (BLOADS * wave + jj) * 1024);
-    }
-  };
-
   auto barrier = [&]() __attribute__((always_inline)) {
     order_point();
     __builtin_amdgcn_s_barrier();
     order_point();
   };
 
-  auto main_loop = [&](auto ntc) __attribute__((always_inline)) {
+  auto main_loop = [&](auto ntc, auto smc) __attribute__((always_inline)) {
     constexpr int NA = decltype(ntc)::value;  // 1 .. 8 active sub-tiles
+    constexpr bool SMALL = decltype(smc)::value != 0;
+    constexpr int SX = SMALL ? SS : S;           // stages of the ring
+    constexpr int BL = SMALL ? SBLOADS : BLOADS;  // B loads per wave per chunk
+    constexpr int LD = RT + 1 + BL;              // VMEM instructions per wave per chunk
+    static_assert(!SMALL || (ACT == ACT_BF16 && NA <= 4), "small ring: bf16 tiles of <= 64 tokens");
+    auto stage = [&](auto uc) -> uint8_t* {
+      if constexpr (SMALL) return stage_small(uc);
+      else return stage_b(uc);
+    };
+
+    // B DMA: the tile's 128 (64 in the small ring) tokens are loads of TPL
+    // tokens; wave w carries loads BL*w .. BL*w + BL-1; lane i carries token
+    // TPL*load + i/PPR, piece slot i%PPR, XOR-swizzled by token
+    // (bf16_piece_pos for bf16).  (clast: the last chunk whose part of this
+    // piece lies inside K)
+    uint32_t boff[BL];
+    int clast[BL];
+#pragma unroll
+    for (int jj = 0; jj < BL; ++jj) {
+      const int tok = TPL * (BL * wave + jj) + lane / PPR;
+      const int slot = lane % PPR;
+      const int p = ACT == ACT_BF16 ? bf16_piece_pos(tok, slot) : (slot ^ ((tok >> 1) & 7));
+      clast[jj] = (K - 1 - p * (16 / EB)) >> 7;
+      const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
+      boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
+    }
+    uint4 aq[SX][RT];   // weight pieces per stage
+    uint32_t sw[SX];    // scale dword per stage
+
+    auto issue = [&](int c, auto stc) __attribute__((always_inline)) {
+      constexpr int u = decltype(stc)::value;
+      const bool cok = c < nc && wok;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        aq[u][rt] = buf_load_b128(wb.blk, cok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
+      sw[u] = buf_load_b32(wb.sc, cok ? uint32_t(((t0 >> 2) * nc + c) * 256 + lane * 4) : kOOB);
+      uint8_t* stb = stage(stc);
+#pragma unroll
+      for (int jj = 0; jj < BL; ++jj) {
+        const bool kok = c <= clast[jj];
+        dma16(bsrc, oob_add(boff[jj], kok ? uint32_t(c) * KB : kOOB), stb + (BL * wave + jj) * 1024);
+      }
+    };
+
     f32x4_t acc[RT][NA];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -834,7 +857,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     auto compute = [&](auto stc) __attribute__((always_inline)) {
       constexpr int u = decltype(stc)::value;
       if (busy) {
-        const uint8_t* sb = stage_b(stc);
+        const uint8_t* sb = stage(stc);
         uint32_t ascb[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) ascb[rt] = (sw[u] >> (((t0 + rt) & 3) * 8)) & 0xFFu;
@@ -886,35 +909,35 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
       }
     };
 
-    // prologue: chunks 0 .. S-2 in flight, issued in chunk order
+    // prologue: chunks 0 .. SX-2 in flight, issued in chunk order
     order_point();
     issue(0, IC<0>{});
     order_point();
-    if constexpr (S > 2) { issue(1, IC<1>{}); order_point(); }
-    if constexpr (S > 3) { issue(2, IC<2>{}); order_point(); }
+    if constexpr (SX > 2) { issue(1, IC<1>{}); order_point(); }
+    if constexpr (SX > 3) { issue(2, IC<2>{}); order_point(); }
 
     // iteration c: wait for chunk c, barrier (its tokens have landed for
     // every wave, and chunk c-1's stage is free), refill that stage with
     // chunk c+S-1, compute chunk c.  Every iteration issues the same loads
     // (chunks past the end read zeros), so the wait count is fixed.
     auto iteration = [&](int c, auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value;  // c % S
-      wait_vmcnt<(S - 2) * LOADS>();
+      constexpr int u = decltype(uc)::value;  // c % SX
+      wait_vmcnt<(SX - 2) * LD>();
       barrier();
-      issue(c + S - 1, IC<(u + S - 1) % S>{});
+      issue(c + SX - 1, IC<(u + SX - 1) % SX>{});
       order_point();
       compute(IC<u>{});
     };
     int c0 = 0;
-    for (; c0 + S <= nc; c0 += S) {
+    for (; c0 + SX <= nc; c0 += SX) {
       iteration(c0 + 0, IC<0>{});
       iteration(c0 + 1, IC<1>{});
-      if constexpr (S > 2) iteration(c0 + 2, IC<2 % S>{});
-      if constexpr (S > 3) iteration(c0 + 3, IC<3 % S>{});
+      if constexpr (SX > 2) iteration(c0 + 2, IC<2 % SX>{});
+      if constexpr (SX > 3) iteration(c0 + 3, IC<3 % SX>{});
     }
     if (c0 + 0 < nc) iteration(c0 + 0, IC<0>{});
-    if (c0 + 1 < nc) iteration(c0 + 1, IC<1 % S>{});
-    if constexpr (S > 3) if (c0 + 2 < nc) iteration(c0 + 2, IC<2 % S>{});
+    if (c0 + 1 < nc) iteration(c0 + 1, IC<1 % SX>{});
+    if constexpr (SX > 3) if (c0 + 2 < nc) iteration(c0 + 2, IC<2 % SX>{});
     wait_vmcnt<0>();
     // Never true (slot counts are non-negative).  It keeps every weight
     // prefetch live: the vmcnt waits count loads, so none may be dropped as
@@ -922,7 +945,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     if (a.n_slots < 0) {
       uint32_t x = 0;
 #pragma unroll
-      for (int d = 0; d < S; ++d) x ^= aq[d][0].x ^ aq[d][1].y ^ aq[d][2].z ^ aq[d][3].w ^ sw[d];
+      for (int d = 0; d < SX; ++d) x ^= aq[d][0].x ^ aq[d][1].y ^ aq[d][2].z ^ aq[d][3].w ^ sw[d];
       static_cast<uint32_t*>(a.out)[0] = x;
     }
 
@@ -946,15 +969,16 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
       }
     }
   };
+  constexpr int SM = ACT == ACT_BF16 ? 1 : 0;  // tiles of <= 64 tokens take the small ring
   switch (na) {
-    case 1: main_loop(IC<1>{}); break;
-    case 2: main_loop(IC<2>{}); break;
-    case 3: main_loop(IC<3>{}); break;
-    case 4: main_loop(IC<4>{}); break;
-    case 5: main_loop(IC<5>{}); break;
-    case 6: main_loop(IC<6>{}); break;
-    case 7: main_loop(IC<7>{}); break;
-    default: main_loop(IC<8>{}); break;
+    case 1: main_loop(IC<1>{}, IC<SM>{}); break;
+    case 2: main_loop(IC<2>{}, IC<SM>{}); break;
+    case 3: main_loop(IC<3>{}, IC<SM>{}); break;
+    case 4: main_loop(IC<4>{}, IC<SM>{}); break;
+    case 5: main_loop(IC<5>{}, IC<0>{}); break;
+    case 6: main_loop(IC<6>{}, IC<0>{}); break;
+    case 7: main_loop(IC<7>{}, IC<0>{}); break;
+    default: main_loop(IC<8>{}, IC<0>{}); break;
   }
 }
 
