@@ -24,6 +24,8 @@ Workloads (synthetic, seeded; see workloads/):
   tiny                 E=4, top-2, H=I=64, T=8, fp32
   unpack_20b           mxfp4_unpack of the 20b expert tensors to bf16 (GB/s)
   linear_t4096_k2880_n5760  weight-only MXFP4 dense layer y = x W^T + b, bf16
+  fp8_linear_t4096_k2880_n5760  FP8 E4M3 W8A8 dense layer, static per-tensor scales
+  bf16_20b_t{T}        the 20b layer at any T (with --path dense: the all-experts path)
 """
 from __future__ import annotations
 
@@ -381,6 +383,53 @@ def bench_linear(args, dev):
                          "algorithmic": f"{fl} flop per call", "traffic": None}}
 
 
+def bench_fp8_linear(args, dev):
+    """The dense FP8 E4M3 layer (W8A8, static per-tensor scales): tokens/s
+    and TFLOP/s of the whole call (setup, x quantisation and the GEMM; HIP
+    events on the stream it runs on)."""
+    import numpy as np
+    import torch
+
+    import mxfp4_quantized_moe_amd as mx
+    import workloads as W
+
+    T, K, N = 4096, 2880, 5760
+    case = W.fp8_linear_case(0, T, K, N)
+    lin = mx.FP8Linear.from_codes(W.array_to_torch(case.w_codes, dev), case.w_scale, case.x_scale,
+                                  W.array_to_torch(case.bias, dev))
+    wbytes = lin.w_tiled.numel()
+    copies = min(64, -(-int(1.0e9) // wbytes) + 1) if args.copies is None else args.copies
+    lins = [lin] + [mx.FP8Linear(lin.w_tiled.clone(), N, K, lin.w_scale, lin.x_scale, lin.bias)
+                    for _ in range(copies - 1)]
+    x = W.array_to_torch(case.x, dev)
+    out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(mx.fp8_linear_workspace_bytes(T, K, N), 256), dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        lins[i % copies](x, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        lins[i % copies](x, out=out, workspace=ws)
+        ends[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    call_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
+    fl = 2 * T * K * N
+    achieved = fl / call_s / 1e12
+    return {"metric": "FP8 W8A8 dense linear tokens/s", "value": T * args.steps / (t1 - t0), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+            "data": "synthetic (seeded random e4m3 weight codes and bf16 activations, fixed static scales)",
+            "config": {"workload": f"fp8_linear_t{T}_k{K}_n{N}", "T": T, "K": K, "N": N, "weight_copies": copies},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK["fp8_TFLOPs"], "unit": "TFLOP/s",
+                         "frac": achieved / PEAK["fp8_TFLOPs"],
+                         "kernel": "whole call: setup + x quantisation + gemm_prefill_tiled_kernel<W8A8, phase 1>",
+                         "algorithmic": f"{fl} flop per call", "traffic": None}}
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
@@ -429,6 +478,8 @@ def main():
         res = bench_unpack(args, dev)
     elif args.workload == "linear_t4096_k2880_n5760":
         res = bench_linear(args, dev)
+    elif args.workload == "fp8_linear_t4096_k2880_n5760":
+        res = bench_fp8_linear(args, dev)
     else:
         res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)

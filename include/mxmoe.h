@@ -167,6 +167,39 @@ mxmoe_status_t mxfp4_linear(const void* x, int64_t T, int64_t K, const uint8_t* 
                             int32_t weight_layout, const void* bias, int64_t N, int32_t act_dtype, void* out,
                             void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Dense FP8 E4M3 layer with static per-tensor scales (W8A8): the attention
+ * projections of the gpt-oss-120b-mxfp4-fp8attn-v2 page ("Model Details";
+ * "Quantization Recipe", steps 1 and 2: weights and inputs in float8_e4m3fn,
+ * symmetric, one static scale per tensor, stored as weight_scale and
+ * input_scale next to the FP8 weight).
+ *
+ * fp8_tiled_bytes — bytes of the tiled FP8 order of an (N, K) weight.
+ * fp8_tile — copy w, (N, K) float8_e4m3fn codes in row-major order (device),
+ *   into that order (device): row tiles of 16 rows (N padded to a multiple
+ *   of 64) x chunks of 128 K (K padded with zero codes), 2 KB per (row tile,
+ *   chunk) in row-tile-major order; inside one, the 32 bytes of lane
+ *   l = 16g + r are row r's bytes 16g .. 16g+15, then 64+16g .. 64+16g+15, of
+ *   the chunk (the K order of an FP8 matrix-instruction operand).
+ * fp8_linear — out = (x_q w^T) * (x_scale * w_scale) + bias, where
+ *   x_q = sat448(rne(fp32(x) * (1 / x_scale))) as e4m3 (1/x_scale in fp32,
+ *   the rule of the MoE FP8 mode) and w holds e4m3 codes of w / w_scale;
+ *   fp32 accumulation, bias added in fp32, rounded once to bf16.
+ *     x       : (T, K) bf16            out : (T, N) bf16
+ *     w_tiled : fp8_tile output         bias: (N,) bf16 or NULL (zero)
+ *     workspace: fp8_linear_workspace_bytes(T, K, N) bytes (holds x_q).
+ * Errors: N or K not a positive multiple of 32 or above 2^20, or tensors
+ * past the 32-bit buffer windows -> MXMOE_ERR_SHAPE; a scale not finite and
+ * > 0 (or 1/x_scale, x_scale * w_scale not finite) -> MXMOE_ERR_VALUE; NULL,
+ * misaligned, short workspace as for moe_mxfp4_forward.  T == 0 is a no-op.
+ */
+mxmoe_status_t fp8_tiled_bytes(int64_t N, int64_t K, int64_t* bytes);
+mxmoe_status_t fp8_tile(const uint8_t* w, int64_t N, int64_t K, uint8_t* w_tiled, void* stream);
+size_t fp8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N);
+mxmoe_status_t fp8_linear(const void* x, int64_t T, int64_t K, const uint8_t* w_tiled, float w_scale, float x_scale,
+                          const void* bias, int64_t N, void* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* One MoE layer's parameters, all device pointers (see the file header). */
 typedef struct {
   int32_t E;            /* experts, 1..MXMOE_MAX_EXPERTS */

@@ -5,6 +5,7 @@ include/mxmoe.h); this package only loads it and marshals torch tensors.
 """
 from .binding import (  # noqa: F401
     EXPORTED,
+    FP8Linear,
     LAYOUT_ROWS,
     LAYOUT_TILED,
     LIB_PATH,
@@ -14,6 +15,10 @@ from .binding import (  # noqa: F401
     PATH_DENSE,
     PATH_ROUTED,
     alloc_workspace,
+    fp8_linear,
+    fp8_linear_workspace_bytes,
+    fp8_tile,
+    fp8_tiled_bytes,
     load_library,
     moe_mxfp4_calibrate_fp8,
     moe_mxfp4_forward,

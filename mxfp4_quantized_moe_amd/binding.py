@@ -43,6 +43,10 @@ EXPORTED = (
     "mxfp4_tile",
     "mxfp4_linear_workspace_bytes",
     "mxfp4_linear",
+    "fp8_tiled_bytes",
+    "fp8_tile",
+    "fp8_linear_workspace_bytes",
+    "fp8_linear",
     "moe_mxfp4_workspace_bytes",
     "moe_mxfp4_forward",
     "moe_mxfp4_route",
@@ -123,6 +127,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_linear_workspace_bytes.argtypes = [i64, i64, i32]
     lib.mxfp4_linear.restype = i32
     lib.mxfp4_linear.argtypes = [vp, i64, i64, vp, vp, i32, vp, i64, i32, vp, vp, sz, vp]
+    f32 = ctypes.c_float
+    lib.fp8_tiled_bytes.restype = i32
+    lib.fp8_tiled_bytes.argtypes = [i64, i64, ctypes.POINTER(i64)]
+    lib.fp8_tile.restype = i32
+    lib.fp8_tile.argtypes = [vp, i64, i64, vp, vp]
+    lib.fp8_linear_workspace_bytes.restype = sz
+    lib.fp8_linear_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.fp8_linear.restype = i32
+    lib.fp8_linear.argtypes = [vp, i64, i64, vp, f32, f32, vp, i64, vp, vp, sz, vp]
     lib.moe_mxfp4_workspace_bytes.restype = sz
     lib.moe_mxfp4_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i64, ctypes.POINTER(FwdOpts)]
     lib.moe_mxfp4_forward.restype = i32
@@ -260,6 +273,65 @@ def mxfp4_linear(x: torch.Tensor, layer: MXFP4Linear, out: Optional[torch.Tensor
     _check(load_library().mxfp4_linear(_ptr(x), T, int(x.shape[1]), _ptr(layer.blocks), _ptr(layer.scales),
                                        layer.layout, _ptr(layer.bias), layer.N, _dtype_code(x.dtype), _ptr(out),
                                        _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+# ------------------------------------------------------- dense FP8 layer
+
+
+def fp8_tiled_bytes(N: int, K: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(load_library().fp8_tiled_bytes(N, K, ctypes.byref(n)))
+    return int(n.value)
+
+
+def fp8_tile(w: torch.Tensor) -> torch.Tensor:
+    """(N, K) uint8 e4m3 codes (row-major, device) -> the tiled FP8 order."""
+    N, K = int(w.shape[0]), int(w.shape[1])
+    out = torch.empty(fp8_tiled_bytes(N, K), dtype=torch.uint8, device=w.device)
+    _check(load_library().fp8_tile(_ptr(w.contiguous()), N, K, _ptr(out), _stream(w.device)))
+    return out
+
+
+@dataclass
+class FP8Linear:
+    """A dense FP8 E4M3 layer with static per-tensor scales (W8A8):
+    y = (q(x) q(W)^T) * (x_scale * w_scale) + b, see include/mxmoe.h.
+    w_tiled is fp8_tile's output; bias (N,) bf16 or None."""
+
+    w_tiled: torch.Tensor
+    N: int
+    K: int
+    w_scale: float
+    x_scale: float
+    bias: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def from_codes(w: torch.Tensor, w_scale: float, x_scale: float,
+                   bias: Optional[torch.Tensor] = None) -> "FP8Linear":
+        return FP8Linear(fp8_tile(w), int(w.shape[0]), int(w.shape[1]), float(w_scale), float(x_scale), bias)
+
+    def __call__(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        return fp8_linear(x, self, out=out, workspace=workspace)
+
+
+def fp8_linear_workspace_bytes(T: int, K: int, N: int) -> int:
+    return int(load_library().fp8_linear_workspace_bytes(T, K, N))
+
+
+def fp8_linear(x: torch.Tensor, layer: FP8Linear, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x (T, K) bf16 -> (T, N) bf16."""
+    T = int(x.shape[0])
+    if out is None:
+        out = torch.empty((T, layer.N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        n = fp8_linear_workspace_bytes(T, layer.K, layer.N)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    _check(load_library().fp8_linear(_ptr(x), T, int(x.shape[1]), _ptr(layer.w_tiled), layer.w_scale, layer.x_scale,
+                                     _ptr(layer.bias), layer.N, _ptr(out), _ptr(workspace), workspace.numel(),
+                                     _stream(x.device)))
     return out
 
 

@@ -514,3 +514,115 @@ mxmoe_status_t mxfp4_linear(const void* x, int64_t T, int64_t K, const uint8_t* 
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------- dense FP8 layer
+
+namespace {
+
+int64_t fp8_tiled_size(int64_t N, int64_t K) { return 4 * ((N + 63) / 64) * ((K + 127) / 128) * 2048; }
+
+struct Fp8LinearWorkspace {
+  size_t offsets, active, tile_off, tiles, bias, xq, total;
+};
+
+Fp8LinearWorkspace fp8_linear_layout(int64_t T, int64_t K, int64_t N) {
+  Fp8LinearWorkspace w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  w.offsets = take(2 * 4);
+  w.active = take(2 * 4);
+  w.tile_off = take(2 * 4);
+  w.tiles = take(size_t((T + kPrefillTokens - 1) / kPrefillTokens) * 16 + 16);
+  w.bias = take(size_t(N) * 2);
+  w.xq = take(size_t(T) * size_t(K));
+  w.total = o;
+  return w;
+}
+
+mxmoe_status_t check_fp8_dims(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0 || N > kMaxDim || K > kMaxDim) return MXMOE_ERR_SHAPE;
+  if (fp8_tiled_size(N, K) > kMaxWindow) return MXMOE_ERR_SHAPE;
+  return MXMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxmoe_status_t fp8_tiled_bytes(int64_t N, int64_t K, int64_t* bytes) {
+  mxmoe_status_t st = check_fp8_dims(N, K);
+  if (st != MXMOE_OK) return st;
+  if (!bytes) return MXMOE_ERR_NULL;
+  *bytes = fp8_tiled_size(N, K);
+  return MXMOE_OK;
+}
+
+mxmoe_status_t fp8_tile(const uint8_t* w, int64_t N, int64_t K, uint8_t* tiled, void* stream) {
+  mxmoe_status_t st = check_fp8_dims(N, K);
+  if (st != MXMOE_OK) return st;
+  if (!w || !tiled) return MXMOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(tiled)) return MXMOE_ERR_ALIGN;
+  return hip_status(launch_fp8_tile(w, int(N), int(K), tiled, static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N) {
+  if (T < 0 || T > kMaxSlots || check_fp8_dims(N, K) != MXMOE_OK) return 0;
+  return fp8_linear_layout(T, K, N).total;
+}
+
+mxmoe_status_t fp8_linear(const void* x, int64_t T, int64_t K, const uint8_t* w_tiled, float w_scale, float x_scale,
+                          const void* bias, int64_t N, void* out, void* ws, size_t ws_bytes, void* stream) {
+  mxmoe_status_t st = check_fp8_dims(N, K);
+  if (st != MXMOE_OK) return st;
+  if (T < 0 || T > kMaxSlots) return MXMOE_ERR_SHAPE;
+  // 32-bit buffer windows over x (bf16), its FP8 codes and out (bf16)
+  if (T * K * 2 > kMaxWindow || T * N * 2 > kMaxWindow) return MXMOE_ERR_SHAPE;
+  if (!(std::isfinite(w_scale) && w_scale > 0.f && std::isfinite(x_scale) && x_scale > 0.f)) return MXMOE_ERR_VALUE;
+  if (!std::isfinite(1.0f / x_scale) || !std::isfinite(x_scale * w_scale)) return MXMOE_ERR_VALUE;
+  if (T == 0) return MXMOE_OK;
+  if (!x || !w_tiled || !out || !ws) return MXMOE_ERR_NULL;
+  const void* ptrs[] = {x, w_tiled, out, ws, bias};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MXMOE_ERR_ALIGN;
+  const Fp8LinearWorkspace w = fp8_linear_layout(T, K, N);
+  if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_linear_setup(int(T), at<int32_t>(ws, w.offsets), at<int32_t>(ws, w.active), at<int32_t>(ws, w.tile_off),
+                          at<int4>(ws, w.tiles), bias ? nullptr : at<void>(ws, w.bias), int(N), 2, s) != hipSuccess)
+    return MXMOE_ERR_HIP;
+  // x -> e4m3 codes with the static input scale (the MoE FP8 mode's rule)
+  if (launch_quant_fp8(static_cast<const uint16_t*>(x), T * K, 1.0f / x_scale, at<uint8_t>(ws, w.xq), s) !=
+      hipSuccess)
+    return MXMOE_ERR_HIP;
+  GemmArgs g{};
+  g.act = ACT_W8A8;
+  g.phase = 1;
+  g.wblk = w_tiled;
+  g.wsc = w_tiled;
+  g.tiled = 1;
+  g.bias = bias ? bias : at<void>(ws, w.bias);
+  g.bias_bf16 = 1;
+  g.R = int(N);
+  g.nb = int(K / 32);
+  g.top_k = 1;
+  g.E = 1;
+  g.bsrc = at<void>(ws, w.xq);
+  g.b_rows = T;
+  g.offsets = at<int32_t>(ws, w.offsets);
+  g.active = at<int32_t>(ws, w.active);
+  g.tile_off = at<int32_t>(ws, w.tile_off);
+  g.tiles = at<int4>(ws, w.tiles);
+  g.out = out;
+  g.acc_scale = x_scale * w_scale;
+  g.out_inv_scale = 1.0f;
+  g.max_active = 1;
+  g.max_tiles = int((T + kPrefillTokens - 1) / kPrefillTokens);
+  g.n_slots = int(T);
+  return hip_status(launch_moe_gemm(g, true, s));
+}
+
+}  // extern "C"

@@ -8,7 +8,9 @@ namespace mxmoe {
 
 // Arithmetic of the expert GEMMs: fp32 or bf16 activations on decoded
 // weights, or FP8 activations on the scaled MXFP4 x FP8 instructions.
-enum Act : int { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2 };
+// ACT_W8A8: FP8 activations against FP8 (e4m3) weights in the tiled FP8
+// order (dense linear only; phase 1 epilogue).
+enum Act : int { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2, ACT_W8A8 = 3 };
 
 // Tile shape of the prefill grouped GEMM: weight rows per workgroup (4 row
 // groups x 16*RT rows), tokens per workgroup tile, and LDS pipeline stages
@@ -81,6 +83,9 @@ hipError_t launch_dense_group(const DenseGroupArgs& a, hipStream_t stream);
 
 // FP8 static quantisation of a (rows, cols) bf16 tensor to e4m3 codes.
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8_t* q, hipStream_t stream);
+
+// (N, K) FP8 e4m3 codes -> the tiled FP8 order of the dense FP8 layer.
+hipError_t launch_fp8_tile(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream);
 
 struct GemmArgs {
   int act;                    // Act: 0 f32, 1 bf16, 2 fp8

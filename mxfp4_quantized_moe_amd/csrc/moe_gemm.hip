@@ -92,6 +92,22 @@ __device__ __forceinline__ WBuf expert_weights(const GemmArgs& a, int e) {
   return w;
 }
 
+// FP8 (e4m3) weights of a dense layer in the tiled FP8 order (declared in
+// mxmoe.h): rt4 row tiles of 16 rows x nc 128-wide chunks, 2 KB each, lane
+// (g, r) holding row r's bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of the
+// chunk (the K order of an FP8 MFMA operand).  No scales: one per tensor.
+__device__ __forceinline__ WBuf fp8_weights(const GemmArgs& a) {
+  WBuf w;
+  w.R = a.R;
+  w.nb = a.nb;
+  w.nc = (a.nb + 3) >> 2;
+  w.rt4 = 4 * ((a.R + 63) >> 6);
+  const int64_t bb = int64_t(w.rt4) * w.nc * 2048;
+  w.blk = make_rsrc(a.wblk, uint32_t(bb));
+  w.sc = w.blk;
+  return w;
+}
+
 // Slot of block b of row r (both within a 16 x 4 piece) in a 1 KB tile:
 // the block index is XOR-swizzled with the row so that the 16 lanes of a
 // lane group read 16 distinct bank groups.
@@ -718,9 +734,11 @@ constexpr int kTiledThreads = 64 * kTiledWaves;
 
 template <int ACT, int PHASE>
 __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefill_tiled_kernel(GemmArgs a) {
-  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "prefill path takes bf16 or fp8 activations");
+  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8 || ACT == ACT_W8A8, "prefill path takes bf16 or fp8 activations");
+  static_assert(ACT != ACT_W8A8 || PHASE == 1, "FP8 weights: dense layer epilogue only");
   static_assert(kPrefillTokens == 128, "eight 16-token sub-tiles per tile");
   static_assert(kTiledRows % 64 == 0, "waves of 4 row tiles: one scale group per wave");
+  constexpr bool W8 = ACT == ACT_W8A8;  // FP8 weights (32 bytes per lane per chunk, no block scales)
   constexpr int RT = 4, S = ACT == ACT_BF16 ? MXMOE_PREFILL_TILED_STAGES : MXMOE_PREFILL_TILED_STAGES_FP8;
   constexpr int EB = ACT == ACT_BF16 ? 2 : 1;
   constexpr int KB = 128 * EB;                  // bytes of one token row per chunk
@@ -774,7 +792,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   const int e = ti.x, row_start = ti.y, ntok = ti.z;
   const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
   const int nb = a.nb, K = nb * 32;
-  const WBuf wb = expert_weights<true>(a, e);
+  const WBuf wb = W8 ? fp8_weights(a) : expert_weights<true>(a, e);
   const int nc = wb.nc;
   const int grow = stripe * kTiledRows + wave * (16 * RT);  // first row of this wave
   const int t0 = grow >> 4;                                   // its first row tile (a scale group start)
@@ -807,7 +825,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     constexpr bool SMALL = decltype(smc)::value != 0;
     constexpr int SX = SMALL ? SS : S;           // stages of the ring
     constexpr int BL = SMALL ? SBLOADS : BLOADS;  // B loads per wave per chunk
-    constexpr int LD = RT + 1 + BL;              // VMEM instructions per wave per chunk
+    constexpr int LD = (W8 ? 2 * RT : RT + 1) + BL;  // VMEM instructions per wave per chunk
     static_assert(!SMALL || (ACT == ACT_BF16 && NA <= 4), "small ring: bf16 tiles of <= 64 tokens");
     auto stage = [&](auto uc) -> uint8_t* {
       if constexpr (SMALL) return stage_small(uc);
@@ -831,15 +849,26 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
       boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
     }
     uint4 aq[SX][RT];   // weight pieces per stage
+    uint4 aq2[W8 ? SX : 1][RT];  // FP8 weights: the second 16 bytes of a lane's piece
     uint32_t sw[SX];    // scale dword per stage
 
     auto issue = [&](int c, auto stc) __attribute__((always_inline)) {
       constexpr int u = decltype(stc)::value;
       const bool cok = c < nc && wok;
+      if constexpr (W8) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        aq[u][rt] = buf_load_b128(wb.blk, cok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
-      sw[u] = buf_load_b32(wb.sc, cok ? uint32_t(((t0 >> 2) * nc + c) * 256 + lane * 4) : kOOB);
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint32_t o = cok ? uint32_t(((t0 + rt) * nc + c) * 2048 + lane * 32) : kOOB;
+          aq[u][rt] = buf_load_b128(wb.blk, o);
+          aq2[u][rt] = buf_load_b128(wb.blk, oob_add(o, 16u));
+        }
+        sw[u] = 0;
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          aq[u][rt] = buf_load_b128(wb.blk, cok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
+        sw[u] = buf_load_b32(wb.sc, cok ? uint32_t(((t0 >> 2) * nc + c) * 256 + lane * 4) : kOOB);
+      }
       uint8_t* stb = stage(stc);
 #pragma unroll
       for (int jj = 0; jj < BL; ++jj) {
@@ -891,7 +920,12 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
             const uint4 q = aq[u][rt];
-            av[rt] = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
+            if constexpr (W8) {
+              const uint4 q2 = aq2[u][rt];
+              av[rt] = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), int(q2.x), int(q2.y), int(q2.z), int(q2.w)};
+            } else {
+              av[rt] = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
+            }
           }
           i32x8_t bcur = load_b(0);
 #pragma unroll
@@ -901,8 +935,8 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
             order_point();
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[rt], bcur, acc[rt][nt], 4, 0, 0,
-                                                                             int(ascb[rt]), 0, 127);
+              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  av[rt], bcur, acc[rt][nt], W8 ? 0 : 4, 0, 0, W8 ? 127 : int(ascb[rt]), 0, 127);
             bcur = bnext;
           }
         }
@@ -946,6 +980,10 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
       uint32_t x = 0;
 #pragma unroll
       for (int d = 0; d < SX; ++d) x ^= aq[d][0].x ^ aq[d][1].y ^ aq[d][2].z ^ aq[d][3].w ^ sw[d];
+      if constexpr (W8) {
+#pragma unroll
+        for (int d = 0; d < SX; ++d) x ^= aq2[d][0].x ^ aq2[d][1].y ^ aq2[d][2].z ^ aq2[d][3].w;
+      }
       static_cast<uint32_t*>(a.out)[0] = x;
     }
 
@@ -1177,7 +1215,10 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_tiled_kernel(GemmArgs a) {
 
 template <int ACT, int PHASE, bool TILED>
 static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
-  if (prefill) {
+  if constexpr (ACT == ACT_W8A8) {  // dense FP8 layer: the tiled LDS-staged kernel only
+    const int64_t items = (int64_t(a.max_tiles) * ((a.R + kTiledRows - 1) / kTiledRows) + 7) / 8 * 8;
+    gemm_prefill_tiled_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kTiledThreads), 0, stream>>>(a);
+  } else if (prefill) {
     if constexpr (ACT != ACT_F32) {
       const int nstripes = TILED ? (a.R + kTiledRows - 1) / kTiledRows : (a.R + kPrefillRows - 1) / kPrefillRows;
       int64_t items = int64_t(a.max_tiles) * nstripes;
@@ -1214,6 +1255,10 @@ hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream) 
     case ACT_BF16 * 2 + 1: launch_one<ACT_BF16, 1>(a, prefill, stream); break;
     case ACT_FP8 * 2 + 0: launch_one<ACT_FP8, 0>(a, prefill, stream); break;
     case ACT_FP8 * 2 + 1: launch_one<ACT_FP8, 1>(a, prefill, stream); break;
+    case ACT_W8A8 * 2 + 1:
+      if (!a.tiled || !prefill) return hipErrorInvalidValue;  // only the tiled LDS-staged kernel
+      launch_layout<ACT_W8A8, 1, true>(a, true, stream);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

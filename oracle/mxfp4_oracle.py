@@ -75,6 +75,7 @@ __all__ = [
     "calibrate_fp8",
     "routing_margin",
     "mxfp4_linear",
+    "fp8_linear",
 ]
 
 # ---------------------------------------------------------------------------
@@ -441,6 +442,30 @@ def mxfp4_linear(x: np.ndarray, blocks: np.ndarray, scales: np.ndarray, bias, ac
     y = xf @ W.T
     if bias is not None:
         y = y + widen(bias, act_dtype)
+    return y
+
+
+def fp8_linear(x: np.ndarray, w_codes: np.ndarray, w_scale: float, x_scale: float, bias=None) -> np.ndarray:
+    """A dense FP8 E4M3 layer with static per-tensor scales (W8A8): the FP8
+    attention projections of the gpt-oss-120b-mxfp4-fp8attn-v2 page ("Model
+    Details"; "Quantization Recipe", steps 1 and 2: weights and inputs in
+    float8_e4m3fn, symmetric, one static scale per tensor kept as
+    weight_scale and input_scale).
+
+    W = e4m3 value of each code * w_scale (N, K); x is quantised with
+    fp8_quant_dequant at x_scale (the same rule as the MoE FP8 mode);
+    y = x_q W^T + b in float64.
+    x: (T, K) bf16 bits; w_codes: (N, K) uint8; bias: (N,) bf16 bits or None.
+    Returns (T, N) float64, unrounded."""
+    xf = widen(x, "bf16")
+    w_codes = np.asarray(w_codes)
+    if xf.ndim != 2 or w_codes.ndim != 2 or xf.shape[1] != w_codes.shape[1]:
+        raise ValueError("x (T, K) and w_codes (N, K) must agree on K")
+    _, xq = fp8_quant_dequant(xf, x_scale)
+    W = e4m3_decode(w_codes) * np.float64(np.float32(w_scale))
+    y = xq @ W.T
+    if bias is not None:
+        y = y + widen(bias, "bf16")
     return y
 
 

@@ -236,3 +236,36 @@ def test_linear_validation(lib):
     assert need > 0
     assert call(ws_bytes=need - 1) == WS
     assert lib.mxfp4_linear_workspace_bytes(8, 64, 7) == 0
+
+
+def test_fp8_linear_validation(lib):
+    n = ctypes.c_int64(0)
+    assert lib.fp8_tiled_bytes(64, 128, ctypes.byref(n)) == OK and n.value == 4 * 1 * 2048
+    assert lib.fp8_tiled_bytes(96, 160, ctypes.byref(n)) == OK and n.value == 8 * 2 * 2048  # padded N and K
+    assert lib.fp8_tiled_bytes(64, 48, ctypes.byref(n)) == SHAPE
+    assert lib.fp8_tiled_bytes(0, 64, ctypes.byref(n)) == SHAPE
+    assert lib.fp8_tiled_bytes(64, 64, None) == NULL
+    assert lib.fp8_tile(P, 64, 48, P, None) == SHAPE
+    assert lib.fp8_tile(None, 64, 64, P, None) == NULL
+    assert lib.fp8_tile(P + 4, 64, 64, P, None) == ALIGN
+
+    def call(T=8, K=64, N=64, x=P, w=P, w_scale=1.0, x_scale=1.0, bias=None, out=P, ws=P, ws_bytes=1 << 30):
+        return lib.fp8_linear(x, T, K, w, w_scale, x_scale, bias, N, out, ws, ws_bytes, None)
+
+    assert call(K=48) == SHAPE
+    assert call(N=40) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert call(w_scale=0.0) == VALUE
+    assert call(x_scale=float("inf")) == VALUE
+    assert call(x_scale=float("nan")) == VALUE
+    assert call(x_scale=1e-40) == VALUE  # 1 / x_scale overflows fp32
+    assert call(x=None) == NULL
+    assert call(w=None) == NULL
+    assert call(bias=P + 2) == ALIGN
+    assert call(out=P + 8) == ALIGN
+    assert call(T=0, x=None, out=None, ws=None) == OK  # empty batch: no-op
+    need = lib.fp8_linear_workspace_bytes(8, 64, 64)
+    assert need >= 8 * 64  # holds x's FP8 codes
+    assert call(ws_bytes=need - 1) == WS
+    assert lib.fp8_linear_workspace_bytes(8, 48, 64) == 0
+    assert lib.fp8_linear_workspace_bytes(-1, 64, 64) == 0

@@ -513,3 +513,64 @@ def test_linear_is_the_down_projection_of_the_layer():
     y = O.mxfp4_linear(parts["h"].astype(np.float32), L.down_blocks[0], L.down_scales[0], L.down_bias[0], "f32")
     assert np.allclose(y, parts["Y"], rtol=1e-6, atol=1e-6)
     assert np.allclose(out, parts["Y"])  # top-1 of one expert: weight 1
+
+
+# ------------------------------------------------------- dense FP8 layer
+
+
+def _bf16(v):
+    return O.bf16_bits(np.asarray(v, dtype=np.float64))
+
+
+def test_fp8_linear_exact_closed_form():
+    """Hand-encoded e4m3 codes (S.EEEE.MMM, bias 7: 0x38 = 1, 0x40 = 2,
+    0xBC = -1.5, 0x48 = 4, 0x30 = 0.5) and power-of-two scales; x on the
+    grid x_scale * e4m3 so its quantisation is exact: y by hand."""
+    w_codes = np.array([[0x38, 0x40, 0xBC, 0x48], [0x30, 0x38, 0x38, 0xC0]], dtype=np.uint8)  # rows of W / w_scale
+    w_vals = np.array([[1, 2, -1.5, 4], [0.5, 1, 1, -2]])
+    w_scale, x_scale = 0.5, 0.25
+    x_grid = np.array([[1, 2, -3, 0.5], [4, -1, 0, 6]])
+    x = _bf16(x_grid * x_scale)
+    b = _bf16([1.0, -2.0])
+    y = O.fp8_linear(x, w_codes, w_scale, x_scale, b)
+    expected = np.array([[sum(x_grid[t, k] * x_scale * w_vals[n, k] * w_scale for k in range(4)) + [1.0, -2.0][n]
+                          for n in range(2)] for t in range(2)])
+    assert np.array_equal(y, expected)
+    assert np.array_equal(O.fp8_linear(x, w_codes, w_scale, x_scale, None), expected - np.array([1.0, -2.0]))
+
+
+def test_fp8_linear_matches_torch_float8():
+    """Against torch's own float8_e4m3fn: its decode of the weight codes and
+    its round-to-nearest cast of fp32(x) * fp32(1/x_scale) (inputs kept
+    inside +-448 x_scale, where no saturation is involved)."""
+    rng = np.random.default_rng(5)
+    T, K, N = 6, 64, 5
+    codes = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x00  # no NaN codes
+    w_scale, x_scale = 0.0123, 0.0071
+    x = _bf16(rng.normal(0, 1, size=(T, K)))
+    b = _bf16(rng.normal(0, 0.1, size=N))
+    y = O.fp8_linear(x, codes, w_scale, x_scale, b)
+    wt = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64) * float(np.float32(w_scale))
+    xf = torch.from_numpy(O.bf16_from_bits(x).astype(np.float32))
+    inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(x_scale, dtype=torch.float32)
+    assert float((xf * inv).abs().max()) < 448
+    xq = (xf * inv).to(torch.float8_e4m3fn).to(torch.float64) * float(np.float32(x_scale))
+    ref = xq @ wt.T + torch.from_numpy(O.bf16_from_bits(b))
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_linear_saturates_inputs():
+    """x beyond 448 x_scale contributes +-448 x_scale (static scheme,
+    saturating cast)."""
+    w_codes = np.array([[0x38, 0x38]], dtype=np.uint8)  # W = [1, 1] * w_scale
+    x = _bf16([[1000.0, -5000.0]])
+    y = O.fp8_linear(x, w_codes, 1.0, 1.0, None)
+    assert np.array_equal(y, np.array([[448.0 - 448.0]]))
+    y = O.fp8_linear(_bf16([[1000.0, 3.0]]), w_codes, 1.0, 1.0, None)
+    assert np.array_equal(y, np.array([[451.0]]))
+
+
+def test_fp8_linear_rejects_mismatched_k():
+    with pytest.raises(ValueError):
+        O.fp8_linear(_bf16(np.zeros((2, 32))), np.zeros((3, 64), np.uint8), 1.0, 1.0)

@@ -36,3 +36,19 @@ def test_piece_slots_are_a_permutation():
         col = slots[:, bb]
         assert len(set(col.tolist())) == 16
         assert sorted((col % 4).tolist()) == sorted([0, 1, 2, 3] * 4)
+
+
+@pytest.mark.parametrize("N,K", [(32, 32), (64, 128), (96, 160), (160, 288)])
+def test_fp8_tile_vectorised_matches_definition(N, K):
+    rng = np.random.default_rng(N + K)
+    w = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    assert np.array_equal(TL.fp8_tile(w), TL.fp8_tile_loops(w))
+
+
+def test_fp8_tile_is_a_permutation_plus_zeros():
+    """Every code lands exactly once; the rest of the tiled tensor is zero."""
+    N, K = 96, 160
+    w = (np.arange(N * K, dtype=np.int64) % 251 + 1).astype(np.uint8).reshape(N, K)  # no zero codes
+    t = TL.fp8_tile(w)
+    assert np.count_nonzero(t) == N * K
+    assert sorted(t[t != 0].tolist()) == sorted(w.ravel().tolist())

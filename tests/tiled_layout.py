@@ -74,3 +74,38 @@ def untile(tb: np.ndarray, ts: np.ndarray, mats: int, rows: int, nb: int):
     s = ts.reshape(mats, rg, nc, 4, 16, 4)  # (m, q, c, b, r, i)
     scales = s.transpose(0, 1, 5, 4, 2, 3).reshape(mats, 64 * rg, 4 * nc)[:, :rows, :nb]
     return np.ascontiguousarray(blocks), np.ascontiguousarray(scales)
+
+
+# ------------------------------------------------- the tiled FP8 order
+#
+# (N, K) e4m3 codes -> [4RG][NC][64][32] with RG = ceil(N/64), NC =
+# ceil(K/128): lane l = 16g + r of (row tile t, chunk c) holds row 16t + r,
+# bytes 128c + 16g .. +16 then 128c + 64 + 16g .. +16; zero past N or K.
+
+
+def fp8_tile_loops(w: np.ndarray) -> np.ndarray:
+    """Byte by byte from the definition (small inputs only)."""
+    N, K = w.shape
+    rt4, nc = 4 * (-(-N // 64)), -(-K // 128)
+    out = np.zeros((rt4, nc, 64, 32), np.uint8)
+    for t in range(rt4):
+        for c in range(nc):
+            for lane in range(64):
+                g, r = lane >> 4, lane & 15
+                row = 16 * t + r
+                for j in range(32):
+                    k = 128 * c + 16 * g + (j % 16) + 64 * (j // 16)
+                    if row < N and k < K:
+                        out[t, c, lane, j] = w[row, k]
+    return out
+
+
+def fp8_tile(w: np.ndarray) -> np.ndarray:
+    """Vectorised form of fp8_tile_loops."""
+    N, K = w.shape
+    rt4, nc = 4 * (-(-N // 64)), -(-K // 128)
+    pad = np.zeros((16 * rt4, 128 * nc), np.uint8)
+    pad[:N, :K] = w
+    # [t][r][c][h][g][16] -> [t][c][g][r][h][16]
+    v = pad.reshape(rt4, 16, nc, 2, 4, 16).transpose(0, 2, 4, 1, 3, 5)
+    return np.ascontiguousarray(v).reshape(rt4, nc, 64, 32)

@@ -230,6 +230,32 @@ def linear_case(seed: int, T: int, K: int, N: int, act_dtype: str = BF16, bias: 
     return LinearCase(f"linear_s{seed}_t{T}_k{K}_n{N}_{act_dtype}", x, blocks, scales, b, act_dtype)
 
 
+@dataclass
+class Fp8LinearCase:
+    name: str
+    x: np.ndarray        # (T, K) bf16 bits
+    w_codes: np.ndarray  # (N, K) uint8 float8_e4m3fn codes
+    w_scale: float       # static per-tensor weight scale
+    x_scale: float       # static per-tensor input scale
+    bias: Optional[np.ndarray]  # (N,) bf16 bits
+
+
+def fp8_linear_case(seed: int, T: int, K: int, N: int, bias: bool = True, w_scale: float = 2.0**-8,
+                    x_scale: float = 2.0**-6) -> Fp8LinearCase:
+    """A dense FP8 E4M3 layer with static per-tensor scales and its input.
+    Draw order: codes, bias, x.  Codes uniform over the finite e4m3 codes
+    (the two NaN codes are redrawn as zero); bias N(0, 0.01); x N(0, 1).
+    The scales are fixed constants, as a calibration would have left them:
+    x_scale = 2^-6 puts inputs up to 7 inside the e4m3 range."""
+    assert K % 32 == 0 and N % 32 == 0
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    b = _real(rng, (N,), 0.01, BF16) if bias else None
+    x = _real(rng, (T, K), 1.0, BF16)
+    return Fp8LinearCase(f"fp8_linear_s{seed}_t{T}_k{K}_n{N}", x, codes, w_scale, x_scale, b)
+
+
 def random_weights(seed: int, rows: int, k: int, std: float = 1.0, dtype: str = F32) -> np.ndarray:
     """A dense weight matrix to be packed (pack parity cases)."""
     rng = np.random.default_rng(seed)
