@@ -26,6 +26,7 @@ Workloads (synthetic, seeded; see workloads/):
   linear_t4096_k2880_n5760  weight-only MXFP4 dense layer y = x W^T + b, bf16
   fp8_linear_t4096_k2880_n5760  FP8 E4M3 W8A8 dense layer, static per-tensor scales
   bf16_20b_t{T}        the 20b layer at any T (with --path dense: the all-experts path)
+  int8_20b_t2048       INT8 W8A8 MoE layer (per-channel weights, per-token activations), 20b shape
 """
 from __future__ import annotations
 
@@ -42,7 +43,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MXFP4 MoE layer tokens/s; % HBM roofline (decode), % MFMA peak (prefill)"
-PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp8_TFLOPs": 5000.0, "fp32_TFLOPs": 157.3}
+PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp8_TFLOPs": 5000.0, "int8_TOPs": 5000.0, "fp32_TFLOPs": 157.3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["mxfp4_quantized_moe_amd/csrc/moe_gemm.hip", "mxfp4_quantized_moe_amd/csrc/codec.hip",
                   "mxfp4_quantized_moe_amd/csrc/device_common.h"]
@@ -430,6 +431,55 @@ def bench_fp8_linear(args, dev):
                          "algorithmic": f"{fl} flop per call", "traffic": None}}
 
 
+def bench_int8(args, dev):
+    """The INT8 W8A8 MoE layer at the 20b shape: tokens/s of whole forwards,
+    and the two grouped GEMMs' int8 ops over the forward's duration (HIP
+    events around each call on its stream) against the dense int8 peak."""
+    import numpy as np
+    import torch
+
+    import mxfp4_quantized_moe_amd as mx
+    import workloads as W
+
+    T = 2048
+    case = W.int8_20b(T)
+    L = case.layer
+    w0 = W.int8_layer_to_torch(L, dev)
+    x = W.array_to_torch(case.x, dev)
+    wbytes = w0.gate_up_w.numel() + w0.down_w.numel()
+    copies = min(16, -(-int(1.0e9) // wbytes) + 1) if args.copies is None else args.copies
+    layers = [w0] + [mx.MoEInt8Weights(w0.gate_up_w.clone(), w0.gate_up_scale, w0.gate_up_bias, w0.down_w.clone(),
+                                       w0.down_scale, w0.down_bias, w0.router_w, w0.router_b, w0.top_k)
+                     for _ in range(copies - 1)]
+    out = torch.empty_like(x)
+    ws = torch.empty(max(mx.moe_int8_workspace_bytes(w0, T), 256), dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        mx.moe_int8_forward(layers[i % copies], x, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        mx.moe_int8_forward(layers[i % copies], x, out=out, workspace=ws)
+        ends[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    call_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
+    ops = 2 * T * L.top_k * (2 * L.I * L.H + L.H * L.I)
+    achieved = ops / call_s / 1e12
+    return {"metric": "INT8 W8A8 MoE layer tokens/s", "value": T * args.steps / (t1 - t0), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+            "data": "synthetic (seeded random int8 codes, per-row scales, bf16 activations)",
+            "config": {"workload": f"int8_20b_t{T}", "E": L.E, "top_k": L.top_k, "H": L.H, "I": L.I, "T": T,
+                       "weight_copies": copies},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK["int8_TOPs"], "unit": "TOP/s",
+                         "frac": achieved / PEAK["int8_TOPs"],
+                         "kernel": "whole forward: routing, int8 quantisation of x and h, both grouped GEMMs, combine",
+                         "algorithmic": f"{ops} int8 ops per forward (gate_up + down)", "traffic": None}}
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
@@ -480,6 +530,8 @@ def main():
         res = bench_linear(args, dev)
     elif args.workload == "fp8_linear_t4096_k2880_n5760":
         res = bench_fp8_linear(args, dev)
+    elif args.workload == "int8_20b_t2048":
+        res = bench_int8(args, dev)
     else:
         res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)

@@ -200,6 +200,51 @@ mxmoe_status_t fp8_linear(const void* x, int64_t T, int64_t K, const uint8_t* w_
                           const void* bias, int64_t N, void* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * INT8 W8A8 mixture-of-experts layer: the gpt-oss-20b-BF16-w8a8-llmcompressor
+ * page ("Quantization": weights int8, symmetric, one static scale per output
+ * channel; activations int8, symmetric, one dynamic scale per token; the
+ * router and every bias kept in bf16).  Same routing, SwiGLU and combine as
+ * moe_mxfp4_forward; the experts' weights are int8 codes instead of MXFP4.
+ *
+ * int8_tiled_bytes / int8_tile — `mats` (rows, k) int8 weights, row-major
+ *   codes (device), into the tiled 8-bit order of fp8_tile, matrix after
+ *   matrix.  Errors: rows or k not a positive multiple of 32 (or above 2^20)
+ *   -> MXMOE_ERR_SHAPE; NULL; misaligned.
+ */
+typedef struct {
+  int32_t E, H, I, top_k;      /* as mxmoe_layer_t */
+  const uint8_t* gate_up_w;    /* int8_tile of the (E, 2I, H) codes; rows gate (even) / up (odd) interleaved */
+  const float* gate_up_scale;  /* (E, 2I) fp32: weight = code * scale of its row */
+  const void* gate_up_bias;    /* (E, 2I) bf16 */
+  const uint8_t* down_w;       /* int8_tile of the (E, H, I) codes */
+  const float* down_scale;     /* (E, H) fp32 */
+  const void* down_bias;       /* (E, H) bf16 */
+  const void* router_w;        /* (E, H) bf16 */
+  const void* router_b;        /* (E,) bf16 */
+} mxmoe_int8_layer_t;
+
+mxmoe_status_t int8_tiled_bytes(int64_t mats, int64_t rows, int64_t k, int64_t* bytes);
+mxmoe_status_t int8_tile(const int8_t* w, int64_t mats, int64_t rows, int64_t k, uint8_t* w_tiled, void* stream);
+
+/*
+ * moe_int8_forward — x (T, H) bf16 -> out (T, H) bf16.  Routing as
+ * moe_mxfp4_forward.  Each token's x and each routed (token, expert) row of
+ * h is quantised with its own scale s = amax|row| / 127 (fp32, correctly
+ * rounded division), code = clamp(rne(v / s), -127, 127) (all zero for an
+ * all-zero row); G = (x_code . W_code) * s_x * s_w + b_gu with exact int32
+ * sums, h = clamped SwiGLU of G rounded to bf16, Y = (h_code . W_code) *
+ * s_h * s_w + b_d rounded to bf16, out_t = sum_j w_j Y_j (fp32, j order).
+ * Inputs must be finite.  Optional topk_idx_out (T, top_k) int32 and
+ * topk_w_out (T, top_k) fp32.  Workspace: moe_int8_workspace_bytes.
+ * Errors as moe_mxfp4_forward; the 8-bit weights of one expert must fit a
+ * 32-bit buffer window.
+ */
+size_t moe_int8_workspace_bytes(const mxmoe_int8_layer_t* layer, int64_t T);
+mxmoe_status_t moe_int8_forward(const mxmoe_int8_layer_t* layer, const void* x, int64_t T, void* out,
+                                int32_t* topk_idx_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* One MoE layer's parameters, all device pointers (see the file header). */
 typedef struct {
   int32_t E;            /* experts, 1..MXMOE_MAX_EXPERTS */

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     LAYOUT_ROWS,
     LAYOUT_TILED,
     LIB_PATH,
+    MoEInt8Weights,
     MoEWeights,
     MXFP4Linear,
     MxmoeError,
@@ -19,6 +20,9 @@ from .binding import (  # noqa: F401
     fp8_linear_workspace_bytes,
     fp8_tile,
     fp8_tiled_bytes,
+    int8_tile,
+    moe_int8_forward,
+    moe_int8_workspace_bytes,
     load_library,
     moe_mxfp4_calibrate_fp8,
     moe_mxfp4_forward,

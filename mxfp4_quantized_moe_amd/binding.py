@@ -47,6 +47,10 @@ EXPORTED = (
     "fp8_tile",
     "fp8_linear_workspace_bytes",
     "fp8_linear",
+    "int8_tiled_bytes",
+    "int8_tile",
+    "moe_int8_workspace_bytes",
+    "moe_int8_forward",
     "moe_mxfp4_workspace_bytes",
     "moe_mxfp4_forward",
     "moe_mxfp4_route",
@@ -73,6 +77,23 @@ class Layer(ctypes.Structure):
         ("gate_up_bias", ctypes.c_void_p),
         ("down_blocks", ctypes.c_void_p),
         ("down_scales", ctypes.c_void_p),
+        ("down_bias", ctypes.c_void_p),
+        ("router_w", ctypes.c_void_p),
+        ("router_b", ctypes.c_void_p),
+    ]
+
+
+class Int8Layer(ctypes.Structure):
+    _fields_ = [
+        ("E", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("I", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("gate_up_w", ctypes.c_void_p),
+        ("gate_up_scale", ctypes.c_void_p),
+        ("gate_up_bias", ctypes.c_void_p),
+        ("down_w", ctypes.c_void_p),
+        ("down_scale", ctypes.c_void_p),
         ("down_bias", ctypes.c_void_p),
         ("router_w", ctypes.c_void_p),
         ("router_b", ctypes.c_void_p),
@@ -136,6 +157,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_linear_workspace_bytes.argtypes = [i64, i64, i64]
     lib.fp8_linear.restype = i32
     lib.fp8_linear.argtypes = [vp, i64, i64, vp, f32, f32, vp, i64, vp, vp, sz, vp]
+    lib.int8_tiled_bytes.restype = i32
+    lib.int8_tiled_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
+    lib.int8_tile.restype = i32
+    lib.int8_tile.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.moe_int8_workspace_bytes.restype = sz
+    lib.moe_int8_workspace_bytes.argtypes = [ctypes.POINTER(Int8Layer), i64]
+    lib.moe_int8_forward.restype = i32
+    lib.moe_int8_forward.argtypes = [ctypes.POINTER(Int8Layer), vp, i64, vp, vp, vp, vp, sz, vp]
     lib.moe_mxfp4_workspace_bytes.restype = sz
     lib.moe_mxfp4_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i64, ctypes.POINTER(FwdOpts)]
     lib.moe_mxfp4_forward.restype = i32
@@ -332,6 +361,82 @@ def fp8_linear(x: torch.Tensor, layer: FP8Linear, out: Optional[torch.Tensor] = 
     _check(load_library().fp8_linear(_ptr(x), T, int(x.shape[1]), _ptr(layer.w_tiled), layer.w_scale, layer.x_scale,
                                      _ptr(layer.bias), layer.N, _ptr(out), _ptr(workspace), workspace.numel(),
                                      _stream(x.device)))
+    return out
+
+
+# ----------------------------------------------------- int8 W8A8 layer
+
+
+def int8_tile(w: torch.Tensor) -> torch.Tensor:
+    """(mats, rows, k) int8 codes (device) -> the tiled 8-bit order (flat)."""
+    mats, rows, k = (int(v) for v in w.shape)
+    n = ctypes.c_int64(0)
+    _check(load_library().int8_tiled_bytes(mats, rows, k, ctypes.byref(n)))
+    out = torch.empty(int(n.value), dtype=torch.uint8, device=w.device)
+    _check(load_library().int8_tile(_ptr(w.contiguous()), mats, rows, k, _ptr(out), _stream(w.device)))
+    return out
+
+
+@dataclass
+class MoEInt8Weights:
+    """Device tensors of one INT8 W8A8 MoE layer (see include/mxmoe.h); the
+    two weights are int8_tile outputs (from_codes tiles them)."""
+
+    gate_up_w: torch.Tensor      # tiled (E, 2I, H) int8 codes
+    gate_up_scale: torch.Tensor  # (E, 2I) fp32
+    gate_up_bias: torch.Tensor   # (E, 2I) bf16
+    down_w: torch.Tensor         # tiled (E, H, I) int8 codes
+    down_scale: torch.Tensor     # (E, H) fp32
+    down_bias: torch.Tensor      # (E, H) bf16
+    router_w: torch.Tensor       # (E, H) bf16
+    router_b: torch.Tensor       # (E,) bf16
+    top_k: int
+
+    @staticmethod
+    def from_codes(gate_up: torch.Tensor, gate_up_scale, gate_up_bias, down: torch.Tensor, down_scale, down_bias,
+                   router_w, router_b, top_k: int) -> "MoEInt8Weights":
+        return MoEInt8Weights(int8_tile(gate_up), gate_up_scale, gate_up_bias, int8_tile(down), down_scale,
+                              down_bias, router_w, router_b, top_k)
+
+    @property
+    def E(self) -> int:
+        return int(self.router_w.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.router_w.shape[1])
+
+    @property
+    def I(self) -> int:  # noqa: E743
+        return int(self.gate_up_bias.shape[1]) // 2
+
+    def descriptor(self) -> Int8Layer:
+        return Int8Layer(E=self.E, H=self.H, I=self.I, top_k=self.top_k, gate_up_w=_ptr(self.gate_up_w),
+                         gate_up_scale=_ptr(self.gate_up_scale), gate_up_bias=_ptr(self.gate_up_bias),
+                         down_w=_ptr(self.down_w), down_scale=_ptr(self.down_scale), down_bias=_ptr(self.down_bias),
+                         router_w=_ptr(self.router_w), router_b=_ptr(self.router_b))
+
+
+def moe_int8_workspace_bytes(layer: MoEInt8Weights, T: int) -> int:
+    d = layer.descriptor()
+    n = load_library().moe_int8_workspace_bytes(ctypes.byref(d), T)
+    if n == 0 and T > 0:
+        raise MxmoeError(3, "invalid int8 layer or token count")
+    return int(n)
+
+
+def moe_int8_forward(layer: MoEInt8Weights, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, topk_idx_out: Optional[torch.Tensor] = None,
+                     topk_w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The INT8 W8A8 MoE layer on x (T, H) bf16; returns out (T, H) bf16."""
+    T = int(x.shape[0])
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(max(moe_int8_workspace_bytes(layer, T), 256), dtype=torch.uint8, device=x.device)
+    d = layer.descriptor()
+    _check(load_library().moe_int8_forward(ctypes.byref(d), _ptr(x), T, _ptr(out), _ptr(topk_idx_out),
+                                           _ptr(topk_w_out), _ptr(workspace), workspace.numel(), _stream(x.device)))
     return out
 
 

@@ -566,7 +566,7 @@ mxmoe_status_t fp8_tile(const uint8_t* w, int64_t N, int64_t K, uint8_t* tiled, 
   if (st != MXMOE_OK) return st;
   if (!w || !tiled) return MXMOE_ERR_NULL;
   if (!aligned16(w) || !aligned16(tiled)) return MXMOE_ERR_ALIGN;
-  return hip_status(launch_fp8_tile(w, int(N), int(K), tiled, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_byte_tile(w, 1, int(N), int(K), tiled, static_cast<hipStream_t>(stream)));
 }
 
 size_t fp8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N) {
@@ -623,6 +623,159 @@ mxmoe_status_t fp8_linear(const void* x, int64_t T, int64_t K, const uint8_t* w_
   g.max_tiles = int((T + kPrefillTokens - 1) / kPrefillTokens);
   g.n_slots = int(T);
   return hip_status(launch_moe_gemm(g, true, s));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------ int8 W8A8 layer
+
+namespace {
+
+int64_t byte_tiled_size(int64_t rows, int64_t k) { return 4 * ((rows + 63) / 64) * ((k + 127) / 128) * 2048; }
+
+mxmoe_status_t check_int8_layer(const mxmoe_int8_layer_t* L) {
+  if (!L) return MXMOE_ERR_NULL;
+  if (L->E < 1 || L->E > MXMOE_MAX_EXPERTS) return MXMOE_ERR_SHAPE;
+  if (L->H <= 0 || L->I <= 0 || L->H > kMaxDim || L->I > kMaxDim || L->H % 32 != 0 || L->I % 32 != 0)
+    return MXMOE_ERR_SHAPE;
+  if (L->top_k < 1 || L->top_k > MXMOE_MAX_TOPK || L->top_k > L->E) return MXMOE_ERR_SHAPE;
+  if (byte_tiled_size(2 * int64_t(L->I), L->H) > kMaxWindow || byte_tiled_size(L->H, L->I) > kMaxWindow)
+    return MXMOE_ERR_SHAPE;
+  const void* ptrs[] = {L->gate_up_w, L->gate_up_scale, L->gate_up_bias, L->down_w,
+                        L->down_scale, L->down_bias,    L->router_w,     L->router_b};
+  for (const void* p : ptrs)
+    if (!p) return MXMOE_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MXMOE_ERR_ALIGN;
+  return MXMOE_OK;
+}
+
+// The routing view of an int8 layer: dimensions, router and (for the GEMM
+// argument setup) biases; the weight fields are replaced before each launch.
+mxmoe_layer_t routing_view(const mxmoe_int8_layer_t* L) {
+  mxmoe_layer_t r{};
+  r.E = L->E;
+  r.H = L->H;
+  r.I = L->I;
+  r.top_k = L->top_k;
+  r.param_dtype = MXMOE_BF16;
+  r.weight_layout = MXMOE_LAYOUT_TILED;
+  r.gate_up_blocks = L->gate_up_w;
+  r.gate_up_scales = L->gate_up_w;
+  r.gate_up_bias = L->gate_up_bias;
+  r.down_blocks = L->down_w;
+  r.down_scales = L->down_w;
+  r.down_bias = L->down_bias;
+  r.router_w = L->router_w;
+  r.router_b = L->router_b;
+  return r;
+}
+
+struct Int8Workspace {
+  Workspace base;  // routing tables, h (bf16), Y (bf16)
+  size_t xq, sx, hq, sh, total;
+};
+
+Int8Workspace int8_layout(const mxmoe_int8_layer_t* L, int64_t T) {
+  Int8Workspace w{};
+  w.base = layout(L->E, L->H, L->I, L->top_k, T, MXMOE_BF16, false, T * L->top_k);
+  size_t o = w.base.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t slots = size_t(T) * size_t(L->top_k);
+  w.xq = take(size_t(T) * size_t(L->H));
+  w.sx = take(size_t(T) * 4);
+  w.hq = take(slots * size_t(L->I));
+  w.sh = take(slots * 4);
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxmoe_status_t int8_tiled_bytes(int64_t mats, int64_t rows, int64_t k, int64_t* bytes) {
+  if (mats < 0 || rows <= 0 || k <= 0 || rows % 32 != 0 || k % 32 != 0 || rows > kMaxDim || k > kMaxDim)
+    return MXMOE_ERR_SHAPE;
+  if (!bytes) return MXMOE_ERR_NULL;
+  const int64_t one = byte_tiled_size(rows, k);
+  if (mats > 0 && one > (int64_t(1) << 62) / mats) return MXMOE_ERR_SHAPE;
+  *bytes = one * mats;
+  return MXMOE_OK;
+}
+
+mxmoe_status_t int8_tile(const int8_t* w, int64_t mats, int64_t rows, int64_t k, uint8_t* tiled, void* stream) {
+  int64_t bytes;
+  mxmoe_status_t st = int8_tiled_bytes(mats, rows, k, &bytes);
+  if (st != MXMOE_OK) return st;
+  if (mats == 0) return MXMOE_OK;
+  if (bytes / 16 > kMaxGridItems) return MXMOE_ERR_SHAPE;
+  if (!w || !tiled) return MXMOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(tiled)) return MXMOE_ERR_ALIGN;
+  return hip_status(launch_byte_tile(reinterpret_cast<const uint8_t*>(w), mats, int(rows), int(k), tiled,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_int8_workspace_bytes(const mxmoe_int8_layer_t* L, int64_t T) {
+  if (check_int8_layer(L) != MXMOE_OK) return 0;
+  const mxmoe_layer_t R = routing_view(L);
+  if (check_tokens(&R, T) != MXMOE_OK) return 0;
+  return int8_layout(L, T).total;
+}
+
+mxmoe_status_t moe_int8_forward(const mxmoe_int8_layer_t* L, const void* x, int64_t T, void* out,
+                                int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  mxmoe_status_t st = check_int8_layer(L);
+  if (st != MXMOE_OK) return st;
+  const mxmoe_layer_t R = routing_view(L);
+  if ((st = check_tokens(&R, T)) != MXMOE_OK) return st;
+  if (T == 0) return MXMOE_OK;
+  if (!x || !out || !ws) return MXMOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return MXMOE_ERR_ALIGN;
+  if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out))) return MXMOE_ERR_ALIGN;
+  const Int8Workspace w = int8_layout(L, T);
+  if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Workspace& b = w.base;
+  if (run_routing(&R, x, T, MXMOE_BF16, b, ws, topk_idx_out, topk_w_out, nullptr, nullptr, nullptr, nullptr, s) !=
+      hipSuccess)
+    return MXMOE_ERR_HIP;
+  // per-token int8 x
+  if (launch_quant_rows_int8(static_cast<const uint16_t*>(x), T, L->H, at<int8_t>(ws, w.xq), at<float>(ws, w.sx), s) !=
+      hipSuccess)
+    return MXMOE_ERR_HIP;
+  // gate_up + SwiGLU -> h (bf16)
+  GemmArgs g0 = gemm_args(&R, b, ws, T, ACT_INT8, 0);
+  g0.bsrc = at<void>(ws, w.xq);
+  g0.row_scale = L->gate_up_scale;
+  g0.tok_scale = at<float>(ws, w.sx);
+  if (launch_moe_gemm(g0, true, s) != hipSuccess) return MXMOE_ERR_HIP;
+  // per-row int8 h
+  const int64_t slots = T * L->top_k;
+  if (launch_quant_rows_int8(at<uint16_t>(ws, b.h), slots, L->I, at<int8_t>(ws, w.hq), at<float>(ws, w.sh), s) !=
+      hipSuccess)
+    return MXMOE_ERR_HIP;
+  // down -> Y (bf16)
+  GemmArgs g1 = gemm_args(&R, b, ws, T, ACT_INT8, 1);
+  g1.bsrc = at<void>(ws, w.hq);
+  g1.row_scale = L->down_scale;
+  g1.tok_scale = at<float>(ws, w.sh);
+  if (launch_moe_gemm(g1, true, s) != hipSuccess) return MXMOE_ERR_HIP;
+  CombineArgs ca{};
+  ca.Y = at<void>(ws, b.y);
+  ca.y_bf16 = 1;
+  ca.pos = at<int32_t>(ws, b.pos);
+  ca.wts = at<float>(ws, b.wts);
+  ca.out = out;
+  ca.out_bf16 = 1;
+  ca.T = int(T);
+  ca.H = L->H;
+  ca.top_k = L->top_k;
+  return hip_status(launch_combine(ca, s));
 }
 
 }  // extern "C"

@@ -213,30 +213,34 @@ __global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t* __restr
   out[i] = v;
 }
 
-// FP8 weight (N, K) e4m3 codes, row-major -> tiled FP8 order: for row tile
-// t (16 rows), chunk c (128 K) and lane l = 16g + r, 32 bytes: row 16t + r,
-// K bytes 128c + 16g .. +16 then 128c + 64 + 16g .. +16 (zeros past N or K).
-// One thread per 16-byte half of a lane's piece.
-__global__ __launch_bounds__(256) void fp8_tile_kernel(const uint8_t* __restrict__ w, uint4* __restrict__ out, int N,
-                                                      int K, int nc, int64_t total) {
+// 8-bit weights (mats, N, K) (e4m3 or int8 codes), row-major -> the tiled
+// 8-bit order: for matrix m, row tile t (16 rows), chunk c (128 K) and lane
+// l = 16g + r, 32 bytes: row 16t + r, K bytes 128c + 16g .. +16 then
+// 128c + 64 + 16g .. +16 (zeros past N or K).  One thread per 16-byte half
+// of a lane's piece.
+__global__ __launch_bounds__(256) void byte_tile_kernel(const uint8_t* __restrict__ w, uint4* __restrict__ out, int N,
+                                                       int K, int rt4, int nc, int64_t total) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= total) return;
   const int h = int(i & 1), l = int((i >> 1) & 63);
-  const int64_t tc = i >> 7;  // (row tile, chunk)
-  const int c = int(tc % nc), t = int(tc / nc);
+  const int64_t tc = i >> 7;  // (matrix, row tile, chunk)
+  const int c = int(tc % nc);
+  const int64_t mt = tc / nc;
+  const int t = int(mt % rt4);
+  const int64_t m = mt / rt4;
   const int row = 16 * t + (l & 15);
   const int k0 = 128 * c + 64 * h + 16 * (l >> 4);
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (row < N && k0 < K) v = *reinterpret_cast<const uint4*>(w + int64_t(row) * K + k0);
+  if (row < N && k0 < K) v = *reinterpret_cast<const uint4*>(w + (m * N + row) * int64_t(K) + k0);
   out[i] = v;
 }
 
-hipError_t launch_fp8_tile(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream) {
+hipError_t launch_byte_tile(const uint8_t* w, int64_t mats, int N, int K, uint8_t* out, hipStream_t stream) {
   const int rt4 = 4 * ((N + 63) / 64), nc = (K + 127) / 128;
-  const int64_t halves = int64_t(rt4) * nc * 128;
+  const int64_t halves = mats * int64_t(rt4) * nc * 128;
   if (halves == 0) return hipSuccess;
-  fp8_tile_kernel<<<dim3(unsigned((halves + 255) / 256)), dim3(256), 0, stream>>>(w, reinterpret_cast<uint4*>(out), N,
-                                                                                 K, nc, halves);
+  byte_tile_kernel<<<dim3(unsigned((halves + 255) / 256)), dim3(256), 0, stream>>>(w, reinterpret_cast<uint4*>(out), N,
+                                                                                  K, rt4, nc, halves);
   return hipGetLastError();
 }
 

@@ -8,9 +8,11 @@ namespace mxmoe {
 
 // Arithmetic of the expert GEMMs: fp32 or bf16 activations on decoded
 // weights, or FP8 activations on the scaled MXFP4 x FP8 instructions.
-// ACT_W8A8: FP8 activations against FP8 (e4m3) weights in the tiled FP8
-// order (dense linear only; phase 1 epilogue).
-enum Act : int { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2, ACT_W8A8 = 3 };
+// ACT_W8A8: FP8 activations against FP8 (e4m3) weights in the tiled 8-bit
+// order (dense linear only; phase 1 epilogue).  ACT_INT8: int8 activations
+// against int8 weights in the same order, int32 accumulation, per-row
+// weight scales and per-token activation scales applied in the epilogue.
+enum Act : int { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2, ACT_W8A8 = 3, ACT_INT8 = 4 };
 
 // Tile shape of the prefill grouped GEMM: weight rows per workgroup (4 row
 // groups x 16*RT rows), tokens per workgroup tile, and LDS pipeline stages
@@ -84,8 +86,12 @@ hipError_t launch_dense_group(const DenseGroupArgs& a, hipStream_t stream);
 // FP8 static quantisation of a (rows, cols) bf16 tensor to e4m3 codes.
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8_t* q, hipStream_t stream);
 
-// (N, K) FP8 e4m3 codes -> the tiled FP8 order of the dense FP8 layer.
-hipError_t launch_fp8_tile(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream);
+// (mats, N, K) 8-bit codes (e4m3 or int8) -> the tiled 8-bit order.
+hipError_t launch_byte_tile(const uint8_t* w, int64_t mats, int N, int K, uint8_t* out, hipStream_t stream);
+
+// Symmetric int8 per row (dynamic scale amax / 127) of a (rows, K) bf16 tensor.
+hipError_t launch_quant_rows_int8(const uint16_t* x, int64_t rows, int K, int8_t* q, float* scale,
+                                  hipStream_t stream);
 
 struct GemmArgs {
   int act;                    // Act: 0 f32, 1 bf16, 2 fp8
@@ -110,6 +116,8 @@ struct GemmArgs {
   int max_active;             // grid bound: min(E, T*k)
   int max_tiles;              // grid bound of the prefill tile list
   int n_slots;                // T*k
+  const float* row_scale;     // ACT_INT8: (E, R) weight scale per output row
+  const float* tok_scale;     // ACT_INT8: activation scale per token (phase 0, by token id) or per row (phase 1)
 };
 hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream);
 

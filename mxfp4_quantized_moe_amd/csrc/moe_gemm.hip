@@ -92,18 +92,19 @@ __device__ __forceinline__ WBuf expert_weights(const GemmArgs& a, int e) {
   return w;
 }
 
-// FP8 (e4m3) weights of a dense layer in the tiled FP8 order (declared in
-// mxmoe.h): rt4 row tiles of 16 rows x nc 128-wide chunks, 2 KB each, lane
-// (g, r) holding row r's bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of the
-// chunk (the K order of an FP8 MFMA operand).  No scales: one per tensor.
-__device__ __forceinline__ WBuf fp8_weights(const GemmArgs& a) {
+// 8-bit (e4m3 or int8) weights of expert e in the tiled 8-bit order
+// (declared in mxmoe.h): rt4 row tiles of 16 rows x nc 128-wide chunks, 2 KB
+// each, lane (g, r) holding row r's bytes 16g .. 16g+15 and 64+16g ..
+// 64+16g+15 of the chunk (the K order of an 8-bit MFMA operand).  No block
+// scales.
+__device__ __forceinline__ WBuf byte_weights(const GemmArgs& a, int e) {
   WBuf w;
   w.R = a.R;
   w.nb = a.nb;
   w.nc = (a.nb + 3) >> 2;
   w.rt4 = 4 * ((a.R + 63) >> 6);
   const int64_t bb = int64_t(w.rt4) * w.nc * 2048;
-  w.blk = make_rsrc(a.wblk, uint32_t(bb));
+  w.blk = make_rsrc(a.wblk + int64_t(e) * bb, uint32_t(bb));
   w.sc = w.blk;
   return w;
 }
@@ -176,7 +177,7 @@ __device__ __forceinline__ void store_rows_biased(const GemmArgs& a, int r0, int
     const float h1 = clamped_swiglu(v2, v3);
     const int64_t I = a.R / 2;
     const int64_t o = p * I + r0 / 2;
-    if constexpr (ACT == ACT_BF16) {
+    if constexpr (ACT == ACT_BF16 || ACT == ACT_INT8) {  // int8: h stays bf16 until its per-row quantisation
       *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + o) = pack_bf16x2(h0, h1);
     } else if constexpr (ACT == ACT_F32) {
       *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o) = make_float2(h0, h1);
@@ -734,11 +735,13 @@ constexpr int kTiledThreads = 64 * kTiledWaves;
 
 template <int ACT, int PHASE>
 __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefill_tiled_kernel(GemmArgs a) {
-  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8 || ACT == ACT_W8A8, "prefill path takes bf16 or fp8 activations");
+  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8 || ACT == ACT_W8A8 || ACT == ACT_INT8,
+                "prefill path takes bf16, fp8 or int8 activations");
   static_assert(ACT != ACT_W8A8 || PHASE == 1, "FP8 weights: dense layer epilogue only");
   static_assert(kPrefillTokens == 128, "eight 16-token sub-tiles per tile");
   static_assert(kTiledRows % 64 == 0, "waves of 4 row tiles: one scale group per wave");
-  constexpr bool W8 = ACT == ACT_W8A8;  // FP8 weights (32 bytes per lane per chunk, no block scales)
+  constexpr bool W8 = ACT == ACT_W8A8 || ACT == ACT_INT8;  // 8-bit weights (32 bytes per lane per chunk)
+  constexpr bool I8 = ACT == ACT_INT8;  // int8 x int8 -> int32, scales in the epilogue
   constexpr int RT = 4, S = ACT == ACT_BF16 ? MXMOE_PREFILL_TILED_STAGES : MXMOE_PREFILL_TILED_STAGES_FP8;
   constexpr int EB = ACT == ACT_BF16 ? 2 : 1;
   constexpr int KB = 128 * EB;                  // bytes of one token row per chunk
@@ -792,7 +795,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   const int e = ti.x, row_start = ti.y, ntok = ti.z;
   const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
   const int nb = a.nb, K = nb * 32;
-  const WBuf wb = W8 ? fp8_weights(a) : expert_weights<true>(a, e);
+  const WBuf wb = W8 ? byte_weights(a, e) : expert_weights<true>(a, e);
   const int nc = wb.nc;
   const int grow = stripe * kTiledRows + wave * (16 * RT);  // first row of this wave
   const int t0 = grow >> 4;                                   // its first row tile (a scale group start)
@@ -934,9 +937,22 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
             if (nt + 1 < NA) bnext = load_b(nt + 1);
             order_point();
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  av[rt], bcur, acc[rt][nt], W8 ? 0 : 4, 0, 0, W8 ? 127 : int(ascb[rt]), 0, 127);
+            for (int rt = 0; rt < RT; ++rt) {
+              if constexpr (I8) {
+                // two K=64 halves (dwords 0-3, then 4-7 of both operands);
+                // the int32 sums live in the float accumulator registers
+                typedef int i32x4_t __attribute__((ext_vector_type(4)));
+                i32x4_t c = __builtin_bit_cast(i32x4_t, acc[rt][nt]);
+                c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_shufflevector(av[rt], av[rt], 0, 1, 2, 3),
+                                                         __builtin_shufflevector(bcur, bcur, 0, 1, 2, 3), c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_shufflevector(av[rt], av[rt], 4, 5, 6, 7),
+                                                         __builtin_shufflevector(bcur, bcur, 4, 5, 6, 7), c, 0, 0, 0);
+                acc[rt][nt] = __builtin_bit_cast(f32x4_t, c);
+              } else {
+                acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    av[rt], bcur, acc[rt][nt], W8 ? 0 : 4, 0, 0, W8 ? 127 : int(ascb[rt]), 0, 127);
+              }
+            }
             bcur = bnext;
           }
         }
@@ -992,11 +1008,25 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
       if (rt < rt_active) {
         // bias of this lane's 4 output rows (raw bf16 bits)
         const uint2 q = *reinterpret_cast<const uint2*>(sBias + 2 * (wave * 16 * RT + 16 * rt + 4 * g));
+        float4 rs = make_float4(1.f, 1.f, 1.f, 1.f);  // int8: weight scales of the 4 rows
+        if constexpr (I8)
+          rs = *reinterpret_cast<const float4*>(a.row_scale + int64_t(e) * a.R + grow + 16 * rt + 4 * g);
 #pragma unroll
         for (int nt = 0; nt < NA; ++nt) {
           const int j = nt * 16 + r16;
           if (j < ntok) {
-            const f32x4_t v = acc[rt][nt];
+            f32x4_t v = acc[rt][nt];
+            if constexpr (I8) {
+              // exact int32 sums -> fp32, times the row's and the token's
+              // scales (the whole vector is reinterpreted: a bit cast of one
+              // element of a vector value reads element 0 with this compiler)
+              typedef int i32x4_t __attribute__((ext_vector_type(4)));
+              const i32x4_t iv = __builtin_bit_cast(i32x4_t, acc[rt][nt]);
+              const int p = row_start + j;
+              const float ts = a.tok_scale[PHASE == 0 ? a.sorted_tok[p] : p];
+              v = f32x4_t{float(iv[0]) * rs.x * ts, float(iv[1]) * rs.y * ts, float(iv[2]) * rs.z * ts,
+                          float(iv[3]) * rs.w * ts};
+            }
             store_rows_biased<ACT, PHASE>(a, grow + 16 * rt + 4 * g, row_start + j,
                                           v[0] * a.acc_scale + __uint_as_float(q.x << 16),
                                           v[1] * a.acc_scale + __uint_as_float(q.x & 0xFFFF0000u),
@@ -1215,7 +1245,7 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_tiled_kernel(GemmArgs a) {
 
 template <int ACT, int PHASE, bool TILED>
 static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
-  if constexpr (ACT == ACT_W8A8) {  // dense FP8 layer: the tiled LDS-staged kernel only
+  if constexpr (ACT == ACT_W8A8 || ACT == ACT_INT8) {  // 8-bit weights: the tiled LDS-staged kernel only
     const int64_t items = (int64_t(a.max_tiles) * ((a.R + kTiledRows - 1) / kTiledRows) + 7) / 8 * 8;
     gemm_prefill_tiled_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kTiledThreads), 0, stream>>>(a);
   } else if (prefill) {
@@ -1258,6 +1288,12 @@ hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream) 
     case ACT_W8A8 * 2 + 1:
       if (!a.tiled || !prefill) return hipErrorInvalidValue;  // only the tiled LDS-staged kernel
       launch_layout<ACT_W8A8, 1, true>(a, true, stream);
+      break;
+    case ACT_INT8 * 2 + 0:
+    case ACT_INT8 * 2 + 1:
+      if (!a.tiled || !prefill) return hipErrorInvalidValue;
+      if (a.phase == 0) launch_layout<ACT_INT8, 0, true>(a, true, stream);
+      else launch_layout<ACT_INT8, 1, true>(a, true, stream);
       break;
     default: return hipErrorInvalidValue;
   }

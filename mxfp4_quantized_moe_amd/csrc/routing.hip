@@ -714,6 +714,59 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, float inv_scale, uint8
   return hipGetLastError();
 }
 
+// ------------------------------------------------ int8 per-row quantisation
+//
+// Symmetric int8 with one dynamic scale per row (per token): s = amax / 127
+// over the row's |values| (fp32, a correctly rounded division), code =
+// clamp(rne(v / s), -127, 127), all codes 0 when the row is all zero (s = 0).
+// One workgroup per row; each thread reads 8 bf16 values at a time.
+
+__global__ __launch_bounds__(256) void quant_rows_int8_kernel(const uint4* __restrict__ x, int K8, int8_t* q,
+                                                              float* scale) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint4* xr = x + row * K8;
+  float m = 0.f;
+  for (int i = threadIdx.x; i < K8; i += 256) {
+    const uint4 v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(w[j] << 16)));
+      m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const float s = amax / 127.0f;
+  if (threadIdx.x == 0) scale[row] = s;
+  uint2* qr = reinterpret_cast<uint2*>(q + row * int64_t(K8) * 8);
+  for (int i = threadIdx.x; i < K8; i += 256) {
+    const uint4 v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+      float c = amax > 0.f ? __builtin_rintf(f / s) : 0.f;
+      c = __builtin_fminf(__builtin_fmaxf(c, -127.f), 127.f);
+      packed[j >> 2] |= (uint32_t(int(c)) & 0xFFu) << (8 * (j & 3));
+    }
+    qr[i] = make_uint2(packed[0], packed[1]);
+  }
+}
+
+hipError_t launch_quant_rows_int8(const uint16_t* x, int64_t rows, int K, int8_t* q, float* scale,
+                                  hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  quant_rows_int8_kernel<<<dim3(unsigned(rows)), dim3(256), 0, stream>>>(reinterpret_cast<const uint4*>(x), K / 8, q,
+                                                                        scale);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- calibration
 //
 // amax over bf16 tensors: |v| as an unsigned bit pattern orders like the

@@ -76,6 +76,8 @@ __all__ = [
     "routing_margin",
     "mxfp4_linear",
     "fp8_linear",
+    "int8_quant_rows",
+    "moe_forward_int8",
 ]
 
 # ---------------------------------------------------------------------------
@@ -467,6 +469,70 @@ def fp8_linear(x: np.ndarray, w_codes: np.ndarray, w_scale: float, x_scale: floa
     if bias is not None:
         y = y + widen(bias, "bf16")
     return y
+
+
+def int8_quant_rows(v: np.ndarray):
+    """Symmetric int8 with one dynamic scale per row (per token), the W8A8
+    scheme of the gpt-oss-20b-BF16-w8a8-llmcompressor page ("Quantization":
+    activations int8, symmetric, per-token dynamic).  The scale and the code
+    are decided in float32, as a device would: s = fp32(amax|row|) / 127,
+    code = clamp(rne(fp32(v) / s), -127, 127); an all-zero row has s = 0 and
+    codes 0.  Returns (codes int64 (rows, K), scales float64 (rows,))."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(f), axis=1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.rint((f / safe[:, None]).astype(np.float32)).astype(np.float64)
+    q = np.clip(q, -127, 127)
+    q = np.where(s[:, None] > 0, q, 0.0)
+    return q.astype(np.int64), s.astype(np.float64)
+
+
+def moe_forward_int8(layer8, x: np.ndarray, route_override=None, return_parts: bool = False):
+    """The INT8 W8A8 MoE layer (gpt-oss-20b-BF16-w8a8-llmcompressor page,
+    "Quantization": weights int8 per output channel with static scales,
+    activations int8 per token with dynamic scales, router and biases kept
+    in bf16).
+
+    layer8: a workloads.Int8MoELayer (int8 codes, fp32 per-row scales, bf16
+    bits elsewhere); x: (T, H) bf16 bits.  Steps: route (as moe_forward);
+    x -> int8 per token; per expert G = (x_code W_code^T) s_x s_w + b_gu
+    (the integer sums exact); h = clamped SwiGLU, rounded to bf16; h -> int8
+    per routed row; Y = (h_code W_code^T) s_h s_w + b_d; out_t =
+    sum_j w[t, j] Y(t, j) in slot order.
+    Returns out (T, H) float64, unrounded (and the parts if asked)."""
+    L = layer8
+    E, H, I, k = L.E, L.H, L.I, L.top_k
+    xf = bf16_from_bits(x)
+    T = xf.shape[0]
+    idx, w, _ = route(xf, bf16_from_bits(L.router_w), bf16_from_bits(L.router_b), k)
+    if route_override is not None:
+        idx = np.asarray(route_override[0], dtype=np.int32)
+        w = np.asarray(route_override[1], dtype=np.float64)
+    counts, offsets, sorted_slots, slot_pos = permute(idx, E)
+    xq, sx = int8_quant_rows(xf)
+    b_gu = bf16_from_bits(L.gate_up_bias)
+    b_d = bf16_from_bits(L.down_bias)
+    Y = np.zeros((T * k, H))
+    hb = np.zeros((T * k, I))
+    for e in range(E):
+        sl = sorted_slots[offsets[e] : offsets[e + 1]]
+        if sl.size == 0:
+            continue
+        tok = sl // k
+        acc = xq[tok] @ L.gate_up_codes[e].astype(np.int64).T  # exact integers
+        G = acc * sx[tok][:, None] * L.gate_up_scale[e].astype(np.float64) + b_gu[e]
+        h = round_bf16(swiglu_clamped(G[:, 0::2], G[:, 1::2]))
+        hb[sl] = h
+        hq, sh = int8_quant_rows(h)
+        acc2 = hq @ L.down_codes[e].astype(np.int64).T
+        Y[sl] = acc2 * sh[:, None] * L.down_scale[e].astype(np.float64) + b_d[e]
+    out = np.zeros((T, H))
+    for j in range(k):
+        out += w[:, j : j + 1] * Y[np.arange(T) * k + j]
+    if return_parts:
+        return out, dict(idx=idx, w=w, h=hb, Y=Y, xq=xq, sx=sx)
+    return out
 
 
 def moe_forward_dense(layer, x: np.ndarray, act_dtype: str) -> np.ndarray:

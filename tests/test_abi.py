@@ -269,3 +269,40 @@ def test_fp8_linear_validation(lib):
     assert call(ws_bytes=need - 1) == WS
     assert lib.fp8_linear_workspace_bytes(8, 48, 64) == 0
     assert lib.fp8_linear_workspace_bytes(-1, 64, 64) == 0
+
+
+def _int8_layer(**kw):
+    d = dict(E=8, H=64, I=64, top_k=2, gate_up_w=P, gate_up_scale=P, gate_up_bias=P, down_w=P, down_scale=P,
+             down_bias=P, router_w=P, router_b=P)
+    d.update(kw)
+    return B.Int8Layer(**d)
+
+
+def test_int8_validation(lib):
+    n = ctypes.c_int64(0)
+    assert lib.int8_tiled_bytes(3, 96, 160, ctypes.byref(n)) == OK and n.value == 3 * 8 * 2 * 2048
+    assert lib.int8_tiled_bytes(1, 96, 48, ctypes.byref(n)) == SHAPE
+    assert lib.int8_tiled_bytes(1, 96, 64, None) == NULL
+    assert lib.int8_tile(P, 1, 64, 40, P, None) == SHAPE
+    assert lib.int8_tile(None, 1, 64, 64, P, None) == NULL
+    assert lib.int8_tile(P, 1, 64, 64, P + 1, None) == ALIGN
+    assert lib.int8_tile(None, 0, 64, 64, None, None) == OK  # no matrices: no-op
+
+    def fwd(L, T=8, x=P, out=P, idx=None, w=None, ws=P, ws_bytes=1 << 30):
+        return lib.moe_int8_forward(ctypes.byref(L), x, T, out, idx, w, ws, ws_bytes, None)
+
+    assert fwd(_int8_layer(H=48)) == SHAPE
+    assert fwd(_int8_layer(top_k=9)) == SHAPE
+    assert fwd(_int8_layer(E=0)) == SHAPE
+    assert fwd(_int8_layer(down_scale=None)) == NULL
+    assert fwd(_int8_layer(router_b=P + 2)) == ALIGN
+    assert fwd(_int8_layer(), T=-1) == SHAPE
+    assert fwd(_int8_layer(), T=0, x=None, out=None, ws=None) == OK
+    assert fwd(_int8_layer(), x=None) == NULL
+    assert fwd(_int8_layer(), idx=P + 4) == ALIGN
+    L = _int8_layer()
+    need = lib.moe_int8_workspace_bytes(ctypes.byref(L), 8)
+    # routing tables, h and Y in bf16, x and h as int8 with one fp32 scale per row
+    assert need >= 8 * 2 * (64 * 2 + 64 * 2) + 8 * 64 + 8 * 2 * 64
+    assert fwd(L, ws_bytes=need - 1) == WS
+    assert lib.moe_int8_workspace_bytes(ctypes.byref(_int8_layer(I=40)), 8) == 0

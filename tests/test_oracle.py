@@ -574,3 +574,71 @@ def test_fp8_linear_saturates_inputs():
 def test_fp8_linear_rejects_mismatched_k():
     with pytest.raises(ValueError):
         O.fp8_linear(_bf16(np.zeros((2, 32))), np.zeros((3, 64), np.uint8), 1.0, 1.0)
+
+
+# ------------------------------------------------------ int8 W8A8 layer
+
+
+def test_int8_quant_rows_matches_torch():
+    """Scale fp32(amax) / 127 and code round-half-to-even(fp32 v / s),
+    clamped to +-127, against torch's fp32 division and torch.round."""
+    rng = np.random.default_rng(11)
+    v = O.bf16_from_bits(_bf16(rng.normal(0, 2, size=(7, 96))))
+    v[3, 5] = 0.0  # a zero among the values
+    q, s = O.int8_quant_rows(v)
+    t = torch.from_numpy(v.astype(np.float32))
+    ts = t.abs().amax(dim=1) / torch.tensor(127.0, dtype=torch.float32)
+    tq = torch.round(t / ts[:, None]).clamp(-127, 127).to(torch.int64)
+    assert np.array_equal(s, ts.numpy().astype(np.float64))
+    assert np.array_equal(q, tq.numpy())
+    # the largest magnitude of a row always maps to +-127
+    for r in range(v.shape[0]):
+        j = int(np.argmax(np.abs(v[r])))
+        assert abs(q[r, j]) == 127
+
+
+def test_int8_quant_rows_special_cases():
+    q, s = O.int8_quant_rows(np.zeros((2, 32)))
+    assert np.all(q == 0) and np.all(s == 0)
+    row = np.zeros((1, 32))
+    row[0, 7] = -3.0
+    q, s = O.int8_quant_rows(row)
+    assert s[0] == np.float64(np.float32(3.0) / np.float32(127.0))
+    assert q[0, 7] == -127 and np.count_nonzero(q) == 1
+
+
+def test_int8_integer_sums_are_exact():
+    """127 * 127 * 2880 < 2^31: the int32 sums of a row are exact, and the
+    oracle keeps them as integers (x scale 1 when amax = 127)."""
+    L = W.int8_case(2, 1, 2880, 32, 1, 1).layer
+    L.gate_up_codes[:] = 127
+    x = _bf16(np.full((1, 2880), 127.0))
+    out, parts = O.moe_forward_int8(L, x, return_parts=True)
+    assert np.array_equal(parts["xq"], np.full((1, 2880), 127))
+    assert parts["sx"][0] == 1.0
+
+
+def test_int8_layer_matches_dense_brute_force():
+    """Every expert for every token, weighted by a (T, E) matrix that is
+    zero outside the top-k, written out here from the definition with plain
+    loops over experts (tiny inputs)."""
+    case = W.int8_case(7, 5, 64, 32, 2, 9)
+    L = case.layer
+    out = O.moe_forward_int8(L, case.x)
+    xf = O.bf16_from_bits(case.x)
+    idx, w, _ = O.route(xf, O.bf16_from_bits(L.router_w), O.bf16_from_bits(L.router_b), L.top_k)
+    xq, sx = O.int8_quant_rows(xf)
+    ref = np.zeros_like(out)
+    for t in range(case.T):
+        for e in range(L.E):
+            hit = [j for j in range(L.top_k) if idx[t, j] == e]
+            if not hit:
+                continue
+            G = np.array([sum(int(xq[t, c]) * int(L.gate_up_codes[e, r, c]) for c in range(L.H))
+                          for r in range(2 * L.I)], dtype=np.float64)
+            G = G * sx[t] * L.gate_up_scale[e].astype(np.float64) + O.bf16_from_bits(L.gate_up_bias[e])
+            h = O.round_bf16(O.swiglu_clamped(G[0::2], G[1::2]))[None, :]
+            hq, sh = O.int8_quant_rows(h)
+            Y = (hq[0] @ L.down_codes[e].astype(np.int64).T) * sh[0] * L.down_scale[e].astype(np.float64)
+            ref[t] += w[t, hit[0]] * (Y + O.bf16_from_bits(L.down_bias[e]))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)

@@ -256,6 +256,81 @@ def fp8_linear_case(seed: int, T: int, K: int, N: int, bias: bool = True, w_scal
     return Fp8LinearCase(f"fp8_linear_s{seed}_t{T}_k{K}_n{N}", x, codes, w_scale, x_scale, b)
 
 
+@dataclass
+class Int8MoELayer:
+    """One INT8 W8A8 MoE layer's parameters (host copies): int8 codes with
+    fp32 per-row scales, bf16 bits for the biases and the router."""
+
+    E: int
+    H: int
+    I: int
+    top_k: int
+    gate_up_codes: np.ndarray  # (E, 2I, H) int8, rows gate/up interleaved
+    gate_up_scale: np.ndarray  # (E, 2I) float32
+    gate_up_bias: np.ndarray   # (E, 2I) bf16 bits
+    down_codes: np.ndarray     # (E, H, I) int8
+    down_scale: np.ndarray     # (E, H) float32
+    down_bias: np.ndarray      # (E, H) bf16 bits
+    router_w: np.ndarray       # (E, H) bf16 bits
+    router_b: np.ndarray       # (E,) bf16 bits
+
+
+def int8_layer(rng: np.random.Generator, E: int, H: int, I: int, top_k: int, scale_lo: float = 2e-4,
+               scale_hi: float = 8e-4, bias_std: float = 0.01, router_std: float = 0.02,
+               router_bias_std: float = 0.01) -> Int8MoELayer:
+    """Draw order: gate_up codes, scales, bias; down codes, scales, bias;
+    router weight, bias.  Codes uniform on [-127, 127]; per-row scales
+    uniform on [scale_lo, scale_hi] (fp32), which keeps G of order one at
+    H = 2880 with x ~ N(0, 1)."""
+    assert H % 32 == 0 and I % 32 == 0
+    gu = rng.integers(-127, 128, size=(E, 2 * I, H), dtype=np.int64).astype(np.int8)
+    gus = rng.uniform(scale_lo, scale_hi, size=(E, 2 * I)).astype(np.float32)
+    gub = _real(rng, (E, 2 * I), bias_std, BF16)
+    dn = rng.integers(-127, 128, size=(E, H, I), dtype=np.int64).astype(np.int8)
+    dns = rng.uniform(scale_lo, scale_hi, size=(E, H)).astype(np.float32)
+    dnb = _real(rng, (E, H), bias_std, BF16)
+    rw = _real(rng, (E, H), router_std, BF16)
+    rb = _real(rng, (E,), router_bias_std, BF16)
+    return Int8MoELayer(E, H, I, top_k, gu, gus, gub, dn, dns, dnb, rw, rb)
+
+
+@dataclass
+class Int8Case:
+    name: str
+    layer: Int8MoELayer
+    x: np.ndarray  # (T, H) bf16 bits
+
+    @property
+    def T(self) -> int:
+        return self.x.shape[0]
+
+
+def int8_case(seed: int, E: int, H: int, I: int, top_k: int, T: int) -> Int8Case:
+    rng = np.random.default_rng(seed)
+    layer = int8_layer(rng, E, H, I, top_k)
+    x = _real(rng, (T, H), 1.0, BF16)
+    return Int8Case(f"int8_s{seed}_e{E}_h{H}_i{I}_k{top_k}_t{T}", layer, x)
+
+
+def int8_20b(T: int, seed: int = 0) -> Int8Case:
+    """The gpt-oss-20b shape (E=32, top-4, H=I=2880) as an INT8 W8A8 layer
+    with T bf16 tokens ~N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    layer = int8_layer(rng, 32, 2880, 2880, 4)
+    x = _real(rng, (T, 2880), 1.0, BF16)
+    return Int8Case(f"gpt_oss_20b_int8_w8a8_t{T}", layer, x)
+
+
+def int8_layer_to_torch(layer: Int8MoELayer, device):
+    """The layer's arrays as device tensors, weights tiled by the library."""
+    from mxfp4_quantized_moe_amd import MoEInt8Weights
+
+    return MoEInt8Weights.from_codes(_t(layer.gate_up_codes, device), _t(layer.gate_up_scale, device),
+                                     _t(layer.gate_up_bias, device), _t(layer.down_codes, device),
+                                     _t(layer.down_scale, device), _t(layer.down_bias, device),
+                                     _t(layer.router_w, device), _t(layer.router_b, device), layer.top_k)
+
+
 def random_weights(seed: int, rows: int, k: int, std: float = 1.0, dtype: str = F32) -> np.ndarray:
     """A dense weight matrix to be packed (pack parity cases)."""
     rng = np.random.default_rng(seed)
