@@ -281,7 +281,9 @@ typedef struct {
    * stage that does not run records its event at the same point as the
    * next.  NULL records nothing, and a NULL entry skips that one event:
    * each record takes a few microseconds of stream time, so a caller timing
-   * one stage passes only the two handles around it. */
+   * one stage passes only the two handles around it.  A batch of at most 16
+   * tokens runs router and grouping as one launch unless event 1 (between
+   * them) is given. */
   void* const* stage_events;
   int32_t expert_path;   /* mxmoe_path_t: which experts each token passes through */
 } mxmoe_fwd_opts_t;

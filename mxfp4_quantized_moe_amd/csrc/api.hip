@@ -149,10 +149,10 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   ra.wts = at<float>(ws, w.wts);
   ra.idx_out = idx_out;
   ra.wts_out = w_out;
-  hipError_t e = launch_route(ra, s);
-  if (e != hipSuccess) return e;
-  if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
   if (dense) {
+    hipError_t e = launch_route(ra, s);
+    if (e != hipSuccess) return e;
+    if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
     DenseGroupArgs da{};
     da.idx = ra.idx;
     da.T = int(T);
@@ -182,7 +182,13 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   pa.tiles = at<int4>(ws, w.tiles);
   pa.counts_out = counts_out;
   pa.offsets_out = offsets_out;
-  return launch_permute(pa, s);
+  if (mid) {  // the stage boundary is recorded: two launches
+    hipError_t e = launch_route(ra, s);
+    if (e != hipSuccess) return e;
+    if ((e = hipEventRecord(mid, s)) != hipSuccess) return e;
+    return launch_permute(pa, s);
+  }
+  return launch_route_permute(ra, pa, s);
 }
 
 GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t T, int act, int phase,

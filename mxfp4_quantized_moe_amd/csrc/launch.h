@@ -37,19 +37,6 @@ hipError_t launch_pack(const void* w, bool in_bf16, int64_t nblocks, uint8_t* bl
 hipError_t launch_tile(const uint8_t* blocks, const uint8_t* scales, int64_t mats, int rows, int nb,
                        uint8_t* tiled_blocks, uint8_t* tiled_scales, hipStream_t stream);
 
-struct RouteArgs {
-  const void* x;        // (T, H) act dtype
-  const void* w_r;      // (E, H) same dtype
-  const void* b_r;      // (E,)
-  int act_bf16;         // 1 = bf16 x and router, 0 = fp32
-  int T, H, E, top_k;
-  int32_t* idx;         // (T, k) workspace
-  float* wts;           // (T, k) workspace
-  int32_t* idx_out;     // optional copies
-  float* wts_out;
-};
-hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
-
 struct PermuteArgs {
   const int32_t* idx;   // (T*k)
   int n_slots, E;
@@ -65,6 +52,22 @@ struct PermuteArgs {
   int32_t* counts_out;  // optional copies
   int32_t* offsets_out;
 };
+struct RouteArgs {
+  const void* x;        // (T, H) act dtype
+  const void* w_r;      // (E, H) same dtype
+  const void* b_r;      // (E,)
+  int act_bf16;         // 1 = bf16 x and router, 0 = fp32
+  int T, H, E, top_k;
+  int32_t* idx;         // (T, k) workspace
+  float* wts;           // (T, k) workspace
+  int32_t* idx_out;     // optional copies
+  float* wts_out;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+// Router then grouping; one launch when one 16-wave router workgroup covers
+// the batch (the grouping then runs in that workgroup after the top-k).
+hipError_t launch_route_permute(const RouteArgs& a, const PermuteArgs& p, hipStream_t stream);
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 
 // Grouping of the dense all-experts path: rows e*T + t for every expert e

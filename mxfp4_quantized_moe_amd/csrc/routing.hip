@@ -183,8 +183,14 @@ __device__ __forceinline__ uint4 lane_permute(uint4 v, int perm) {
                     uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(v.w))));
 }
 
-template <bool BF16, int RG, int NG, int KW>
-__global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
+// The grouping of one workgroup of kPermThreads threads (defined below).
+__device__ void permute_block(const PermuteArgs& a);
+
+// FUSE: the workgroup (the only one, 16 waves) goes on to group the slots
+// once its top-k are written.
+template <bool BF16, int RG, int NG, int KW, bool FUSE>
+__global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a, PermuteArgs pa) {
+  static_assert(!FUSE || KW == 16, "the grouping takes one workgroup of 16 waves");
   extern __shared__ float part[];  // [KW][16][E]
   __shared__ float sbias[256];     // b_r, read before the contraction
   constexpr int kLanesPerToken = 4 * KW;
@@ -297,23 +303,27 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a) {
     if (a.top_k <= 4) topk_softmax<4, kLanesPerToken>(a, part + 4 * tl, t0 + tl);
     else topk_softmax<MAX_TOPK_DEV, kLanesPerToken>(a, part + 4 * tl, t0 + tl);
   }
+  if constexpr (FUSE) {
+    __syncthreads();  // the expert ids written above are visible to the whole workgroup
+    permute_block(pa);
+  }
 }
 
-template <bool BF16, int KW>
-static void launch_route_typed(const RouteArgs& a, unsigned grid, hipStream_t stream) {
+template <bool BF16, int KW, bool FUSE = false>
+static void launch_route_typed(const RouteArgs& a, unsigned grid, hipStream_t stream, const PermuteArgs& pa = {}) {
   const size_t lds = size_t(KW) * kRouteTokens * ((a.E + 15) & ~15) * sizeof(float);
   const dim3 g(grid), b(64 * KW);
   // register tiles sized to E (fp32 operands take twice the registers)
   if (a.E <= 32)
-    route_kernel<BF16, 2, 1, KW><<<g, b, lds, stream>>>(a);
+    route_kernel<BF16, 2, 1, KW, FUSE><<<g, b, lds, stream>>>(a, pa);
   else if constexpr (BF16 || KW <= 8) {  // fp32 past E = 32: at most 8 waves (registers)
     if (a.E <= 64)
-      route_kernel<BF16, 4, 1, KW><<<g, b, lds, stream>>>(a);
+      route_kernel<BF16, 4, 1, KW, FUSE><<<g, b, lds, stream>>>(a, pa);
     else if constexpr (KW <= 8) {  // E > 64 takes at most 8 waves (LDS bound)
       if (a.E <= 128)
-        route_kernel<BF16, (BF16 ? 8 : 4), (BF16 ? 1 : 2), KW><<<g, b, lds, stream>>>(a);
+        route_kernel<BF16, (BF16 ? 8 : 4), (BF16 ? 1 : 2), KW, FUSE><<<g, b, lds, stream>>>(a, pa);
       else if constexpr (KW == 4)  // E > 128 always takes 4 waves
-        route_kernel<BF16, 4, 4, KW><<<g, b, lds, stream>>>(a);
+        route_kernel<BF16, 4, 4, KW, FUSE><<<g, b, lds, stream>>>(a, pa);
     }
   }
 }
@@ -371,7 +381,7 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
   return x - v;
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) {
+__device__ void permute_block(const PermuteArgs& a) {
   __shared__ int cnt[256];
   __shared__ int off[257];
   __shared__ int toff[257];
@@ -485,6 +495,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) {
     __syncthreads();
   }
 }
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) { permute_block(a); }
 
 // Expert-parallel grouping for large batches: workgroup e handles expert e.
 // Every workgroup builds the full histogram in LDS (integer counts, order
@@ -606,6 +618,20 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   else
     permute_kernel<<<dim3(1), dim3(kPermThreads), 0, stream>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const RouteArgs& a, const PermuteArgs& p, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  static_assert(kPermThreads == 64 * 16, "the fused grouping runs on the router's 16 waves");
+  const bool one_group = a.T <= kRouteTokens;  // one router workgroup
+  if (one_group && a.E <= (a.act_bf16 ? 64 : 32) && p.n_slots <= kPermSmall) {
+    if (a.act_bf16) launch_route_typed<true, 16, true>(a, 1, stream, p);
+    else launch_route_typed<false, 16, true>(a, 1, stream, p);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_route(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_permute(p, stream);
 }
 
 // --------------------------------------------------------------- FP8 quant
