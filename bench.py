@@ -187,6 +187,32 @@ def cpu_baseline(case, budget_s: float, dense: bool = False):
                       f"{'every expert' if dense and not case.fp8 else 'their routed experts'}"}
 
 
+def oracle_slices(fn, total: int, budget_s: float, what: str) -> dict:
+    """The oracle as it stands, fn(lo, hi) on slices [lo, hi) of `total`
+    rows of doubling size until about budget_s seconds are used.  Returns
+    rows per second with the sample description."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        cores = int(info[0]["num_threads"]) if info else os.cpu_count()
+        blas = info[0].get("internal_api", "blas") if info else "unknown"
+    except Exception:
+        cores, blas = os.cpu_count(), "unknown"
+    n, done, elapsed = 1, 0, 0.0
+    while done < total:
+        hi = min(done + n, total)
+        t0 = time.perf_counter()
+        fn(done, hi)
+        elapsed += time.perf_counter() - t0
+        done = hi
+        if elapsed >= budget_s:
+            break
+        n = min(n * 2, total - done)
+    return {"rows_per_s": done / elapsed, "cores": cores, "kind": "oracle",
+            "sample": f"first {done} of {total} {what}, float64 NumPy ({blas}), {elapsed:.1f} s, slices of doubling size"}
+
+
 # ------------------------------------------------------------ main legs
 
 def bench_layer(args, dev):
@@ -333,7 +359,18 @@ def bench_unpack(args, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     gbps = byts * args.steps / (t1 - t0) / 1e9
-    return {"metric": "mxfp4_unpack GB/s (bf16 out)", "value": gbps, "unit": "GB/s", "n_gpus": 1,
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+
+        b0, s0 = case.tensors[0]
+        rb, rs = b0.reshape(-1, b0.shape[-2], 16), s0.reshape(-1, s0.shape[-1])
+        row_bytes = rb.shape[1] * 16 + rb.shape[1] + rb.shape[1] * 32 * 2
+        r = oracle_slices(lambda lo, hi: O.mxfp4_unpack(rb[lo:hi], rs[lo:hi]), rb.shape[0], args.cpu_budget,
+                          "gate_up rows")
+        cpu = {"value": r["rows_per_s"] * row_bytes / 1e9, "unit": "GB/s", "cores": r["cores"], "kind": "oracle",
+               "sample": r["sample"]}
+    return {"metric": "mxfp4_unpack GB/s (bf16 out)", "value": gbps, "unit": "GB/s", "n_gpus": 1, "cpu_baseline": cpu,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": (t1 - t0) * 1e3 / args.steps,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8->bf16",
             "data": "synthetic", "config": {"workload": case.name, "bytes_per_step": byts},
@@ -378,7 +415,16 @@ def bench_linear(args, dev):
     call_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
     fl = 2 * T * K * N
     achieved = fl / call_s / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+
+        r = oracle_slices(lambda lo, hi: O.mxfp4_linear(case.x[lo:hi], case.blocks, case.scales, case.bias, "bf16"),
+                          T, args.cpu_budget, "tokens")
+        cpu = {"value": r["rows_per_s"], "unit": "tokens/s", "cores": r["cores"], "kind": "oracle",
+               "sample": r["sample"]}
     return {"metric": "MXFP4 dense linear tokens/s", "value": T * args.steps / (t1 - t0), "unit": "tokens/s",
+            "cpu_baseline": cpu,
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": (t1 - t0) * 1e3 / args.steps,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded random MXFP4 weight and bf16 activations)",
@@ -425,7 +471,16 @@ def bench_fp8_linear(args, dev):
     call_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
     fl = 2 * T * K * N
     achieved = fl / call_s / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+
+        r = oracle_slices(lambda lo, hi: O.fp8_linear(case.x[lo:hi], case.w_codes, case.w_scale, case.x_scale,
+                                                      case.bias), T, args.cpu_budget, "tokens")
+        cpu = {"value": r["rows_per_s"], "unit": "tokens/s", "cores": r["cores"], "kind": "oracle",
+               "sample": r["sample"]}
     return {"metric": "FP8 W8A8 dense linear tokens/s", "value": T * args.steps / (t1 - t0), "unit": "tokens/s",
+            "cpu_baseline": cpu,
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": (t1 - t0) * 1e3 / args.steps,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
             "data": "synthetic (seeded random e4m3 weight codes and bf16 activations, fixed static scales)",
@@ -473,7 +528,15 @@ def bench_int8(args, dev):
     call_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
     ops = 2 * T * L.top_k * (2 * L.I * L.H + L.H * L.I)
     achieved = ops / call_s / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+
+        r = oracle_slices(lambda lo, hi: O.moe_forward_int8(L, case.x[lo:hi]), T, args.cpu_budget, "tokens")
+        cpu = {"value": r["rows_per_s"], "unit": "tokens/s", "cores": r["cores"], "kind": "oracle",
+               "sample": r["sample"]}
     return {"metric": "INT8 W8A8 MoE layer tokens/s", "value": T * args.steps / (t1 - t0), "unit": "tokens/s",
+            "cpu_baseline": cpu,
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": (t1 - t0) * 1e3 / args.steps,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
             "data": "synthetic (seeded random int8 codes, per-row scales, bf16 activations)",
