@@ -779,18 +779,36 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
 
-  // Work items (token tile, row stripe), stripe fastest.  The grid is sized
-  // for the most tiles a routing can produce; the valid items are the first
-  // nvalid.  Hardware places workgroup b on XCD b % 8, so XCD x takes the
-  // x-th eighth of the valid items, in order: every XCD gets an even share
-  // and the stripes of one token tile run on one XCD, sharing its L2.
+  // Work items (expert, row stripe, token tile), token tile fastest: the
+  // workgroups that neighbour each other in launch order stream the same
+  // weight stripe for the expert's several token tiles, so all but the first
+  // read of it come from L2 (a tile-major order re-read every expert's
+  // weights once per token tile).  The grid is sized for the most tiles a
+  // routing can produce; the valid items are the first nvalid.  Hardware
+  // places workgroup b on XCD b % 8, so XCD x takes the x-th eighth of the
+  // valid items, in order: every XCD gets an even share and an expert's
+  // stripes mostly stay on one XCD, sharing its L2.
   const int nstripes = (a.R + kTiledRows - 1) / kTiledRows;
   const int nvalid = a.tile_off[a.E] * nstripes;
   const int per_xcd = (nvalid + 7) >> 3;
   const int idx = blockIdx.x >> 3;
   const int item = (blockIdx.x & 7) * per_xcd + idx;
-  if (idx >= per_xcd || item >= nvalid) return;
-  const int tile = item / nstripes, stripe = item - tile * nstripes;
+  if (idx >= per_xcd || item >= nvalid) return;  // uniform per workgroup
+  // Expert e owns items [tile_off[e], tile_off[e+1]) * nstripes; binary
+  // search for it (tile_off is non-decreasing from 0, so the item lies in a
+  // non-empty range: nt_e >= 1).
+  __shared__ int s_toff[257];  // E <= 256, checked on the host
+  for (int i = threadIdx.x; i <= a.E; i += kTiledThreads) s_toff[i] = a.tile_off[i];
+  __syncthreads();
+  int lo = 0, hi = a.E;  // s_toff[lo] * nstripes <= item < s_toff[hi] * nstripes
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_toff[mid] * nstripes <= item) lo = mid;
+    else hi = mid;
+  }
+  const int nt_e = s_toff[lo + 1] - s_toff[lo];
+  const int local = item - s_toff[lo] * nstripes;
+  const int stripe = local / nt_e, tile = s_toff[lo] + (local - stripe * nt_e);
   const int4 ti = a.tiles[tile];  // {expert, first sorted row, tokens}
   const int e = ti.x, row_start = ti.y, ntok = ti.z;
   const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
