@@ -794,21 +794,31 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   const int idx = blockIdx.x >> 3;
   const int item = (blockIdx.x & 7) * per_xcd + idx;
   if (idx >= per_xcd || item >= nvalid) return;  // uniform per workgroup
-  // Expert e owns items [tile_off[e], tile_off[e+1]) * nstripes; binary
-  // search for it (tile_off is non-decreasing from 0, so the item lies in a
-  // non-empty range: nt_e >= 1).
-  __shared__ int s_toff[257];  // E <= 256, checked on the host
-  for (int i = threadIdx.x; i <= a.E; i += kTiledThreads) s_toff[i] = a.tile_off[i];
-  __syncthreads();
-  int lo = 0, hi = a.E;  // s_toff[lo] * nstripes <= item < s_toff[hi] * nstripes
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_toff[mid] * nstripes <= item) lo = mid;
-    else hi = mid;
+  int tile, stripe;
+  if (a.E == 1) {
+    // One weight matrix (a dense linear): stripe fastest instead, so each XCD
+    // reads an eighth of the activations, which outweigh the 4- or 8-bit
+    // weights, rather than all of them.
+    tile = item / nstripes;
+    stripe = item - tile * nstripes;
+  } else {
+    // Expert e owns items [tile_off[e], tile_off[e+1]) * nstripes; binary
+    // search for it (tile_off is non-decreasing from 0, so the item lies in
+    // a non-empty range: nt_e >= 1).
+    __shared__ int s_toff[257];  // E <= 256, checked on the host
+    for (int i = threadIdx.x; i <= a.E; i += kTiledThreads) s_toff[i] = a.tile_off[i];
+    __syncthreads();
+    int lo = 0, hi = a.E;  // s_toff[lo] * nstripes <= item < s_toff[hi] * nstripes
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_toff[mid] * nstripes <= item) lo = mid;
+      else hi = mid;
+    }
+    const int nt_e = s_toff[lo + 1] - s_toff[lo];
+    const int local = item - s_toff[lo] * nstripes;
+    stripe = local / nt_e;
+    tile = s_toff[lo] + (local - stripe * nt_e);
   }
-  const int nt_e = s_toff[lo + 1] - s_toff[lo];
-  const int local = item - s_toff[lo] * nstripes;
-  const int stripe = local / nt_e, tile = s_toff[lo] + (local - stripe * nt_e);
   const int4 ti = a.tiles[tile];  // {expert, first sorted row, tokens}
   const int e = ti.x, row_start = ti.y, ntok = ti.z;
   const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
