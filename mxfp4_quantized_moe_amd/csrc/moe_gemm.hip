@@ -716,6 +716,13 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
 // one 512-row, three-stage workgroup per CU).
 // =====================================================================
 
+// Estimated cost of streaming one weight stripe, in units of one 16-token
+// sub-tile's MFMA work (splits the tiled kernel's items over the XCDs).
+#ifndef MXMOE_TILE_COST
+#define MXMOE_TILE_COST 4
+#endif
+constexpr int kTileCost = MXMOE_TILE_COST;
+
 // Rows per workgroup (64 per wave) of the tiled-order kernel.
 #ifndef MXMOE_PREFILL_TILED_ROWS
 #define MXMOE_PREFILL_TILED_ROWS 256
@@ -783,31 +790,101 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   // workgroups that neighbour each other in launch order stream the same
   // weight stripe for the expert's several token tiles, so all but the first
   // read of it come from L2 (a tile-major order re-read every expert's
-  // weights once per token tile).  The grid is sized for the most tiles a
-  // routing can produce; the valid items are the first nvalid.  Hardware
-  // places workgroup b on XCD b % 8, so XCD x takes the x-th eighth of the
-  // valid items, in order: every XCD gets an even share and an expert's
-  // stripes mostly stay on one XCD, sharing its L2.
+  // weights once per token tile).  Hardware places workgroup b on XCD b % 8;
+  // XCD x takes a contiguous range of the items, so an expert's stripes
+  // mostly stay on one XCD, sharing its L2.  The ranges split the estimated
+  // work evenly rather than the item count, since the launch lasts as long
+  // as its busiest XCD: an item costs kTileCost (its weight stripe is
+  // streamed whatever its token count) plus its active 16-token sub-tiles.
+  // The grid holds G workgroups per XCD, at least an eighth of the items.
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3, G = gridDim.x >> 3;
   const int nstripes = (a.R + kTiledRows - 1) / kTiledRows;
   const int nvalid = a.tile_off[a.E] * nstripes;
-  const int per_xcd = (nvalid + 7) >> 3;
-  const int idx = blockIdx.x >> 3;
-  const int item = (blockIdx.x & 7) * per_xcd + idx;
-  if (idx >= per_xcd || item >= nvalid) return;  // uniform per workgroup
+  __shared__ int s_toff[257];  // E <= 256, checked on the host
+  __shared__ int s_woff[257];  // prefix of the experts' per-stripe costs
+  __shared__ int s_wtot[kTiledWaves];
+  static_assert(kTiledThreads >= 256, "one thread per expert");
   int tile, stripe;
   if (a.E == 1) {
     // One weight matrix (a dense linear): stripe fastest instead, so each XCD
     // reads an eighth of the activations, which outweigh the 4- or 8-bit
-    // weights, rather than all of them.
+    // weights, rather than all of them.  Its tiles are full but the last, so
+    // equal item counts are equal work.
+    const int per_xcd = (nvalid + 7) >> 3;
+    const int item = xcd * per_xcd + idx;
+    if (idx >= per_xcd || item >= nvalid) return;  // uniform per workgroup
     tile = item / nstripes;
     stripe = item - tile * nstripes;
   } else {
-    // Expert e owns items [tile_off[e], tile_off[e+1]) * nstripes; binary
-    // search for it (tile_off is non-decreasing from 0, so the item lies in
-    // a non-empty range: nt_e >= 1).
-    __shared__ int s_toff[257];  // E <= 256, checked on the host
-    for (int i = threadIdx.x; i <= a.E; i += kTiledThreads) s_toff[i] = a.tile_off[i];
+    // per-stripe cost of expert t: kTileCost per tile plus ceil(count / 16)
+    // sub-tiles (its tiles are full but the last); block-wide scan
+    const int t = threadIdx.x;
+    int c = 0;
+    if (t < a.E) {
+      const int cnt = a.offsets[t + 1] - a.offsets[t];
+      c = kTileCost * ((cnt + kPrefillTokens - 1) / kPrefillTokens) + ((cnt + 15) >> 4);
+    }
+    for (int i = t; i <= a.E; i += kTiledThreads) s_toff[i] = a.tile_off[i];
+    int x = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wtot[wave] = x;
     __syncthreads();
+    for (int w = 0; w < wave; ++w) x += s_wtot[w];
+    if (t < a.E) s_woff[t + 1] = x;
+    if (t == 0) s_woff[0] = 0;
+    __syncthreads();
+    // Lane xx <= 8 finds the first item of XCD xx: the first whose work
+    // prefix reaches xx/8 of the total.  The prefix of item (expert j,
+    // stripe s, tile q) is s_woff[j] * nstripes + s * (s_woff[j+1] - s_woff[j])
+    // + q * (kTileCost + 8): tiles before an expert's last are full.
+    int bnd = nvalid;
+    {
+      const int64_t W = int64_t(s_woff[a.E]) * nstripes;
+      const int64_t target = (W * lane + 7) / 8;
+      if (lane == 0) {
+        bnd = 0;
+      } else if (lane < 8 && target < W) {
+        int lo = 0, hi = a.E;  // s_woff[lo] * nstripes <= target < s_woff[hi] * nstripes
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (int64_t(s_woff[mid]) * nstripes <= target) lo = mid;
+          else hi = mid;
+        }
+        const int gc = s_woff[lo + 1] - s_woff[lo];  // > 0: the target lies in expert lo's range
+        const int nt = s_toff[lo + 1] - s_toff[lo];
+        const int64_t rem = target - int64_t(s_woff[lo]) * nstripes;
+        const int st = int(rem / gc);
+        const int r2 = int(rem - int64_t(st) * gc);
+        // past the last tile's start, the next stripe's (or expert's) first
+        // item follows: index st * nt + nt
+        const int q = min((r2 + kTileCost + 7) / (kTileCost + 8), nt);
+        bnd = s_toff[lo] * nstripes + st * nt + q;
+      }
+    }
+    // No XCD may own more than G items: clamp forward, then backward from
+    // nvalid.  Since nvalid <= 8 G, every range ends up within G.
+    int bx[9];
+#pragma unroll
+    for (int xx = 0; xx < 9; ++xx) bx[xx] = __builtin_amdgcn_readlane(bnd, xx);
+#pragma unroll
+    for (int xx = 0; xx < 8; ++xx) bx[xx + 1] = min(max(bx[xx + 1], bx[xx]), bx[xx] + G);
+    bx[8] = nvalid;
+#pragma unroll
+    for (int xx = 7; xx >= 1; --xx) bx[xx] = max(bx[xx], bx[xx + 1] - G);
+    int first = bx[0], last = bx[1];
+#pragma unroll
+    for (int xx = 1; xx < 8; ++xx)
+      if (xcd == xx) {
+        first = bx[xx];
+        last = bx[xx + 1];
+      }
+    const int item = first + idx;
+    if (item >= last) return;  // uniform per workgroup
+    // Expert e owns items [tile_off[e], tile_off[e+1]) * nstripes
     int lo = 0, hi = a.E;  // s_toff[lo] * nstripes <= item < s_toff[hi] * nstripes
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
