@@ -87,11 +87,13 @@ mxmoe_status_t check_layer(const mxmoe_layer_t* L) {
   return MXMOE_OK;
 }
 
-mxmoe_status_t check_opts(const mxmoe_layer_t* L, const mxmoe_fwd_opts_t* o, bool use_fp8) {
+// `forward`: the options of a forward call, whose FP8 fields and expert path
+// are checked too (the routing-only call ignores them).
+mxmoe_status_t check_opts(const mxmoe_layer_t* L, const mxmoe_fwd_opts_t* o, bool forward) {
   if (!o) return MXMOE_ERR_NULL;
   if (o->act_dtype != MXMOE_F32 && o->act_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
   if (o->act_dtype != L->param_dtype) return MXMOE_ERR_DTYPE;  // one dtype for x, router and biases
-  if (use_fp8) {
+  if (forward) {
     if (o->fp8_act != 0 && o->fp8_act != 1) return MXMOE_ERR_VALUE;
     if (o->fp8_act) {
       if (o->act_dtype != MXMOE_BF16) return MXMOE_ERR_DTYPE;
@@ -100,7 +102,7 @@ mxmoe_status_t check_opts(const mxmoe_layer_t* L, const mxmoe_fwd_opts_t* o, boo
       if (!std::isfinite(1.0f / o->x_scale) || !std::isfinite(1.0f / o->h_scale)) return MXMOE_ERR_VALUE;
     }
   }
-  if (use_fp8 && o->expert_path != MXMOE_PATH_ROUTED && o->expert_path != MXMOE_PATH_DENSE) return MXMOE_ERR_VALUE;
+  if (forward && o->expert_path != MXMOE_PATH_ROUTED && o->expert_path != MXMOE_PATH_DENSE) return MXMOE_ERR_VALUE;
   if (o->topk_idx_out && !aligned16(o->topk_idx_out)) return MXMOE_ERR_ALIGN;
   if (o->topk_w_out && !aligned16(o->topk_w_out)) return MXMOE_ERR_ALIGN;
   return MXMOE_OK;
