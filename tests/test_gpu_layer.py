@@ -225,3 +225,23 @@ def test_decode_prefixes_agree(dev):
     a = O.bf16_from_bits(W.torch_to_array(o64[:8]))
     b = O.bf16_from_bits(W.torch_to_array(o8))
     assert np.max(np.abs(a - b)) <= 1e-2 * np.max(np.abs(a))
+
+
+def test_skewed_routing_clamped_xcd_ranges(dev):
+    """A router bias of std 3 sends almost every token to a few experts and
+    leaves several with a handful: weighted by estimated work, one XCD's
+    range of gate_up items would exceed the grid's workgroups per XCD, so
+    the tiled kernel's clamp decides the split (checked on the oracle's
+    routing with the host-side model of the split)."""
+    from tests.test_xcd_split import TILE_COST, weighted_bounds
+
+    case = W.small_case(33, 32, 128, 1024, 2, 2000, router_bias_std=3.0)
+    L = case.layer
+    idx, _, _ = O.route(O.bf16_from_bits(case.x), O.bf16_from_bits(L.router_w), O.bf16_from_bits(L.router_b), L.top_k)
+    cnt = np.bincount(idx.reshape(-1), minlength=L.E).tolist()
+    bnd, G, _, _, _ = weighted_bounds(cnt, 2 * L.I, TILE_COST)
+    assert max(bnd[x + 1] - bnd[x] for x in range(8)) > G
+    note(f"{case.name} tiled, expert counts {sorted(cnt)[-3:]} .. {sorted(cnt)[:3]}")
+    res, _, _ = run_gpu(case, dev, layout="tiled")
+    check_perm(case, res["route"])
+    check_layer(case, res)

@@ -15,14 +15,16 @@ import pytest
 
 TOKENS = 128      # tokens per prefill tile
 ROWS = 256        # weight rows per workgroup
+TILE_COST = 4     # the kernel's fixed cost per item, in 16-token sub-tiles
 
 
 def cdiv(a, b):
     return -(-a // b)
 
 
-def split(cnt, R, c0):
-    """Per-XCD item ranges, the items' (tile, stripe) and per-XCD work."""
+def weighted_bounds(cnt, R, c0):
+    """The nine weighted range bounds before clamping, the grid's G per XCD,
+    the item count and the tile and cost prefixes."""
     E = len(cnt)
     ns = cdiv(R, ROWS)
     toff = np.concatenate([[0], np.cumsum([cdiv(c, TOKENS) for c in cnt])]).astype(np.int64)
@@ -32,24 +34,13 @@ def split(cnt, R, c0):
     cost = [c0 * cdiv(c, TOKENS) + cdiv(c, 16) for c in cnt]
     woff = np.concatenate([[0], np.cumsum(cost)]).astype(np.int64)
     W = int(woff[E]) * ns
-
-    def upper(arr, v):  # largest j in [0, E) with arr[j] * ns <= v (arr[0] = 0)
-        lo, hi = 0, E
-        while hi - lo > 1:
-            mid = (lo + hi) >> 1
-            if arr[mid] * ns <= v:
-                lo = mid
-            else:
-                hi = mid
-        return lo
-
     bnd = []
     for lane in range(9):
         target = (W * lane + 7) // 8
         if lane == 0:
             b = 0
         elif lane < 8 and target < W:
-            j = upper(woff, target)
+            j = upper(woff, target, E, ns)
             gc = int(woff[j + 1] - woff[j])
             nt = int(toff[j + 1] - toff[j])
             assert gc > 0 and nt > 0
@@ -60,6 +51,26 @@ def split(cnt, R, c0):
         else:
             b = nvalid
         bnd.append(b)
+    return bnd, G, nvalid, ns, toff
+
+
+def upper(arr, v, E, ns):
+    """Largest j in [0, E) with arr[j] * ns <= v (arr[0] = 0)."""
+    lo, hi = 0, E
+    while hi - lo > 1:
+        mid = (lo + hi) >> 1
+        if arr[mid] * ns <= v:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def split(cnt, R, c0):
+    """Per-XCD work of the clamped ranges, checking the partition."""
+    E = len(cnt)
+    bnd, G, nvalid, ns, toff = weighted_bounds(cnt, R, c0)
+    bnd = list(bnd)
     for x in range(8):
         bnd[x + 1] = min(max(bnd[x + 1], bnd[x]), bnd[x] + G)
     bnd[8] = nvalid
@@ -72,7 +83,7 @@ def split(cnt, R, c0):
         first, last = bnd[x], bnd[x + 1]
         assert 0 <= first <= last <= nvalid and last - first <= G
         for item in range(first, last):
-            j = upper(toff, item)
+            j = upper(toff, item, E, ns)
             nt = int(toff[j + 1] - toff[j])
             assert nt > 0
             local = item - int(toff[j]) * ns
@@ -109,9 +120,9 @@ def test_ranges_partition_the_items(seed):
 
 
 def test_single_token_and_empty_experts():
-    split([0, 1, 0, 0], 64, 4)
-    split([0] * 255 + [3], 5760, 4)
-    split([1] * 256, 5760, 4)
+    split([0, 1, 0, 0], 64, TILE_COST)
+    split([0] * 255 + [3], 5760, TILE_COST)
+    split([1] * 256, 5760, TILE_COST)
 
 
 def test_skewed_routing_balances_work():
@@ -120,5 +131,5 @@ def test_skewed_routing_balances_work():
     rng = np.random.default_rng(7)
     p = rng.dirichlet(np.full(128, 1.0))
     cnt = rng.multinomial(4096 * 4, p).tolist()
-    w = split(cnt, 5760, 4)
+    w = split(cnt, 5760, TILE_COST)
     assert w.max() / w.mean() < 1.01
