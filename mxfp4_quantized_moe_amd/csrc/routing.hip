@@ -506,21 +506,34 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) { 
 // slots.  For those, each wave takes a contiguous range of slots, counts its
 // matches with ballots, takes a prefix over the waves, and sweeps the range
 // again writing positions in slot order.
+// Batches up to this many slots keep their expert ids in LDS as bytes
+// (E <= 256) after the histogram pass reads them, so the two ranking passes
+// read LDS instead of global memory.
+constexpr int kPermLdsSlots = 1 << 16;
+
 __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(PermuteArgs a) {
   __shared__ int cnt[256];
   __shared__ int s_off, s_toff, s_act;
   __shared__ int wsum[kPermWaves];
+  __shared__ uint8_t sidx[kPermLdsSlots];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, N = a.n_slots, me = blockIdx.x;
+  const bool cached = N <= kPermLdsSlots;
 
   for (int e = tid; e < 256; e += kPermThreads) cnt[e] = 0;
   __syncthreads();
   for (int s = tid; s < N; s += kPermThreads) {
     int e = a.idx[s];
     e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    if (cached) sidx[s] = uint8_t(e);
     atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
+  auto key_at = [&](int s) -> int {
+    if (cached) return sidx[s];
+    const int e = a.idx[s];
+    return e < 0 ? 0 : (e >= E ? E - 1 : e);
+  };
 
   if (wave == 0) {
     // each lane scans 4 consecutive experts
@@ -575,11 +588,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
   int mine = 0;
   for (int b = s0; b < s1; b += 64) {
     const int s = b + lane;
-    int key = -1;
-    if (s < s1) {
-      key = a.idx[s];
-      key = key < 0 ? 0 : (key >= E ? E - 1 : key);
-    }
+    const int key = s < s1 ? key_at(s) : -1;
     mine += __popcll(__ballot(key == me));
   }
   if (lane == 0) wsum[wave] = mine;
@@ -589,11 +598,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int b = s0; b < s1; b += 64) {
     const int s = b + lane;
-    int key = -1;
-    if (s < s1) {
-      key = a.idx[s];
-      key = key < 0 ? 0 : (key >= E ? E - 1 : key);
-    }
+    const int key = s < s1 ? key_at(s) : -1;
     const uint64_t m = __ballot(key == me);
     if (key == me) {
       const int p = run + __popcll(m & lt_mask);
