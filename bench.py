@@ -565,7 +565,7 @@ def measured_traffic(workload: str, kernel: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_120b_t4096")
     ap.add_argument("--copies", type=int, default=None, help="weight copies cycled through (default: >= 1 GB apart)")
