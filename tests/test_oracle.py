@@ -280,6 +280,16 @@ def test_route_brute_force_random():
         assert np.allclose(w.sum(1), 1.0) and np.all(np.diff(w, axis=1) <= 0)
 
 
+def test_routing_margin_by_hand():
+    """The gap between the k-th and (k+1)-th largest logit, worked by hand;
+    zero at a tie that straddles the cut, inf when every expert is chosen."""
+    logits = np.array([[0.5, 3.0, -1.0, 2.0], [1.0, 1.0, 1.0, 0.0], [4.0, -2.0, 0.0, 4.0]])
+    assert O.routing_margin(logits, 1).tolist() == [1.0, 0.0, 0.0]
+    assert O.routing_margin(logits, 2).tolist() == [1.5, 0.0, 4.0]
+    assert O.routing_margin(logits, 3).tolist() == [1.5, 1.0, 2.0]
+    assert np.all(np.isinf(O.routing_margin(logits, 4)))
+
+
 def test_permute_invariants_and_brute_force():
     rng = np.random.default_rng(9)
     E, T, k = 7, 33, 3
