@@ -187,6 +187,8 @@ def _check(status: int) -> None:
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if t is None:
         return None
+    if not t.is_cuda:  # the kernels dereference every pointer on the GPU
+        raise ValueError("tensors passed to the library must be GPU tensors")
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
     return t.data_ptr()

@@ -306,3 +306,16 @@ def test_int8_validation(lib):
     assert need >= 8 * 2 * (64 * 2 + 64 * 2) + 8 * 64 + 8 * 2 * 64
     assert fwd(L, ws_bytes=need - 1) == WS
     assert lib.moe_int8_workspace_bytes(ctypes.byref(_int8_layer(I=40)), 8) == 0
+
+
+def test_binding_rejects_host_tensors(lib):
+    """The Python binding refuses CPU tensors before any library call: every
+    pointer the kernels receive must be device memory."""
+    import torch
+
+    blocks = torch.zeros((2, 1, 16), dtype=torch.uint8)
+    scales = torch.zeros((2, 1), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        mx.mxfp4_unpack(blocks, scales)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        mx.mxfp4_pack(torch.zeros((2, 32), dtype=torch.bfloat16))
