@@ -307,10 +307,10 @@ def bench_layer(args, dev):
         achieved = fl / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
         algo = f"{fl} flop per launch"
-    roof["kernel"] = "gemm_prefill_kernel<phase 0>" if not decode_shaped else "gemm_decode_kernel<phase 0>"
+    roof["kernel"] = gate_up_kernel_name(case, decode_shaped, args.layout == "tiled")
     roof["launches_timed"] = f"{len(gu_ms)} of the {args.steps} timed steps (every {EV_EVERY}th)"
     roof["algorithmic"] = algo
-    roof["traffic"] = measured_traffic(args.workload, roof["kernel"])
+    roof["traffic"] = measured_traffic(args.workload, roof["kernel"]) if not dense else None
     res = {
         "metric": METRIC,
         "value": T * args.steps / (t1 - t0),
@@ -548,14 +548,27 @@ def bench_int8(args, dev):
                          "algorithmic": f"{ops} int8 ops per forward (gate_up + down)", "traffic": None}}
 
 
+def gate_up_kernel_name(case, decode_shaped: bool, tiled: bool) -> str:
+    """The gate_up kernel the library launches for this case, as rocprofv3
+    names it (template arguments: activation code, phase[, tiled])."""
+    act = 2 if case.fp8 else (1 if case.act_dtype == "bf16" else 0)
+    if decode_shaped:
+        if tiled and act != 0:
+            return f"mxmoe::gemm_decode_tiled_kernel<{act}, 0>"
+        return f"mxmoe::gemm_decode_kernel<{act}, 0, {'true' if tiled else 'false'}>"
+    if tiled:
+        return f"mxmoe::gemm_prefill_tiled_kernel<{act}, 0>"
+    return f"mxmoe::gemm_prefill_kernel<{act}, 0, false>"
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
+    it was taken on this kernel and the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         ent = t.get(workload)
-        if ent and ent.get("kernel_source_hash") == kernel_source_hash():
+        if ent and ent.get("kernel") == kernel and ent.get("kernel_source_hash") == kernel_source_hash():
             return ent["bytes_per_launch"]
     except (OSError, ValueError):
         pass
