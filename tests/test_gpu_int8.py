@@ -120,3 +120,14 @@ def test_int8_20b_full_size(dev):
     note(case.name)
     res = _run(case, dev)
     _check(case, res, sample=np.linspace(0, case.T - 1, 12).astype(int))
+
+
+def test_int8_zero_token_rows(dev):
+    """All-zero token rows quantise to scale 0 and codes 0 (no 0/0): their
+    logits are the router bias alone and their gate_up output is the bias."""
+    case = W.int8_case(65, 6, 128, 96, 2, 20)
+    case.x[[0, 7, 19]] = 0
+    note(case.name + " with zero rows 0, 7, 19")
+    res = _run(case, dev)
+    assert np.all(np.isfinite(O.bf16_from_bits(res[0])))
+    _check(case, res)
