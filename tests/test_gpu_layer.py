@@ -245,3 +245,15 @@ def test_skewed_routing_clamped_xcd_ranges(dev):
     res, _, _ = run_gpu(case, dev, layout="tiled")
     check_perm(case, res["route"])
     check_layer(case, res)
+
+
+def test_fp8_saturating_activations(dev):
+    """FP8 mode with x about 50x beyond the calibrated range: most codes of x
+    saturate at +-448 on both sides (decided in fp32 from the same scale)."""
+    case = W.small_case(34, 4, 96, 160, 2, 400, act_dtype="bf16", fp8=True)
+    s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+    case.x = O.bf16_bits(O.round_bf16(O.bf16_from_bits(case.x) * 50.0))
+    assert np.mean(np.abs(O.bf16_from_bits(case.x)) / s_x > 448) > 0.5
+    note(f"{case.name} fp8 saturating tiled")
+    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False, layout="tiled")
+    check_layer(case, res, x_scale=s_x, h_scale=s_h)
