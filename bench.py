@@ -133,7 +133,8 @@ def expert_gemm_bytes(case, phase: int, n_active: int, dense: bool = False) -> i
         w = 2 * I * (H // 32) * 17 + 2 * I * pb
         return n_active * w + T * H * ab + T * k * I * ab
     w = H * (I // 32) * 17 + H * pb
-    return n_active * w + T * k * I * ab + T * k * H * 4
+    yb = 2 if case.act_dtype == "bf16" else 4  # Y: bf16 with bf16 activations, else fp32
+    return n_active * w + T * k * I * ab + T * k * H * yb
 
 
 def expert_gemm_flops(case, phase: int, dense: bool = False) -> int:
