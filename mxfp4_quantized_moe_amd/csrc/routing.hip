@@ -790,11 +790,72 @@ __global__ __launch_bounds__(256) void quant_rows_int8_kernel(const uint4* __res
   }
 }
 
+// Rows of at most 64 * 8 * NL values: one wave per row (4 rows per
+// workgroup) keeps the row in registers, NL 16-byte pieces per lane, so it
+// is read once and the maximum needs no workgroup barrier.  Same arithmetic
+// as above, so the same codes.
+template <int NL>
+__global__ __launch_bounds__(256) void quant_rows_int8_wave_kernel(const uint4* __restrict__ x, int64_t rows, int K8,
+                                                                   int8_t* q, float* scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // wave-uniform
+  const uint4* xr = x + row * K8;
+  uint4 v[NL];
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int i = lane + 64 * j;
+    v[j] = i < K8 ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(w[t] << 16)));
+      m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(w[t] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  const float amax = m;
+  const float s = amax / 127.0f;
+  if (lane == 0) scale[row] = s;
+  uint2* qr = reinterpret_cast<uint2*>(q + row * int64_t(K8) * 8);
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int i = lane + 64 * j;
+    if (i < K8) {
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float f = __uint_as_float((t & 1) ? (w[t >> 1] & 0xFFFF0000u) : (w[t >> 1] << 16));
+        float c = amax > 0.f ? __builtin_rintf(f / s) : 0.f;
+        c = __builtin_fminf(__builtin_fmaxf(c, -127.f), 127.f);
+        packed[t >> 2] |= (uint32_t(int(c)) & 0xFFu) << (8 * (t & 3));
+      }
+      qr[i] = make_uint2(packed[0], packed[1]);
+    }
+  }
+}
+
 hipError_t launch_quant_rows_int8(const uint16_t* x, int64_t rows, int K, int8_t* q, float* scale,
                                   hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  quant_rows_int8_kernel<<<dim3(unsigned(rows)), dim3(256), 0, stream>>>(reinterpret_cast<const uint4*>(x), K / 8, q,
-                                                                        scale);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int K8 = K / 8;
+  const int nl = (K8 + 63) / 64;  // 16-byte pieces per lane
+  const dim3 g(unsigned((rows + 3) / 4)), b(256);
+  switch (nl) {
+    case 1: quant_rows_int8_wave_kernel<1><<<g, b, 0, stream>>>(xv, rows, K8, q, scale); break;
+    case 2: quant_rows_int8_wave_kernel<2><<<g, b, 0, stream>>>(xv, rows, K8, q, scale); break;
+    case 3: quant_rows_int8_wave_kernel<3><<<g, b, 0, stream>>>(xv, rows, K8, q, scale); break;
+    case 4: quant_rows_int8_wave_kernel<4><<<g, b, 0, stream>>>(xv, rows, K8, q, scale); break;
+    case 5: quant_rows_int8_wave_kernel<5><<<g, b, 0, stream>>>(xv, rows, K8, q, scale); break;
+    case 6: quant_rows_int8_wave_kernel<6><<<g, b, 0, stream>>>(xv, rows, K8, q, scale); break;
+    case 7: quant_rows_int8_wave_kernel<7><<<g, b, 0, stream>>>(xv, rows, K8, q, scale); break;
+    case 8: quant_rows_int8_wave_kernel<8><<<g, b, 0, stream>>>(xv, rows, K8, q, scale); break;
+    default: quant_rows_int8_kernel<<<dim3(unsigned(rows)), dim3(256), 0, stream>>>(xv, K8, q, scale); break;
+  }
   return hipGetLastError();
 }
 
