@@ -51,6 +51,24 @@ def as_f64(a, act):
     return O.bf16_from_bits(a) if act == "bf16" else a.astype(np.float64)
 
 
+def boundary_tokens(case, route):
+    """Tokens at the tile boundaries of the busiest expert (its first row,
+    rows 127 and 128 of the sorted order: the last of its first 128-token
+    tile and the first of the next, and its last row) and the first and last
+    rows of the least busy expert with tokens."""
+    idx, w, counts, offsets, sorted_slots, pos = route
+    k = case.layer.top_k
+    busy = [e for e in range(case.layer.E) if counts[e] > 0]
+    emax = max(busy, key=lambda e: counts[e])
+    emin = min(busy, key=lambda e: counts[e])
+    picks = []
+    for e, rows in ((emax, (0, 127, 128, counts[emax] - 1)), (emin, (0, counts[emin] - 1))):
+        for r in rows:
+            if 0 <= r < counts[e]:
+                picks.append(int(sorted_slots[offsets[e] + r]) // k)
+    return picks
+
+
 def check_perm(case, route):
     idx, w, counts, offsets, sorted_slots, pos = route
     c, o, s, p = O.permute(idx, case.layer.E)
@@ -101,7 +119,8 @@ def test_decode_20b(dev, T, layout):
 @pytest.mark.parametrize("layout", ["rows", "tiled"])
 def test_prefill_120b_full_size(dev, layout):
     """T=4096 at the 120b shape: routing and grouping for every token, the
-    layer output on 12 tokens spread over the batch (the oracle computes
+    layer output on 12 tokens spread over the batch plus the tokens at the
+    busiest and least busy experts' tile boundaries (the oracle computes
     them one by one; tokens are independent)."""
     case = W.prefill_120b()
     note(f"{case.name} {layout}")
@@ -109,19 +128,22 @@ def test_prefill_120b_full_size(dev, layout):
     check_perm(case, res["route"])
     counts = res["route"][2]
     assert counts.max() > 3 * counts.mean()  # the router bias skews expert load
-    sample = np.linspace(0, case.T - 1, 12).astype(int)
+    spread = np.linspace(0, case.T - 1, 12).astype(int)
+    sample = np.unique(np.concatenate([spread, boundary_tokens(case, res["route"])]))
     check_layer(case, res, sample=sample)
 
 
 @pytest.mark.parametrize("layout", ["rows", "tiled"])
 def test_fp8_20b_full_size(dev, layout):
     """W-MXFP4 A-FP8 at T=2048: static scales from the 256-token calibration
-    batch (the oracle's values, fed to both sides), output on 12 tokens."""
+    batch (the oracle's values, fed to both sides), output on 12 tokens
+    spread over the batch plus the tile-boundary tokens."""
     case = W.fp8_20b()
     s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
     note(f"{case.name} {layout} s_x={s_x} s_h={s_h}")
-    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False, layout=layout)
-    sample = np.linspace(0, case.T - 1, 12).astype(int)
+    res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, layout=layout)
+    spread = np.linspace(0, case.T - 1, 12).astype(int)
+    sample = np.unique(np.concatenate([spread, boundary_tokens(case, res["route"])]))
     check_layer(case, res, sample=sample, x_scale=s_x, h_scale=s_h)
 
 
