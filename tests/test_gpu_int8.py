@@ -115,11 +115,16 @@ def test_int8_20b_decode_sizes(dev, T):
 
 def test_int8_20b_full_size(dev):
     """T=2048 at the 20b shape: routing for every token, the output on 12
-    tokens spread over the batch."""
+    tokens spread over the batch plus the tokens at the busiest and least
+    busy experts' tile boundaries (grouping of the GPU's routing)."""
+    from tests.test_gpu_layer import boundary_tokens
+
     case = W.int8_20b(2048)
     note(case.name)
     res = _run(case, dev)
-    _check(case, res, sample=np.linspace(0, case.T - 1, 12).astype(int))
+    route = (res[1], res[2], *O.permute(res[1].astype(np.int64), case.layer.E))
+    spread = np.linspace(0, case.T - 1, 12).astype(int)
+    _check(case, res, sample=np.unique(np.concatenate([spread, boundary_tokens(case, route)])))
 
 
 def test_int8_zero_token_rows(dev):
