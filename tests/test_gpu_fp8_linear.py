@@ -75,7 +75,8 @@ def test_fp8_linear_full_size(dev):
     case = W.fp8_linear_case(55, 4096, 2880, 5760)
     note(case.name)
     got = _run(case, dev)
-    rows = np.linspace(0, case.x.shape[0] - 1, 16).astype(int)
+    # 16 spread rows plus both sides of the first and last 128-row tile boundaries
+    rows = np.unique(np.concatenate([np.linspace(0, case.x.shape[0] - 1, 16).astype(int), [127, 128, 3967, 3968]]))
     ref = O.fp8_linear(case.x[rows], case.w_codes, case.w_scale, case.x_scale, case.bias)
     err = max_rel_err(got[rows], ref)
     note(f"{case.name}: max|d|/max|ref| = {err:.3e} on 16 rows (bar {TOL})")
