@@ -960,7 +960,8 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     uint4 aq2[W8 ? SX : 1][RT];  // FP8 weights: the second 16 bytes of a lane's piece
     uint32_t sw[SX];    // scale dword per stage
 
-    auto issue = [&](int c, auto stc) __attribute__((always_inline)) {
+    // weights and scales of chunk c into register stage u
+    auto issue_w = [&](int c, auto stc) __attribute__((always_inline)) {
       constexpr int u = decltype(stc)::value;
       const bool cok = c < nc && wok;
       if constexpr (W8) {
@@ -977,6 +978,9 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
           aq[u][rt] = buf_load_b128(wb.blk, cok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
         sw[u] = buf_load_b32(wb.sc, cok ? uint32_t(((t0 >> 2) * nc + c) * 256 + lane * 4) : kOOB);
       }
+    };
+    // tokens of chunk c into LDS stage u
+    auto issue_b = [&](int c, auto stc) __attribute__((always_inline)) {
       uint8_t* stb = stage(stc);
 #pragma unroll
       for (int jj = 0; jj < BL; ++jj) {
@@ -991,8 +995,12 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
 #pragma unroll
       for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](auto stc) __attribute__((always_inline)) {
+    // compute stage u; mid() (the next chunk's token DMA) runs once, halfway
+    // through the MFMA steps, so the wave's loads do not all leave in one
+    // burst after the barrier (measured 1-3% faster on the full tiles)
+    auto compute = [&](auto stc, auto mid) __attribute__((always_inline)) {
       constexpr int u = decltype(stc)::value;
+      if (!busy) mid();
       if (busy) {
         const uint8_t* sb = stage(stc);
         uint32_t ascb[RT];
@@ -1001,6 +1009,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
         if constexpr (ACT == ACT_BF16) {
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
+            if (st == 2) mid();
             bf16x8_t b[NA];
 #pragma unroll
             for (int nt = 0; nt < NA; ++nt)
@@ -1038,6 +1047,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
           i32x8_t bcur = load_b(0);
 #pragma unroll
           for (int nt = 0; nt < NA; ++nt) {
+            if (nt == NA / 2) mid();
             i32x8_t bnext = bcur;
             if (nt + 1 < NA) bnext = load_b(nt + 1);
             order_point();
@@ -1065,6 +1075,10 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     };
 
     // prologue: chunks 0 .. SX-2 in flight, issued in chunk order
+    auto issue = [&](int c, auto stc) __attribute__((always_inline)) {
+      issue_w(c, stc);
+      issue_b(c, stc);
+    };
     order_point();
     issue(0, IC<0>{});
     order_point();
@@ -1073,15 +1087,20 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
 
     // iteration c: wait for chunk c, barrier (its tokens have landed for
     // every wave, and chunk c-1's stage is free), refill that stage with
-    // chunk c+S-1, compute chunk c.  Every iteration issues the same loads
-    // (chunks past the end read zeros), so the wait count is fixed.
+    // chunk c+S-1 (weights now, tokens from inside compute), compute chunk
+    // c.  Every iteration issues the same loads (chunks past the end read
+    // zeros), weights before tokens, so the wait count is fixed.
     auto iteration = [&](int c, auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;  // c % SX
       wait_vmcnt<(SX - 2) * LD>();
       barrier();
-      issue(c + SX - 1, IC<(u + SX - 1) % SX>{});
+      issue_w(c + SX - 1, IC<(u + SX - 1) % SX>{});
       order_point();
-      compute(IC<u>{});
+      compute(IC<u>{}, [&]() __attribute__((always_inline)) {
+        order_point();
+        issue_b(c + SX - 1, IC<(u + SX - 1) % SX>{});
+        order_point();
+      });
     };
     int c0 = 0;
     for (; c0 + SX <= nc; c0 += SX) {
