@@ -522,11 +522,25 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
 
   for (int e = tid; e < 256; e += kPermThreads) cnt[e] = 0;
   __syncthreads();
-  for (int s = tid; s < N; s += kPermThreads) {
-    int e = a.idx[s];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    if (cached) sidx[s] = uint8_t(e);
-    atomicAdd(&cnt[e], 1);
+  // histogram: a thread's loads for kB slots leave together, so the pass
+  // waits on one L2 round trip per kB slots rather than per slot
+  constexpr int kB = 8;
+  for (int base = tid; base < N; base += kB * kPermThreads) {
+    int ev[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int s = base + j * kPermThreads;
+      ev[j] = s < N ? a.idx[s] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int s = base + j * kPermThreads;
+      if (s < N) {
+        const int e = ev[j] < 0 ? 0 : (ev[j] >= E ? E - 1 : ev[j]);
+        if (cached) sidx[s] = uint8_t(e);
+        atomicAdd(&cnt[e], 1);
+      }
+    }
   }
   __syncthreads();
   auto key_at = [&](int s) -> int {
