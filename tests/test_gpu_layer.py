@@ -182,6 +182,7 @@ def test_fp8_calibration_scales(dev):
     (25, 8, 64, 32, 2, 3000, "bf16"),    # grouping: > 2048 slots (one workgroup per expert)
     (26, 256, 64, 32, 8, 600, "bf16"),   # grouping: > 2048 slots over 256 experts
     (37, 8, 64, 32, 2, 40000, "bf16"),   # grouping: > 65536 slots (expert ids re-read from global memory)
+    (38, 8, 32, 32, 4, 270000, "bf16"),  # grouping: > 2^20 slots (back to the single-workgroup kernel)
     (27, 48, 160, 64, 4, 40, "f32"),     # router: fp32 with 32 < E <= 64 and few tokens (8 waves)
     (35, 4, 8192, 1024, 2, 300, "bf16"), # long K: 64 gate_up chunks through the prefill kernels
     (36, 4, 4096, 2048, 2, 5, "bf16"),   # long K through the decode kernels (32 and 16 chunks)
