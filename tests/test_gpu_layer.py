@@ -147,6 +147,36 @@ def test_fp8_20b_full_size(dev, layout):
     check_layer(case, res, sample=sample, x_scale=s_x, h_scale=s_h)
 
 
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_fp8_by_hand(dev, layout):
+    """The FP8 mode on the hand-derived layer of tests/hand_cases.py: the
+    output must be exactly [0.875, 28, 0, ...] (router on the unquantised x,
+    x and h quantised with their static scales, h saturating)."""
+    from tests import hand_cases as HC
+
+    case = HC.fp8_by_hand()
+    note(f"{case.name} {layout}")
+    res, _, _ = run_gpu(case, dev, x_scale=HC.FP8_X_SCALE, h_scale=HC.FP8_H_SCALE, want_route=False, layout=layout)
+    assert res["idx"][0, 0] == 0 and res["w"][0, 0] == 1.0
+    assert np.array_equal(O.bf16_from_bits(res["out"][0]), HC.FP8_EXPECTED)
+
+
+def test_fp8_calibration_by_hand(dev):
+    """GPU calibration on the hand-derived one-token batch: s_x has the bits
+    of fp32(3/448) and s_h = 28/448 exactly."""
+    import torch
+    import mxfp4_quantized_moe_amd as mx
+    from tests import hand_cases as HC
+
+    case = HC.calib_by_hand()
+    note(case.name)
+    wts = W.layer_to_torch(case.layer, dev)
+    sc = mx.moe_mxfp4_calibrate_fp8(wts, W.array_to_torch(case.x_calib, dev))
+    torch.cuda.synchronize()
+    g = W.torch_to_array(sc).astype(np.float32)
+    assert g[0].view(np.uint32) == HC.CALIB_SX_BITS and g[1] == HC.CALIB_SH
+
+
 def test_fp8_calibration_scales(dev):
     import torch
     import mxfp4_quantized_moe_amd as mx

@@ -475,6 +475,39 @@ def test_fp8_quant_dequant_and_scale():
     assert np.array_equal(d, q * np.float64(np.float32(s)))
 
 
+def test_fp8_layer_by_hand():
+    """The FP8 activation mode on a layer whose output was derived by hand
+    (tests/hand_cases.py gives the derivation): router on the unquantised x,
+    x quantised with x_scale before gate_up, h requantised with h_scale
+    (saturating) before down.  gpt-oss-120b-mxfp4-fp8attn-v2 page, FP8 script
+    (float8_e4m3fn, symmetric, per-tensor, static); amd/gpt-oss-20b-MoE-Quant-
+    W-MXFP4-A-FP8-KV-FP8 page, "Quantization schemes" (router not quantised,
+    activations of the MoE linears FP8 per-tensor)."""
+    from tests import hand_cases as HC
+
+    case = HC.fp8_by_hand()
+    out, parts = O.moe_forward(case.layer, case.x, "bf16", fp8=True, x_scale=HC.FP8_X_SCALE,
+                               h_scale=HC.FP8_H_SCALE, return_parts=True)
+    assert parts["idx"][0, 0] == 0  # routed on x, not on its FP8 value
+    assert np.array_equal(out[0], HC.FP8_EXPECTED)
+    # the bf16 path of the same layer: h_0 = 1.0625 * sigmoid(1.808375) =
+    # 0.91286 -> bf16 0.9140625 (spacing 2^-8), h_1 = 55.99963 -> bf16 56
+    plain = O.moe_forward(case.layer, case.x, "bf16")[0]
+    assert plain[0] == 0.9140625 and plain[1] == 56.0 and not np.any(plain[2:])
+
+
+def test_fp8_calibration_by_hand():
+    """Static scales from a one-token calibration batch, derived by hand
+    (tests/hand_cases.py): s_x = amax(x)/448 in fp32 and s_h = amax of the
+    bf16 h of the routed expert / 448."""
+    from tests import hand_cases as HC
+
+    case = HC.calib_by_hand()
+    s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+    assert np.float32(s_x).view(np.uint32) == HC.CALIB_SX_BITS
+    assert s_h == HC.CALIB_SH
+
+
 def test_fp8_mode_error_is_fp8_sized():
     case = W.small_case(4, 4, 64, 64, 2, 16, act_dtype="bf16", fp8=True)
     s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
