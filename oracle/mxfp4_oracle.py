@@ -488,6 +488,18 @@ def int8_quant_rows(v: np.ndarray):
     return q.astype(np.int64), s.astype(np.float64)
 
 
+def _exact_int_matmul(a: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """a (n, K) int codes times w (R, K) int8 codes transposed, exactly.
+
+    Every product and every partial sum is an integer of magnitude at most
+    127 * 127 * K < 2^53 (K < 2^39), so a float64 matrix product holds them
+    all exactly whatever its summation order: the result equals the integer
+    product (a float64 product rather than an int64 one only for speed)."""
+    K = a.shape[1]
+    assert K < 2**39 and np.abs(a).max(initial=0) <= 127
+    return a.astype(np.float64) @ w.astype(np.float64).T
+
+
 def moe_forward_int8(layer8, x: np.ndarray, route_override=None, return_parts: bool = False):
     """The INT8 W8A8 MoE layer (gpt-oss-20b-BF16-w8a8-llmcompressor page,
     "Quantization": weights int8 per output channel with static scales,
@@ -520,12 +532,12 @@ def moe_forward_int8(layer8, x: np.ndarray, route_override=None, return_parts: b
         if sl.size == 0:
             continue
         tok = sl // k
-        acc = xq[tok] @ L.gate_up_codes[e].astype(np.int64).T  # exact integers
+        acc = _exact_int_matmul(xq[tok], L.gate_up_codes[e])
         G = acc * sx[tok][:, None] * L.gate_up_scale[e].astype(np.float64) + b_gu[e]
         h = round_bf16(swiglu_clamped(G[:, 0::2], G[:, 1::2]))
         hb[sl] = h
         hq, sh = int8_quant_rows(h)
-        acc2 = hq @ L.down_codes[e].astype(np.int64).T
+        acc2 = _exact_int_matmul(hq, L.down_codes[e])
         Y[sl] = acc2 * sh[:, None] * L.down_scale[e].astype(np.float64) + b_d[e]
     out = np.zeros((T, H))
     for j in range(k):
