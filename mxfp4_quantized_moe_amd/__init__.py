@@ -6,6 +6,7 @@ include/mxmoe.h); this package only loads it and marshals torch tensors.
 from .binding import (  # noqa: F401
     EXPORTED,
     FP8Linear,
+    ForwardPlan,
     LAYOUT_ROWS,
     LAYOUT_TILED,
     LIB_PATH,

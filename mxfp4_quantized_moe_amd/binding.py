@@ -206,19 +206,52 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise ValueError(f"unsupported dtype {dt}")
 
 
+# Shape checks done here, before any pointer reaches the library: the C ABI
+# takes sizes, not shapes, so a tensor smaller than the sizes say would be
+# read or written past its end by the kernels.
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape=None, dtype=None, min_numel: Optional[int] = None) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if min_numel is not None and (t.dim() != 1 or t.numel() < min_numel):
+        raise ValueError(f"{name} must be a flat tensor of at least {min_numel} elements, got {tuple(t.shape)}")
+
+
+def _expect_same_device(*ts: Optional[torch.Tensor]) -> None:
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors passed to one call must share a device, got {sorted(map(str, devs))}")
+
+
+def _expect_out(out: torch.Tensor, shape, dtype, name: str = "out") -> None:
+    _expect(out, name, shape, dtype)
+
+
 # ---------------------------------------------------------------- codec
 
 
 def mxfp4_unpack(blocks: torch.Tensor, scales: torch.Tensor, dtype: torch.dtype = torch.bfloat16,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """(..., nb, 16) uint8 blocks + (..., nb) uint8 scales -> (..., nb*32)."""
+    if blocks.dim() < 2 or blocks.shape[-1] != 16:
+        raise ValueError(f"blocks must be (..., nb, 16), got {tuple(blocks.shape)}")
     nb = blocks.shape[-2]
     lead = tuple(blocks.shape[:-2])
+    _expect(blocks, "blocks", dtype=torch.uint8)
+    _expect(scales, "scales", lead + (nb,), torch.uint8)
     rows = 1
     for d in lead:
         rows *= d
     if out is None:
         out = torch.empty(lead + (nb * 32,), dtype=dtype, device=blocks.device)
+    _expect_out(out, lead + (nb * 32,), out.dtype)
+    _dtype_code(out.dtype)
+    _expect_same_device(blocks, scales, out)
     _check(load_library().mxfp4_unpack(_ptr(blocks), _ptr(scales), rows, nb * 32, _ptr(out),
                                        _dtype_code(out.dtype), _stream(blocks.device)))
     return out
@@ -226,6 +259,9 @@ def mxfp4_unpack(blocks: torch.Tensor, scales: torch.Tensor, dtype: torch.dtype 
 
 def mxfp4_pack(w: torch.Tensor):
     """(..., K) bf16/fp32 -> (blocks (..., K/32, 16) uint8, scales (..., K/32) uint8)."""
+    if w.dim() < 1:
+        raise ValueError("w must have a contracting dimension")
+    _dtype_code(w.dtype)
     K = w.shape[-1]
     lead = tuple(w.shape[:-1])
     rows = 1
@@ -248,7 +284,12 @@ def mxfp4_tiled_bytes(mats: int, rows: int, k: int):
 def mxfp4_tile(blocks: torch.Tensor, scales: torch.Tensor):
     """(mats, rows, nb, 16) blocks + (mats, rows, nb) scales in row order ->
     flat uint8 (tiled_blocks, tiled_scales) in the tiled order of mxmoe.h."""
+    if blocks.dim() != 4 or blocks.shape[-1] != 16:
+        raise ValueError(f"blocks must be (mats, rows, nb, 16), got {tuple(blocks.shape)}")
     mats, rows, nb = (int(d) for d in blocks.shape[:3])
+    _expect(blocks, "blocks", dtype=torch.uint8)
+    _expect(scales, "scales", (mats, rows, nb), torch.uint8)
+    _expect_same_device(blocks, scales)
     bb, sb = mxfp4_tiled_bytes(mats, rows, nb * 32)
     tb = torch.empty(max(bb, 16), dtype=torch.uint8, device=blocks.device)[:bb]
     ts = torch.empty(max(sb, 16), dtype=torch.uint8, device=blocks.device)[:sb]
@@ -287,6 +328,21 @@ class MXFP4Linear:
                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
         return mxfp4_linear(x, self, out=out, workspace=workspace)
 
+    def validate(self, act_dtype: torch.dtype) -> None:
+        """Tensor shapes and dtypes against N, K (ValueError on a mismatch)."""
+        if self.layout == LAYOUT_TILED:
+            bb, sb = mxfp4_tiled_bytes(1, self.N, self.K)
+            _expect(self.blocks, "blocks", dtype=torch.uint8, min_numel=bb)
+            _expect(self.scales, "scales", dtype=torch.uint8, min_numel=sb)
+        elif self.layout == LAYOUT_ROWS:
+            _expect(self.blocks, "blocks", (self.N, self.K // 32, 16), torch.uint8)
+            _expect(self.scales, "scales", (self.N, self.K // 32), torch.uint8)
+        else:
+            raise ValueError(f"unknown layout {self.layout}")
+        if self.bias is not None:
+            _expect(self.bias, "bias", (self.N,), act_dtype)
+        _expect_same_device(self.blocks, self.scales, self.bias)
+
 
 def mxfp4_linear_workspace_bytes(T: int, N: int, act_dtype: torch.dtype) -> int:
     return int(load_library().mxfp4_linear_workspace_bytes(T, N, _dtype_code(act_dtype)))
@@ -295,9 +351,15 @@ def mxfp4_linear_workspace_bytes(T: int, N: int, act_dtype: torch.dtype) -> int:
 def mxfp4_linear(x: torch.Tensor, layer: MXFP4Linear, out: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = x W^T + b for x (T, K) in bf16 or fp32; returns (T, N)."""
+    if x.dim() != 2 or int(x.shape[1]) != layer.K:
+        raise ValueError(f"x must be (T, {layer.K}), got {tuple(x.shape)}")
+    _dtype_code(x.dtype)
+    layer.validate(x.dtype)
     T = int(x.shape[0])
     if out is None:
         out = torch.empty((T, layer.N), dtype=x.dtype, device=x.device)
+    _expect_out(out, (T, layer.N), x.dtype)
+    _expect_same_device(x, layer.blocks, out, workspace)
     if workspace is None:
         n = mxfp4_linear_workspace_bytes(T, layer.N, x.dtype)
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
@@ -318,6 +380,9 @@ def fp8_tiled_bytes(N: int, K: int) -> int:
 
 def fp8_tile(w: torch.Tensor) -> torch.Tensor:
     """(N, K) uint8 e4m3 codes (row-major, device) -> the tiled FP8 order."""
+    if w.dim() != 2:
+        raise ValueError(f"w must be (N, K), got {tuple(w.shape)}")
+    _expect(w, "w", dtype=torch.uint8)
     N, K = int(w.shape[0]), int(w.shape[1])
     out = torch.empty(fp8_tiled_bytes(N, K), dtype=torch.uint8, device=w.device)
     _check(load_library().fp8_tile(_ptr(w.contiguous()), N, K, _ptr(out), _stream(w.device)))
@@ -346,6 +411,13 @@ class FP8Linear:
                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
         return fp8_linear(x, self, out=out, workspace=workspace)
 
+    def validate(self) -> None:
+        """Tensor shapes and dtypes against N, K (ValueError on a mismatch)."""
+        _expect(self.w_tiled, "w_tiled", dtype=torch.uint8, min_numel=fp8_tiled_bytes(self.N, self.K))
+        if self.bias is not None:
+            _expect(self.bias, "bias", (self.N,), torch.bfloat16)
+        _expect_same_device(self.w_tiled, self.bias)
+
 
 def fp8_linear_workspace_bytes(T: int, K: int, N: int) -> int:
     return int(load_library().fp8_linear_workspace_bytes(T, K, N))
@@ -354,9 +426,15 @@ def fp8_linear_workspace_bytes(T: int, K: int, N: int) -> int:
 def fp8_linear(x: torch.Tensor, layer: FP8Linear, out: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """x (T, K) bf16 -> (T, N) bf16."""
+    _expect(x, "x", dtype=torch.bfloat16)
+    if x.dim() != 2 or int(x.shape[1]) != layer.K:
+        raise ValueError(f"x must be (T, {layer.K}), got {tuple(x.shape)}")
+    layer.validate()
     T = int(x.shape[0])
     if out is None:
         out = torch.empty((T, layer.N), dtype=torch.bfloat16, device=x.device)
+    _expect_out(out, (T, layer.N), torch.bfloat16)
+    _expect_same_device(x, layer.w_tiled, out, workspace)
     if workspace is None:
         n = fp8_linear_workspace_bytes(T, layer.K, layer.N)
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
@@ -371,6 +449,9 @@ def fp8_linear(x: torch.Tensor, layer: FP8Linear, out: Optional[torch.Tensor] = 
 
 def int8_tile(w: torch.Tensor) -> torch.Tensor:
     """(mats, rows, k) int8 codes (device) -> the tiled 8-bit order (flat)."""
+    if w.dim() != 3:
+        raise ValueError(f"w must be (mats, rows, k), got {tuple(w.shape)}")
+    _expect(w, "w", dtype=torch.int8)
     mats, rows, k = (int(v) for v in w.shape)
     n = ctypes.c_int64(0)
     _check(load_library().int8_tiled_bytes(mats, rows, k, ctypes.byref(n)))
@@ -412,6 +493,27 @@ class MoEInt8Weights:
     def I(self) -> int:  # noqa: E743
         return int(self.gate_up_bias.shape[1]) // 2
 
+    def validate(self) -> None:
+        """Every tensor's shape and dtype against E, H, I (ValueError on a
+        mismatch): the library sizes its reads from those alone."""
+        if self.router_w.dim() != 2 or self.gate_up_bias.dim() != 2 or self.gate_up_bias.shape[1] % 2:
+            raise ValueError("router_w must be (E, H) and gate_up_bias (E, 2I)")
+        E, H, I = self.E, self.H, self.I
+        bf = torch.bfloat16
+        n = ctypes.c_int64(0)
+        _check(load_library().int8_tiled_bytes(E, 2 * I, H, ctypes.byref(n)))
+        _expect(self.gate_up_w, "gate_up_w", dtype=torch.uint8, min_numel=int(n.value))
+        _check(load_library().int8_tiled_bytes(E, H, I, ctypes.byref(n)))
+        _expect(self.down_w, "down_w", dtype=torch.uint8, min_numel=int(n.value))
+        _expect(self.gate_up_scale, "gate_up_scale", (E, 2 * I), torch.float32)
+        _expect(self.gate_up_bias, "gate_up_bias", (E, 2 * I), bf)
+        _expect(self.down_scale, "down_scale", (E, H), torch.float32)
+        _expect(self.down_bias, "down_bias", (E, H), bf)
+        _expect(self.router_w, "router_w", (E, H), bf)
+        _expect(self.router_b, "router_b", (E,), bf)
+        _expect_same_device(self.gate_up_w, self.gate_up_scale, self.gate_up_bias, self.down_w, self.down_scale,
+                            self.down_bias, self.router_w, self.router_b)
+
     def descriptor(self) -> Int8Layer:
         return Int8Layer(E=self.E, H=self.H, I=self.I, top_k=self.top_k, gate_up_w=_ptr(self.gate_up_w),
                          gate_up_scale=_ptr(self.gate_up_scale), gate_up_bias=_ptr(self.gate_up_bias),
@@ -431,9 +533,16 @@ def moe_int8_forward(layer: MoEInt8Weights, x: torch.Tensor, out: Optional[torch
                      workspace: Optional[torch.Tensor] = None, topk_idx_out: Optional[torch.Tensor] = None,
                      topk_w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The INT8 W8A8 MoE layer on x (T, H) bf16; returns out (T, H) bf16."""
+    layer.validate()
+    _expect(x, "x", dtype=torch.bfloat16)
+    if x.dim() != 2 or int(x.shape[1]) != layer.H:
+        raise ValueError(f"x must be (T, {layer.H}), got {tuple(x.shape)}")
     T = int(x.shape[0])
     if out is None:
         out = torch.empty_like(x)
+    _expect_out(out, (T, layer.H), torch.bfloat16)
+    _check_topk_outs(topk_idx_out, topk_w_out, T, layer.top_k)
+    _expect_same_device(x, layer.router_w, out, workspace, topk_idx_out, topk_w_out)
     if workspace is None:
         workspace = torch.empty(max(moe_int8_workspace_bytes(layer, T), 256), dtype=torch.uint8, device=x.device)
     d = layer.descriptor()
@@ -484,6 +593,38 @@ class MoEWeights:
         return MoEWeights(gb, gs, self.gate_up_bias, db, ds, self.down_bias, self.router_w, self.router_b,
                           top_k=self.top_k, layout=LAYOUT_TILED)
 
+    def validate(self) -> None:
+        """Every tensor's shape and dtype against E, H, I and the layout
+        (ValueError on a mismatch): the library sizes its reads from those
+        alone.  Router and biases share one dtype (bf16 or fp32)."""
+        if self.router_w.dim() != 2 or self.gate_up_bias.dim() != 2 or self.gate_up_bias.shape[1] % 2:
+            raise ValueError("router_w must be (E, H) and gate_up_bias (E, 2I)")
+        E, H, I = self.E, self.H, self.I
+        pd = self.router_w.dtype
+        _dtype_code(pd)
+        _expect(self.router_b, "router_b", (E,), pd)
+        _expect(self.gate_up_bias, "gate_up_bias", (E, 2 * I), pd)
+        _expect(self.down_bias, "down_bias", (E, H), pd)
+        u8 = torch.uint8
+        if self.layout == LAYOUT_ROWS:
+            if H % 32 or I % 32:
+                raise ValueError(f"H and I must be multiples of 32, got {H}, {I}")
+            _expect(self.gate_up_blocks, "gate_up_blocks", (E, 2 * I, H // 32, 16), u8)
+            _expect(self.gate_up_scales, "gate_up_scales", (E, 2 * I, H // 32), u8)
+            _expect(self.down_blocks, "down_blocks", (E, H, I // 32, 16), u8)
+            _expect(self.down_scales, "down_scales", (E, H, I // 32), u8)
+        elif self.layout == LAYOUT_TILED:
+            gb, gs = mxfp4_tiled_bytes(E, 2 * I, H)
+            db, ds = mxfp4_tiled_bytes(E, H, I)
+            _expect(self.gate_up_blocks, "gate_up_blocks", dtype=u8, min_numel=gb)
+            _expect(self.gate_up_scales, "gate_up_scales", dtype=u8, min_numel=gs)
+            _expect(self.down_blocks, "down_blocks", dtype=u8, min_numel=db)
+            _expect(self.down_scales, "down_scales", dtype=u8, min_numel=ds)
+        else:
+            raise ValueError(f"unknown layout {self.layout}")
+        _expect_same_device(self.gate_up_blocks, self.gate_up_scales, self.gate_up_bias, self.down_blocks,
+                            self.down_scales, self.down_bias, self.router_w, self.router_b)
+
     def descriptor(self) -> Layer:
         return Layer(
             E=self.E, H=self.H, I=self.I, top_k=self.top_k, param_dtype=_dtype_code(self.router_w.dtype),
@@ -492,6 +633,23 @@ class MoEWeights:
             gate_up_bias=_ptr(self.gate_up_bias), down_blocks=_ptr(self.down_blocks),
             down_scales=_ptr(self.down_scales), down_bias=_ptr(self.down_bias), router_w=_ptr(self.router_w),
             router_b=_ptr(self.router_b))
+
+
+def _check_x(layer, x: torch.Tensor) -> int:
+    """x must be (T, H) in the layer's parameter dtype; returns T."""
+    layer.validate()
+    if x.dim() != 2 or int(x.shape[1]) != layer.H:
+        raise ValueError(f"x must be (T, {layer.H}), got {tuple(x.shape)}")
+    if x.dtype != layer.router_w.dtype:
+        raise ValueError(f"x must have the parameters' dtype {layer.router_w.dtype}, got {x.dtype}")
+    return int(x.shape[0])
+
+
+def _check_topk_outs(idx_out: Optional[torch.Tensor], w_out: Optional[torch.Tensor], T: int, k: int) -> None:
+    if idx_out is not None:
+        _expect(idx_out, "topk_idx_out", (T, k), torch.int32)
+    if w_out is not None:
+        _expect(w_out, "topk_w_out", (T, k), torch.float32)
 
 
 def _opts(act_dtype: torch.dtype, fp8: bool, x_scale: float, h_scale: float, idx_out=None, w_out=None,
@@ -529,9 +687,12 @@ def moe_mxfp4_forward(layer: MoEWeights, x: torch.Tensor, fp8: bool = False, x_s
     its top_k; the combine is the same.
     stage_events: optional ctypes array of STAGE_EVENTS hipEvent_t handles
     (see include/mxmoe.h) recorded around the stages on the current stream."""
-    T = int(x.shape[0])
+    T = _check_x(layer, x)
     if out is None:
         out = torch.empty_like(x)
+    _expect_out(out, (T, layer.H), x.dtype)
+    _check_topk_outs(topk_idx_out, topk_w_out, T, layer.top_k)
+    _expect_same_device(x, layer.router_w, out, workspace, topk_idx_out, topk_w_out)
     if workspace is None:
         workspace = alloc_workspace(layer, T, x.dtype, fp8, dense)
     d = layer.descriptor()
@@ -541,9 +702,51 @@ def moe_mxfp4_forward(layer: MoEWeights, x: torch.Tensor, fp8: bool = False, x_s
     return out
 
 
+class ForwardPlan:
+    """A prepared moe_mxfp4_forward call for a loop that repeats it on the
+    same tensors (a serving or benchmark loop): the tensors are checked and
+    the descriptor is built once; each call then only passes the stored
+    arguments and the current stream to the library.  The tensors must keep
+    their shapes and storage for the plan's lifetime (their contents may
+    change between calls)."""
+
+    def __init__(self, layer: MoEWeights, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, fp8: bool = False, x_scale: float = 1.0,
+                 h_scale: float = 1.0, topk_idx_out: Optional[torch.Tensor] = None,
+                 topk_w_out: Optional[torch.Tensor] = None, dense: bool = False):
+        T = _check_x(layer, x)
+        if out is None:
+            out = torch.empty_like(x)
+        _expect_out(out, (T, layer.H), x.dtype)
+        _check_topk_outs(topk_idx_out, topk_w_out, T, layer.top_k)
+        if workspace is None:
+            workspace = alloc_workspace(layer, T, x.dtype, fp8, dense)
+        _expect_same_device(x, layer.router_w, out, workspace, topk_idx_out, topk_w_out)
+        self.layer, self.x, self.out, self.workspace = layer, x, out, workspace
+        self._keep = (topk_idx_out, topk_w_out)
+        self._d = layer.descriptor()
+        self._o = _opts(x.dtype, fp8, x_scale, h_scale, topk_idx_out, topk_w_out, None, dense)
+        self._dev = x.device
+        self._fn = load_library().moe_mxfp4_forward
+        self._args = (ctypes.byref(self._d), _ptr(x), T, _ptr(out), ctypes.byref(self._o), _ptr(workspace),
+                      workspace.numel())
+
+    def __call__(self, stage_events=None) -> torch.Tensor:
+        """Enqueue the forward on the current stream; returns out."""
+        if stage_events is not None:
+            self._o.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
+        try:
+            _check(self._fn(*self._args, _stream(self._dev)))
+        finally:
+            if stage_events is not None:
+                self._o.stage_events = None
+        return self.out
+
+
 def moe_mxfp4_route(layer: MoEWeights, x: torch.Tensor, workspace: Optional[torch.Tensor] = None):
     """Routing only: returns (idx, w, counts, offsets, sorted_slots, slot_pos)."""
-    T = int(x.shape[0])
+    T = _check_x(layer, x)
+    _expect_same_device(x, layer.router_w, workspace)
     k, E = layer.top_k, layer.E
     dev = x.device
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -565,7 +768,10 @@ def moe_mxfp4_route(layer: MoEWeights, x: torch.Tensor, workspace: Optional[torc
 def moe_mxfp4_calibrate_fp8(layer: MoEWeights, x_calib: torch.Tensor,
                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Static FP8 scales (s_x, s_h) from a bf16 calibration batch, as a device float[2]."""
-    T = int(x_calib.shape[0])
+    T = _check_x(layer, x_calib)
+    if x_calib.dtype != torch.bfloat16:
+        raise ValueError("the calibration batch must be bf16")
+    _expect_same_device(x_calib, layer.router_w, workspace)
     scales = torch.empty((4,), dtype=torch.float32, device=x_calib.device)
     if workspace is None:
         workspace = alloc_workspace(layer, T, torch.bfloat16)

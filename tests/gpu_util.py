@@ -70,3 +70,33 @@ def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 def sub_case(case: W.MoECase, rows) -> W.MoECase:
     """The same layer on a subset of tokens (tokens are independent)."""
     return W.MoECase(case.name + "_sample", case.layer, case.x[rows].copy(), case.act_dtype, case.fp8, case.x_calib)
+
+
+# Float64 oracle outputs of the full-size cases, computed once per test
+# session and shared by every test that compares against them (both weight
+# layouts, the routed and the dense path).
+_REF_CACHE = {}
+
+
+def oracle_full(case: W.MoECase, x_scale=None, h_scale=None):
+    """(out, idx) of the oracle over every token of the case, with its own
+    routing (cached by case name and FP8 scales)."""
+    key = (case.name, case.fp8, x_scale, h_scale)
+    if key not in _REF_CACHE:
+        note(f"oracle over all {case.T} tokens of {case.name}")
+        out, parts = O.moe_forward(case.layer, case.x, case.act_dtype, fp8=case.fp8, x_scale=x_scale,
+                                   h_scale=h_scale, return_parts=True)
+        _REF_CACHE[key] = (out, parts["idx"])
+    return _REF_CACHE[key]
+
+
+def differing_sets(gpu_idx: np.ndarray, ref_idx: np.ndarray) -> np.ndarray:
+    """Tokens whose chosen expert sets differ (rounding-level near-ties)."""
+    return np.array([t for t in range(gpu_idx.shape[0])
+                     if set(gpu_idx[t].tolist()) != set(ref_idx[t].tolist())], dtype=np.int64)
+
+
+def poison(t) -> None:
+    """Fill a scratch tensor with 0xFF bytes (bf16 and e4m3 NaN) so that any
+    intermediate row a kernel fails to write shows up in the output."""
+    t.view(-1).view(__import__("torch").uint8).fill_(0xFF)

@@ -54,26 +54,23 @@ def test_unpack_ragged_rows(dev):
 
 
 def test_unpack_20b_expert_shapes_full_size(dev):
-    """The unpack workload at full size (gpt-oss-20b expert tensors, 32 experts):
-    two experts of each tensor compared in full, plus 4096 random rows."""
+    """The unpack workload at full size (gpt-oss-20b expert tensors, 32
+    experts each), in the launch configuration the benchmark times: every
+    output bit of both tensors, compared one expert at a time.  Scales lie
+    in [118, 127], so every value is finite and exact in bf16 and the raw
+    bits of the oracle's values (sign of zero included) are the reference."""
     import torch
     import mxfp4_quantized_moe_amd as mx
 
     case = W.unpack_20b()
-    rng = np.random.default_rng(1)
     for ti, (b, s) in enumerate(case.tensors):
         note(f"unpack 20b tensor {ti} shape {b.shape}")
         db, ds = W.array_to_torch(b, dev), W.array_to_torch(s, dev)
         out = mx.mxfp4_unpack(db, ds, torch.bfloat16)
         torch.cuda.synchronize()
-        for e in (0, b.shape[0] - 1):
-            got = O.bf16_from_bits(W.torch_to_array(out[e]))
-            _bits_equal_f64(got, O.mxfp4_unpack(b[e], s[e]))
-        E, R = b.shape[0], b.shape[1]
-        ee = rng.integers(0, E, size=4096)
-        rr = rng.integers(0, R, size=4096)
-        got = O.bf16_from_bits(W.torch_to_array(out[torch.from_numpy(ee).to(dev), torch.from_numpy(rr).to(dev)]))
-        _bits_equal_f64(got, O.mxfp4_unpack(b[ee, rr], s[ee, rr]))
+        for e in range(b.shape[0]):
+            got = W.torch_to_array(out[e])
+            assert np.array_equal(got, O.bf16_bits(O.mxfp4_unpack(b[e], s[e]))), (ti, e)
         del out, db, ds
         torch.cuda.empty_cache()
 

@@ -12,8 +12,8 @@ import pytest
 
 import oracle as O
 import workloads as W
-from tests.gpu_util import compare_routing, device, note
-from tests.test_gpu_layer import check_layer, run_gpu
+from tests.gpu_util import compare_routing, device, note, oracle_full
+from tests.test_gpu_layer import check_layer, fp8_20b_scales, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -56,14 +56,13 @@ def test_dense_decode_20b(dev, T):
 
 
 def test_dense_fp8_20b(dev):
-    """W-MXFP4 A-FP8 at T=2048 on the dense path (65536 GEMM rows); output on
-    12 tokens spread over the batch."""
+    """W-MXFP4 A-FP8 at T=2048 on the dense path (65536 GEMM rows); output of
+    every token against the routed oracle (shared with the routed test)."""
     case = W.fp8_20b()
-    s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+    s_x, s_h = fp8_20b_scales(case)
     note(f"{case.name} tiled dense")
     res, _, _ = run_gpu(case, dev, x_scale=s_x, h_scale=s_h, want_route=False, layout="tiled", dense=True)
-    sample = np.linspace(0, case.T - 1, 12).astype(int)
-    check_layer(case, res, sample=sample, x_scale=s_x, h_scale=s_h)
+    check_layer(case, res, x_scale=s_x, h_scale=s_h, full_ref=oracle_full(case, s_x, s_h))
 
 
 def test_dense_matches_routed_on_gpu(dev):

@@ -70,16 +70,13 @@ def test_fp8_linear_small(dev, seed, T, K, N, bias):
 
 def test_fp8_linear_full_size(dev):
     """T=4096 through a 2880 -> 5760 projection, in the launch configuration
-    the benchmark times; output on 16 rows spread over the batch (rows are
-    independent)."""
+    the benchmark times; every output row."""
     case = W.fp8_linear_case(55, 4096, 2880, 5760)
     note(case.name)
     got = _run(case, dev)
-    # 16 spread rows plus both sides of the first and last 128-row tile boundaries
-    rows = np.unique(np.concatenate([np.linspace(0, case.x.shape[0] - 1, 16).astype(int), [127, 128, 3967, 3968]]))
-    ref = O.fp8_linear(case.x[rows], case.w_codes, case.w_scale, case.x_scale, case.bias)
-    err = max_rel_err(got[rows], ref)
-    note(f"{case.name}: max|d|/max|ref| = {err:.3e} on 16 rows (bar {TOL})")
+    ref = O.fp8_linear(case.x, case.w_codes, case.w_scale, case.x_scale, case.bias)
+    err = max_rel_err(got, ref)
+    note(f"{case.name}: max|d|/max|ref| = {err:.3e} over all rows (bar {TOL})")
     assert np.all(np.isfinite(got)) and err <= TOL
 
 

@@ -14,7 +14,7 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import tiled_layout as TL
-from tests.gpu_util import device, max_rel_err, note
+from tests.gpu_util import device, max_rel_err, note, poison
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,9 @@ def _run(case, dev):
     T, k = case.T, case.layer.top_k
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    out = mx.moe_int8_forward(wts, x, topk_idx_out=idx, topk_w_out=w)
+    ws = torch.empty(max(mx.moe_int8_workspace_bytes(wts, T), 256), dtype=torch.uint8, device=dev)
+    poison(ws)  # an intermediate row left unwritten turns the output NaN
+    out = mx.moe_int8_forward(wts, x, topk_idx_out=idx, topk_w_out=w, workspace=ws)
     torch.cuda.synchronize()
     return W.torch_to_array(out), W.torch_to_array(idx), W.torch_to_array(w)
 
@@ -66,14 +68,13 @@ def _check_routing(case, gidx, gw, tau_rel=1e-4):
     return gidx.astype(np.int32), z / z.sum(axis=1, keepdims=True)
 
 
-def _check(case, res, sample=None):
+def _check(case, res):
+    """Every token against the oracle on the GPU's routing."""
     out, gidx, gw = res
     ov = _check_routing(case, gidx, gw)
-    rows = np.arange(case.T) if sample is None else sample
-    sub = W.Int8Case(case.name, case.layer, case.x[rows].copy())
-    ref = O.moe_forward_int8(sub.layer, sub.x, route_override=(ov[0][rows], ov[1][rows]))
-    got = O.bf16_from_bits(out[rows])
-    assert np.all(np.isfinite(O.bf16_from_bits(out)))
+    ref = O.moe_forward_int8(case.layer, case.x, route_override=ov)
+    got = O.bf16_from_bits(out)
+    assert np.all(np.isfinite(got))
     err = max_rel_err(got, ref)
     note(f"{case.name}: max|d|/max|ref| = {err:.3e} (bar {TOL})")
     assert err <= TOL
@@ -114,17 +115,10 @@ def test_int8_20b_decode_sizes(dev, T):
 
 
 def test_int8_20b_full_size(dev):
-    """T=2048 at the 20b shape: routing for every token, the output on 12
-    tokens spread over the batch plus the tokens at the busiest and least
-    busy experts' tile boundaries (grouping of the GPU's routing)."""
-    from tests.test_gpu_layer import boundary_tokens
-
+    """T=2048 at the 20b shape: routing and the output of every token."""
     case = W.int8_20b(2048)
     note(case.name)
-    res = _run(case, dev)
-    route = (res[1], res[2], *O.permute(res[1].astype(np.int64), case.layer.E))
-    spread = np.linspace(0, case.T - 1, 12).astype(int)
-    _check(case, res, sample=np.unique(np.concatenate([spread, boundary_tokens(case, route)])))
+    _check(case, _run(case, dev))
 
 
 def test_int8_zero_token_rows(dev):

@@ -56,13 +56,13 @@ def test_linear_matches_oracle(dev, seed, T, K, N, act, bias, layout):
     assert err <= bar
 
 
-def test_linear_full_size_sampled(dev):
-    """The bench shape (T=4096, K=2880, N=5760, tiled), checked on 8 spread tokens
-    and the rows at two tile boundaries."""
+def test_linear_full_size(dev):
+    """The bench shape (T=4096, K=2880, N=5760, tiled): every output row."""
     case = W.linear_case(10, 4096, 2880, 5760, "bf16", True)
     note(case.name)
     got = as_f64(run(case, dev, "tiled"), "bf16")
-    # 8 spread rows plus both sides of the first and last 128-row tile boundaries
-    sample = np.unique(np.concatenate([np.linspace(0, case.x.shape[0] - 1, 8).astype(int), [127, 128, 3967, 3968]]))
-    ref = O.mxfp4_linear(case.x[sample], case.blocks, case.scales, case.bias, "bf16")
-    assert max_rel_err(got[sample], ref) <= 1e-2
+    ref = O.mxfp4_linear(case.x, case.blocks, case.scales, case.bias, "bf16")
+    assert np.all(np.isfinite(got))
+    err = max_rel_err(got, ref)
+    note(f"  max|d|/max|ref| = {err:.3e} over all rows (bar 1e-2)")
+    assert err <= 1e-2
