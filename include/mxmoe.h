@@ -20,7 +20,9 @@
  *     leaves every output untouched.  MXMOE_ERR_HIP means a HIP call failed
  *     after validation; the outputs are then undefined.
  *   - The library allocates no device memory: scratch space comes from the
- *     caller's workspace, sized by the matching *_workspace_bytes call.
+ *     caller's workspace, sized by the matching *_workspace_bytes call
+ *     (moe_mxfp4_forward_noalloc uses a fixed device array of the library
+ *     instead).
  *   - Calls on distinct streams with distinct outputs and workspaces may run
  *     concurrently; two calls sharing a workspace must be ordered.
  *   - No C++ exception crosses this interface.
@@ -341,6 +343,26 @@ size_t moe_mxfp4_workspace_bytes(const mxmoe_layer_t* layer, int64_t T, const mx
 mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* layer, const void* x, int64_t T, void* out,
                                  const mxmoe_fwd_opts_t* opts, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * moe_mxfp4_forward_noalloc — moe_mxfp4_forward without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, results and errors as moe_mxfp4_forward; the scratch
+ * space is a device array of MXMOE_NOALLOC_SCRATCH_BYTES inside the library
+ * (one per GPU, held until the process ends; the call itself allocates
+ * nothing).  A call whose moe_mxfp4_workspace_bytes figure exceeds it
+ * returns MXMOE_ERR_WORKSPACE and launches nothing.  Nothing in that array
+ * needs to start at any value: the forward writes every entry it reads.
+ * All calls on one GPU share the array, so calls that may overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the
+ * caller.  The first call on a device looks up that device's copy of the
+ * array; the device must be current.
+ */
+#define MXMOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+mxmoe_status_t moe_mxfp4_forward_noalloc(const mxmoe_layer_t* layer, const void* x, int64_t T, void* out,
+                                         const mxmoe_fwd_opts_t* opts, void* stream);
 
 /*
  * moe_mxfp4_route — only the routing steps of the forward: router logits,

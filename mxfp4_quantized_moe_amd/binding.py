@@ -53,6 +53,7 @@ EXPORTED = (
     "moe_int8_forward",
     "moe_mxfp4_workspace_bytes",
     "moe_mxfp4_forward",
+    "moe_mxfp4_forward_noalloc",
     "moe_mxfp4_route",
     "moe_mxfp4_calibrate_fp8",
 )
@@ -169,6 +170,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mxfp4_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i64, ctypes.POINTER(FwdOpts)]
     lib.moe_mxfp4_forward.restype = i32
     lib.moe_mxfp4_forward.argtypes = [ctypes.POINTER(Layer), vp, i64, vp, ctypes.POINTER(FwdOpts), vp, sz, vp]
+    lib.moe_mxfp4_forward_noalloc.restype = i32
+    lib.moe_mxfp4_forward_noalloc.argtypes = [ctypes.POINTER(Layer), vp, i64, vp, ctypes.POINTER(FwdOpts), vp]
     lib.moe_mxfp4_route.restype = i32
     lib.moe_mxfp4_route.argtypes = [ctypes.POINTER(Layer), vp, i64, ctypes.POINTER(FwdOpts),
                                     vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -699,6 +702,30 @@ def moe_mxfp4_forward(layer: MoEWeights, x: torch.Tensor, fp8: bool = False, x_s
     o = _opts(x.dtype, fp8, x_scale, h_scale, topk_idx_out, topk_w_out, stage_events, dense)
     _check(load_library().moe_mxfp4_forward(ctypes.byref(d), _ptr(x), T, _ptr(out), ctypes.byref(o),
                                             _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+# Size of the library's own scratch array used by moe_mxfp4_forward_noalloc
+# (MXMOE_NOALLOC_SCRATCH_BYTES in include/mxmoe.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_mxfp4_forward_noalloc(layer: MoEWeights, x: torch.Tensor, out: torch.Tensor, fp8: bool = False,
+                              x_scale: float = 1.0, h_scale: float = 1.0,
+                              topk_idx_out: Optional[torch.Tensor] = None,
+                              topk_w_out: Optional[torch.Tensor] = None, dense: bool = False) -> torch.Tensor:
+    """moe_mxfp4_forward on the library's fixed scratch array instead of a
+    workspace: nothing is allocated (out is the caller's).  Batches whose
+    workspace_bytes exceed NOALLOC_SCRATCH_BYTES raise MXMOE_ERR_WORKSPACE;
+    calls that may overlap on one GPU must be ordered by the caller."""
+    T = _check_x(layer, x)
+    _expect_out(out, (T, layer.H), x.dtype)
+    _check_topk_outs(topk_idx_out, topk_w_out, T, layer.top_k)
+    _expect_same_device(x, layer.router_w, out, topk_idx_out, topk_w_out)
+    d = layer.descriptor()
+    o = _opts(x.dtype, fp8, x_scale, h_scale, topk_idx_out, topk_w_out, None, dense)
+    _check(load_library().moe_mxfp4_forward_noalloc(ctypes.byref(d), _ptr(x), T, _ptr(out), ctypes.byref(o),
+                                                    _stream(x.device)))
     return out
 
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/mxmoe.h"
 #include "launch.h"
@@ -244,6 +245,64 @@ bool use_prefill(const mxmoe_layer_t* L, int64_t T, int act, bool dense = false)
   return slots > 16 * active;
 }
 
+// The whole forward of moe_mxfp4_forward on a given scratch buffer.
+mxmoe_status_t forward_impl(const mxmoe_layer_t* L, const void* x, int64_t T, void* out, const mxmoe_fwd_opts_t* o,
+                            void* ws, size_t ws_bytes, void* stream) {
+  mxmoe_status_t st = check_layer(L);
+  if (st != MXMOE_OK) return st;
+  if ((st = check_opts(L, o, true)) != MXMOE_OK) return st;
+  const bool dense = o->expert_path == MXMOE_PATH_DENSE;
+  if ((st = check_tokens(L, T, dense)) != MXMOE_OK) return st;
+  if (T == 0) return MXMOE_OK;
+  if (!x || !out || !ws) return MXMOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return MXMOE_ERR_ALIGN;
+  const bool fp8 = o->fp8_act == 1;
+  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, fp8, gemm_rows(L, T, dense));
+  if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* const* ev = o->stage_events;
+  auto mark = [&](int i) { return ev && ev[i] ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
+  if (mark(0) != hipSuccess) return MXMOE_ERR_HIP;
+  hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
+                             nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr, dense);
+  if (e != hipSuccess) return MXMOE_ERR_HIP;
+  if (mark(2) != hipSuccess) return MXMOE_ERR_HIP;
+  const int act = fp8 ? ACT_FP8 : (o->act_dtype == MXMOE_BF16 ? ACT_BF16 : ACT_F32);
+  const float inv_x = fp8 ? 1.0f / o->x_scale : 1.0f;
+  const float inv_h = fp8 ? 1.0f / o->h_scale : 1.0f;
+  if (fp8) {
+    e = launch_quant_fp8(static_cast<const uint16_t*>(x), T * L->H, inv_x, at<uint8_t>(ws, w.xq), s);
+    if (e != hipSuccess) return MXMOE_ERR_HIP;
+  }
+  if (mark(3) != hipSuccess) return MXMOE_ERR_HIP;
+  const bool prefill = use_prefill(L, T, act, dense);
+  GemmArgs g0 = gemm_args(L, w, ws, T, act, 0, dense);
+  g0.bsrc = fp8 ? at<void>(ws, w.xq) : x;
+  if (fp8) {
+    g0.acc_scale = o->x_scale;
+    g0.out_inv_scale = inv_h;
+  }
+  if ((e = launch_moe_gemm(g0, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  if (mark(4) != hipSuccess) return MXMOE_ERR_HIP;
+  GemmArgs g1 = gemm_args(L, w, ws, T, act, 1, dense);
+  if (fp8) g1.acc_scale = o->h_scale;
+  if ((e = launch_moe_gemm(g1, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  if (mark(5) != hipSuccess) return MXMOE_ERR_HIP;
+  CombineArgs ca{};
+  ca.Y = at<void>(ws, w.y);
+  ca.y_bf16 = act != ACT_F32;
+  ca.pos = at<int32_t>(ws, w.pos);
+  ca.wts = at<float>(ws, w.wts);
+  ca.out = out;
+  ca.out_bf16 = o->act_dtype == MXMOE_BF16;
+  ca.T = int(T);
+  ca.H = L->H;
+  ca.top_k = L->top_k;
+  if ((e = launch_combine(ca, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  return hip_status(mark(6));
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,59 +386,7 @@ size_t moe_mxfp4_workspace_bytes(const mxmoe_layer_t* L, int64_t T, const mxmoe_
 
 mxmoe_status_t moe_mxfp4_forward(const mxmoe_layer_t* L, const void* x, int64_t T, void* out,
                                  const mxmoe_fwd_opts_t* o, void* ws, size_t ws_bytes, void* stream) {
-  mxmoe_status_t st = check_layer(L);
-  if (st != MXMOE_OK) return st;
-  if ((st = check_opts(L, o, true)) != MXMOE_OK) return st;
-  const bool dense = o->expert_path == MXMOE_PATH_DENSE;
-  if ((st = check_tokens(L, T, dense)) != MXMOE_OK) return st;
-  if (T == 0) return MXMOE_OK;
-  if (!x || !out || !ws) return MXMOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return MXMOE_ERR_ALIGN;
-  const bool fp8 = o->fp8_act == 1;
-  const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, fp8, gemm_rows(L, T, dense));
-  if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  void* const* ev = o->stage_events;
-  auto mark = [&](int i) { return ev && ev[i] ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
-  if (mark(0) != hipSuccess) return MXMOE_ERR_HIP;
-  hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
-                             nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr, dense);
-  if (e != hipSuccess) return MXMOE_ERR_HIP;
-  if (mark(2) != hipSuccess) return MXMOE_ERR_HIP;
-  const int act = fp8 ? ACT_FP8 : (o->act_dtype == MXMOE_BF16 ? ACT_BF16 : ACT_F32);
-  const float inv_x = fp8 ? 1.0f / o->x_scale : 1.0f;
-  const float inv_h = fp8 ? 1.0f / o->h_scale : 1.0f;
-  if (fp8) {
-    e = launch_quant_fp8(static_cast<const uint16_t*>(x), T * L->H, inv_x, at<uint8_t>(ws, w.xq), s);
-    if (e != hipSuccess) return MXMOE_ERR_HIP;
-  }
-  if (mark(3) != hipSuccess) return MXMOE_ERR_HIP;
-  const bool prefill = use_prefill(L, T, act, dense);
-  GemmArgs g0 = gemm_args(L, w, ws, T, act, 0, dense);
-  g0.bsrc = fp8 ? at<void>(ws, w.xq) : x;
-  if (fp8) {
-    g0.acc_scale = o->x_scale;
-    g0.out_inv_scale = inv_h;
-  }
-  if ((e = launch_moe_gemm(g0, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
-  if (mark(4) != hipSuccess) return MXMOE_ERR_HIP;
-  GemmArgs g1 = gemm_args(L, w, ws, T, act, 1, dense);
-  if (fp8) g1.acc_scale = o->h_scale;
-  if ((e = launch_moe_gemm(g1, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
-  if (mark(5) != hipSuccess) return MXMOE_ERR_HIP;
-  CombineArgs ca{};
-  ca.Y = at<void>(ws, w.y);
-  ca.y_bf16 = act != ACT_F32;
-  ca.pos = at<int32_t>(ws, w.pos);
-  ca.wts = at<float>(ws, w.wts);
-  ca.out = out;
-  ca.out_bf16 = o->act_dtype == MXMOE_BF16;
-  ca.T = int(T);
-  ca.H = L->H;
-  ca.top_k = L->top_k;
-  if ((e = launch_combine(ca, s)) != hipSuccess) return MXMOE_ERR_HIP;
-  return hip_status(mark(6));
+  return forward_impl(L, x, T, out, o, ws, ws_bytes, stream);
 }
 
 mxmoe_status_t moe_mxfp4_route(const mxmoe_layer_t* L, const void* x, int64_t T, const mxmoe_fwd_opts_t* o,
@@ -784,6 +791,60 @@ mxmoe_status_t moe_int8_forward(const mxmoe_int8_layer_t* L, const void* x, int6
   ca.H = L->H;
   ca.top_k = L->top_k;
   return hip_status(launch_combine(ca, s));
+}
+
+}  // extern "C"
+
+// ------------------------------------------- forward without allocation
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the forward's scratch space is one file-scope device array of
+// MXMOE_NOALLOC_SCRATCH_BYTES, which every GPU the library runs on holds
+// until the process ends.  In host code the array's name only stands in for
+// it; its device address is looked up once per device with that device
+// current, and only that address is handed to kernels.
+
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[MXMOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's copy of `scratch` (the current device's; looked up on its
+// first use and kept).
+mxmoe_status_t scratch_address(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MXMOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MXMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return MXMOE_ERR_HIP;
+    g_scratch_ptr[dev] = q;
+  }
+  *p = g_scratch_ptr[dev];
+  return MXMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxmoe_status_t moe_mxfp4_forward_noalloc(const mxmoe_layer_t* L, const void* x, int64_t T, void* out,
+                                         const mxmoe_fwd_opts_t* o, void* stream) {
+  mxmoe_status_t st = check_layer(L);
+  if (st != MXMOE_OK) return st;
+  if ((st = check_opts(L, o, true)) != MXMOE_OK) return st;
+  const bool dense = o->expert_path == MXMOE_PATH_DENSE;
+  if ((st = check_tokens(L, T, dense)) != MXMOE_OK) return st;
+  if (T == 0) return MXMOE_OK;
+  const size_t need = layout(L->E, L->H, L->I, L->top_k, T, o->act_dtype, o->fp8_act == 1, gemm_rows(L, T, dense)).total;
+  if (need > MXMOE_NOALLOC_SCRATCH_BYTES) return MXMOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MXMOE_OK) return st;
+  return forward_impl(L, x, T, out, o, ws, MXMOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -149,6 +149,32 @@ def test_forward_token_and_workspace_validation(lib):
     assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(_layer(H=40)), 8, ctypes.byref(_opts())) == 0
 
 
+def test_forward_noalloc_validation(lib):
+    """The no-allocation forward validates like moe_mxfp4_forward and refuses
+    a batch whose workspace exceeds its fixed scratch array, before any
+    launch and before it looks up the array's device address."""
+    L = _layer()
+
+    def fwd(layer=L, T=8, opts=None, x=P, out=P):
+        opts = opts or _opts()
+        return lib.moe_mxfp4_forward_noalloc(ctypes.byref(layer), x, T, out, ctypes.byref(opts), None)
+
+    assert fwd(_layer(H=48)) == SHAPE
+    assert fwd(_layer(router_b=None)) == NULL
+    assert fwd(opts=_opts(act_dtype=0)) == DTYPE
+    assert fwd(opts=_opts(fp8_act=1, x_scale=0.0)) == VALUE
+    assert fwd(T=-1) == SHAPE
+    assert fwd(T=0, x=None, out=None) == OK  # empty batch: no-op
+    big = _layer(E=32, H=2880, I=2880, top_k=4)
+    n = lib.moe_mxfp4_workspace_bytes(ctypes.byref(big), 4096, ctypes.byref(_opts()))
+    assert n > B.NOALLOC_SCRATCH_BYTES
+    assert fwd(big, T=4096) == WS
+    # the header's figure and the binding's agree
+    text = open(HEADER).read()
+    assert re.search(r"#define MXMOE_NOALLOC_SCRATCH_BYTES \(32u << 20\)", text)
+    assert B.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
 def test_dense_path_validation(lib):
     L = _layer(E=32, H=2880, I=2880, top_k=4)
     assert _fwd(lib, _layer(), opts=_opts(expert_path=2)) == VALUE
