@@ -137,6 +137,19 @@ def expert_gemm_bytes(case, phase: int, n_active: int, dense: bool = False) -> i
     return n_active * w + T * k * I * ab + T * k * H * yb
 
 
+def step_bytes(case, n_active: int) -> int:
+    """Algorithmic HBM bytes of one whole routed step: the router's weights
+    and bias, x in, the routed experts' packed weights, scales and biases of
+    both matrices once, and the output (the intermediates h and Y need not
+    leave the chip)."""
+    L = case.layer
+    H, I, T = L.H, L.I, case.T
+    pb = 2 if L.param_dtype == "bf16" else 4
+    ab = 2 if case.act_dtype == "bf16" else 4  # x and out stay bf16 in the FP8 mode
+    expert = 2 * I * (H // 32) * 17 + 2 * I * pb + H * (I // 32) * 17 + H * pb
+    return L.E * H * pb + L.E * pb + n_active * expert + 2 * T * H * ab
+
+
 def expert_gemm_flops(case, phase: int, dense: bool = False) -> int:
     L = case.layer
     slots = case.T * (L.E if dense else L.top_k)
@@ -336,6 +349,12 @@ def bench_layer(args, dev):
         "stages_us": {name: float(v * 1e3) for name, v in zip(STAGES, avg)},
         "stages_note": "separate untimed pass with all stage events (each record adds a few us)",
     }
+    if decode_shaped and not dense:
+        # the whole step against HBM: its algorithmic bytes over the wall
+        # time per step (launch gaps and the small stages included)
+        sb = step_bytes(case, n_active)
+        res["step_hbm"] = {"bytes": sb, "GBps": sb / (ms_step * 1e-3) / 1e9,
+                           "frac": sb / (ms_step * 1e-3) / 1e9 / PEAK["hbm_GBps"]}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, dense)
     return res

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxmoe.so")
-SOURCES = ["api.hip", "codec.hip", "routing.hip", "moe_gemm.hip"]
+SOURCES = ["moe_gemm.hip", "routing.hip", "api.hip", "codec.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -30,11 +30,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile and link the library; returns its path.  Raises on failure."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), *srcs, "-o", tmp]
+def _run(cmd, verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     try:
@@ -45,7 +41,27 @@ def build(verbose: bool = False) -> str:
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel, one object each) and link the
+    library; returns its path.  Raises on failure."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    with tempfile.TemporaryDirectory(prefix="mxmoe_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
+        cflags = [f for f in FLAGS if f != "-shared"]
+        cmds = [[HIPCC, *cflags, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as pool:
+            errs = list(pool.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB + ".tmp"
+        errs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose))
+    err = "\n".join(e for e in errs if e.strip())
+    if verbose and err:
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB

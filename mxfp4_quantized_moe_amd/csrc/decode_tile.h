@@ -1,0 +1,205 @@
+// Decode-shaped tile of the MXFP4 expert GEMMs on the tiled weight order
+// (bf16 and FP8 activations), for gfx950: one 64-row group of one routed
+// expert against that expert's tokens.
+//
+// Bound by streaming the routed experts' packed weights.  The workgroup's 4
+// waves split the K chunks (c = wave, wave + 4, ...) and every wave covers
+// all 4 row tiles, so each activation fragment it loads feeds 4 MFMAs.  Per
+// chunk a wave loads 4 contiguous 1 KB weight pieces, one scale dword (the
+// 4 row tiles' scale bytes of its lane) and its token fragments, and keeps D
+// chunks in flight in a register ring with explicit vmcnt waits.  A pass
+// covers up to 32 tokens.  Partial sums meet in LDS in a fixed wave order,
+// one token sub-tile at a time.
+#pragma once
+
+#include "gemm_common.h"
+
+namespace mxmoe {
+
+template <int ACT, int NA>
+struct DecodeStage {
+  // 16-byte B loads per token sub-tile: 4 for bf16 tokens (32 values), 2
+  // for FP8 codes
+  static constexpr int BL = ACT == ACT_BF16 ? 4 : 2;
+  uint4 aq[4];
+  uint32_t sw;
+  uint4 bq[NA][BL];
+};
+
+// LDS of one decode tile: the 4 waves' partial sums of one token sub-tile.
+constexpr int kDecodeTileLds = 4 * 4 * 64 * 16;
+
+// Tile (expert e, row group q) for the n_e tokens in sorted rows row_start
+// .. row_start + n_e - 1.  red: kDecodeTileLds bytes of LDS.
+template <int ACT, int PHASE>
+__device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int row_start, int n_e,
+                                            f32x4_t* red_lds) {
+  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "bf16 or fp8 activations");
+  // [wave][row tile][lane] of one token sub-tile
+  f32x4_t (*red)[4][64] = reinterpret_cast<f32x4_t (*)[4][64]>(red_lds);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const WBuf wb = expert_weights<true>(a, e);
+  const int t0 = 4 * q;  // first row tile of the group
+  const int nb = a.nb, nc = wb.nc, K = nb * 32;
+  constexpr int EB = ACT == ACT_BF16 ? 2 : 1;  // bytes per B element
+  const uint32_t row_bytes = uint32_t(K) * EB;
+  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
+  const int nj = (nc - wave + 3) >> 2;  // chunks of this wave (0 when nc <= wave)
+  const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
+  // bias of the 4 output rows this lane stores (row tile t0 + wave, rows
+  // 4g .. 4g+3), fetched before the K loop as raw bf16 bits
+  const int r0 = 16 * (t0 + wave) + 4 * g;
+  const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
+  const uint2 biasq = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, r0 < a.R ? uint32_t(r0) * 2u : kOOB, 0, 0));
+
+  // up to 32 tokens per pass over the weights (registers bound the tile)
+  for (int tg = 0; tg < n_e; tg += 32) {
+    uint32_t boff[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      boff[nt] = act_row_offset(a, PHASE, row_start, tg + nt * 16 + r16, n_e, row_bytes);
+    const int nt_active = min(2, (n_e - tg + 15) >> 4);
+
+    auto pass = [&](auto ntc) __attribute__((always_inline)) {
+      constexpr int NA = decltype(ntc)::value;
+      constexpr int D = NA == 1 ? 3 : 2;  // chunks in flight per wave (3 measured faster than 2 and 4)
+      using St = DecodeStage<ACT, NA>;
+      constexpr int LOADS = 4 + 1 + NA * St::BL;        // VMEM instructions per chunk
+      St st[D];
+      f32x4_t acc[4][NA];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+      // chunk j of this wave is c = wave + 4j; past the wave's last chunk
+      // every load reads zeros
+      auto issue = [&](int j, St& s) __attribute__((always_inline)) {
+        const int c = wave + 4 * j;
+        const bool ok = j < nj;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          s.aq[rt] = buf_load_b128(wb.blk, ok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
+        s.sw = buf_load_b32(wb.sc, ok ? uint32_t((q * nc + c) * 256 + lane * 4) : kOOB);
+        if constexpr (ACT == ACT_BF16) {
+          const uint32_t kofs = (ok && 4 * c + g < nb) ? uint32_t(128 * c + 32 * g) * 2 : kOOB;
+#pragma unroll
+          for (int nt = 0; nt < NA; ++nt)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) s.bq[nt][s4] = buf_load_b128(bsrc, oob_add(boff[nt], oob_add(kofs, 16u * s4)));
+        } else {
+          // FP8 B: lane group g holds K = 128c + 16g .. +16 and 128c + 64 + 16g .. +16
+          const uint32_t k0 = (ok && 4 * c + (g >> 1) < nb) ? uint32_t(128 * c + 16 * g) * EB : kOOB;
+          const uint32_t k1 = (ok && 4 * c + 2 + (g >> 1) < nb) ? uint32_t(128 * c + 64 + 16 * g) * EB : kOOB;
+#pragma unroll
+          for (int nt = 0; nt < NA; ++nt) {
+            s.bq[nt][0] = buf_load_b128(bsrc, oob_add(boff[nt], k0));
+            s.bq[nt][1] = buf_load_b128(bsrc, oob_add(boff[nt], k1));
+          }
+        }
+      };
+      auto compute = [&](const St& s) __attribute__((always_inline)) {
+        if constexpr (ACT == ACT_BF16) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              const bf16x8_t av = fp4x8_to_bf16x8(dword(s.aq[rt], s4), e8m0_as_scale_operand((s.sw >> (8 * rt)) & 0xFFu));
+#pragma unroll
+              for (int nt = 0; nt < NA; ++nt)
+                acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, s.bq[nt][s4]),
+                                                                      acc[rt][nt], 0, 0, 0);
+            }
+          }
+        } else {
+          i32x8_t bv[NA];
+#pragma unroll
+          for (int nt = 0; nt < NA; ++nt) {
+            const uint4 p0 = s.bq[nt][0], p1 = s.bq[nt][1];
+            bv[nt] = i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
+          }
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const uint4 q4 = s.aq[rt];
+            const i32x8_t av = i32x8_t{int(q4.x), int(q4.y), int(q4.z), int(q4.w), 0, 0, 0, 0};
+#pragma unroll
+            for (int nt = 0; nt < NA; ++nt)
+              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[nt], acc[rt][nt], 4, 0, 0,
+                                                                             int((s.sw >> (8 * rt)) & 0xFFu), 0, 127);
+          }
+        }
+      };
+
+      // prologue: chunks 0 .. D-2 in flight, issued in order
+      order_point();
+      issue(0, st[0]);
+      order_point();
+      if constexpr (D > 2) { issue(1, st[1]); order_point(); }
+      if constexpr (D > 3) { issue(2, st[2]); order_point(); }
+      // iteration j: wait for chunk j (D-2 later chunks may stay in flight),
+      // issue chunk j + D - 1 into the stage chunk j-1 used, compute chunk j
+      auto iteration = [&](int j, auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;  // j % D
+        wait_vmcnt<(D - 2) * LOADS>();
+        issue(j + D - 1, st[(u + D - 1) % D]);
+        order_point();
+        compute(st[u]);
+      };
+      int j0 = 0;
+      for (; j0 + D <= nj; j0 += D) {
+        iteration(j0, IC<0>{});
+        iteration(j0 + 1, IC<1>{});
+        if constexpr (D > 2) iteration(j0 + 2, IC<2 % D>{});
+        if constexpr (D > 3) iteration(j0 + 3, IC<3 % D>{});
+      }
+      if (j0 < nj) iteration(j0, IC<0>{});
+      if (j0 + 1 < nj) iteration(j0 + 1, IC<1 % D>{});
+      if constexpr (D > 3) if (j0 + 2 < nj) iteration(j0 + 2, IC<2 % D>{});
+      wait_vmcnt<0>();
+      // Never true (slot counts are non-negative).  It keeps every prefetch
+      // live: the vmcnt waits above count loads, so none may be dropped as
+      // dead even when its chunk lies past the end.
+      if (a.n_slots < 0) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          x ^= st[d].aq[0].x ^ st[d].aq[1].y ^ st[d].aq[2].z ^ st[d].aq[3].w ^ st[d].sw;
+#pragma unroll
+          for (int nt = 0; nt < NA; ++nt)
+#pragma unroll
+            for (int b = 0; b < St::BL; ++b) x ^= st[d].bq[nt][b].x;
+        }
+        static_cast<uint32_t*>(a.out)[0] = x;
+      }
+
+      // fixed-order sum of the 4 waves' partials, one token sub-tile at a
+      // time; wave w finishes row tile w
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt][nt];
+        __syncthreads();
+        const int j = tg + nt * 16 + r16;
+        if (j < n_e && r0 < a.R) {
+          f32x4_t sum = red[0][wave][lane];
+          sum += red[1][wave][lane];
+          sum += red[2][wave][lane];
+          sum += red[3][wave][lane];
+          store_rows_biased<ACT, PHASE>(a, r0, row_start + j, sum[0] * a.acc_scale + __uint_as_float(biasq.x << 16),
+                                             sum[1] * a.acc_scale + __uint_as_float(biasq.x & 0xFFFF0000u),
+                                             sum[2] * a.acc_scale + __uint_as_float(biasq.y << 16),
+                                             sum[3] * a.acc_scale + __uint_as_float(biasq.y & 0xFFFF0000u));
+        }
+        __syncthreads();
+      }
+    };
+    if (nt_active == 1)
+      pass(IC<1>{});
+    else
+      pass(IC<2>{});
+  }
+}
+
+}  // namespace mxmoe

@@ -32,10 +32,8 @@
 //
 // All tile loads are range-checked buffer loads (see device_common.h): the
 // tails read as zero without branches.
-#include <type_traits>
-
-#include "device_common.h"
-#include "launch.h"
+#include "decode_tile.h"
+#include "gemm_common.h"
 
 namespace mxmoe {
 
@@ -51,168 +49,6 @@ namespace mxmoe {
 constexpr int kDecodeRowTiles = MXMOE_DECODE_ROW_TILES;
 constexpr int kDecodeChunkBuf = MXMOE_DECODE_CHUNKS;
 
-// ------------------------------------------------------------ operands
-
-struct AFrag {
-  uint4 q;       // 16 bytes = 32 nibbles of one block of one weight row
-  uint32_t sw;   // the aligned dword holding its e8m0 scale byte (0 past the tensor)
-  uint32_t sh;   // bit position of that byte in sw
-  // The scale byte is extracted at its use, not right after the load: an
-  // extension next to the load would make every prefetch wait at once.
-  __device__ __forceinline__ uint32_t scale() const { return (sw >> sh) & 0xFFu; }
-};
-
-// Weights of one expert as buffers.  Row order: blocks (R, nb, 16) and
-// scales (R, nb).  Tiled order (declared in mxmoe.h): rt4 row tiles of 16
-// rows x nc chunks, one 1 KB piece each, in the order the LDS tiles are
-// read; scales in 256-byte groups per 64 rows and chunk, whose dword l
-// holds the scales of lane l for the group's 4 row tiles.
-struct WBuf {
-  rsrc_t blk, sc;
-  int R, nb;
-  int rt4, nc;  // tiled order only
-};
-
-template <bool TILED>
-__device__ __forceinline__ WBuf expert_weights(const GemmArgs& a, int e) {
-  WBuf w;
-  w.R = a.R;
-  w.nb = a.nb;
-  w.nc = (a.nb + 3) >> 2;
-  w.rt4 = 4 * ((a.R + 63) >> 6);
-  if constexpr (TILED) {
-    const int64_t bb = int64_t(w.rt4) * w.nc * 1024, sb = int64_t(w.rt4 / 4) * w.nc * 256;
-    w.blk = make_rsrc(a.wblk + int64_t(e) * bb, uint32_t(bb));
-    w.sc = make_rsrc(a.wsc + int64_t(e) * sb, uint32_t(sb));
-  } else {
-    const int64_t rb = int64_t(a.R) * a.nb;
-    w.blk = make_rsrc(a.wblk + int64_t(e) * rb * 16, uint32_t(rb * 16));
-    w.sc = make_rsrc(a.wsc + int64_t(e) * rb, uint32_t(rb));
-  }
-  return w;
-}
-
-// 8-bit (e4m3 or int8) weights of expert e in the tiled 8-bit order
-// (declared in mxmoe.h): rt4 row tiles of 16 rows x nc 128-wide chunks, 2 KB
-// each, lane (g, r) holding row r's bytes 16g .. 16g+15 and 64+16g ..
-// 64+16g+15 of the chunk (the K order of an 8-bit MFMA operand).  No block
-// scales.
-__device__ __forceinline__ WBuf byte_weights(const GemmArgs& a, int e) {
-  WBuf w;
-  w.R = a.R;
-  w.nb = a.nb;
-  w.nc = (a.nb + 3) >> 2;
-  w.rt4 = 4 * ((a.R + 63) >> 6);
-  const int64_t bb = int64_t(w.rt4) * w.nc * 2048;
-  w.blk = make_rsrc(a.wblk + int64_t(e) * bb, uint32_t(bb));
-  w.sc = w.blk;
-  return w;
-}
-
-// Slot of block b of row r (both within a 16 x 4 piece) in a 1 KB tile:
-// the block index is XOR-swizzled with the row so that the 16 lanes of a
-// lane group read 16 distinct bank groups.
-__device__ __forceinline__ int piece_slot(int r, int b) { return r * 4 + (b ^ ((r >> 2) & 3)); }
-
-// Position of 16-byte piece p (K = 8p .. 8p+7 of the chunk) in the 256-byte
-// LDS row of token tok, bf16 token tiles.  gfx950 serves ds_read_b128 16
-// lanes at a time against 64 banks of 4 bytes; the 16 lanes of a group are
-// the 4-lane blocks of one half-wave whose lane bits 2..4 have the same
-// parity (measured with SQ_LDS_BANK_CONFLICT over lane patterns chosen to
-// tell the candidate groupings apart), and a group is conflict-free when its
-// 16 slots are distinct modulo 16.  In MFMA step st lane (g, r) reads piece
-// 4g + st of token r; XOR-ing the piece with the token's low 4 bits rotated
-// by 2 makes every group conflict-free for all four steps (checked for all
-// of them against that grouping).
-__device__ __forceinline__ int bf16_piece_pos(int tok, int p) { return p ^ (((tok << 2) | ((tok >> 2) & 3)) & 15); }
-
-// Block `block` of weight row `row`; zero when either is out of range.
-__device__ __forceinline__ AFrag load_a(const WBuf& w, int row, int block) {
-  const bool ok = row < w.R && block < w.nb;
-  const uint32_t o = uint32_t(row * w.nb + block);
-  AFrag f;
-  f.q = buf_load_b128(w.blk, ok ? o * 16u : kOOB);
-  f.sw = buf_load_b32(w.sc, ok ? (o & ~3u) : kOOB);
-  f.sh = (o & 3u) * 8u;
-  return f;
-}
-
-// Tiled order: lane (g, r16) of row tile t, chunk c (block 4c+g of row
-// 16t + r16); zero past the padded tensor.
-__device__ __forceinline__ AFrag load_a_tiled(const WBuf& w, int t, int c, int r16, int g) {
-  const bool ok = t < w.rt4 && c < w.nc;
-  AFrag f;
-  f.q = buf_load_b128(w.blk, ok ? uint32_t((t * w.nc + c) * 1024 + piece_slot(r16, g) * 16) : kOOB);
-  f.sw = buf_load_b32(w.sc, ok ? uint32_t(((t >> 2) * w.nc + c) * 256 + (16 * g + r16) * 4) : kOOB);
-  f.sh = uint32_t(t & 3) * 8u;
-  return f;
-}
-
-__device__ __forceinline__ uint32_t dword(const uint4& q, int i) {
-  return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
-}
-
-// Byte offset of token row j (of n >= 1) of a tile inside bsrc, or kOOB.
-// gate_up gathers x rows by token id; down reads h rows in sorted order.
-// The token-id load is unconditional (clamped index) so it needs no branch.
-__device__ __forceinline__ uint32_t act_row_offset(const GemmArgs& a, int phase, int row_start, int j, int n,
-                                                   uint32_t row_bytes) {
-  const int p = row_start + min(j, n - 1);
-  const int src_row = phase == 0 ? a.sorted_tok[p] : p;
-  return j < n ? uint32_t(src_row) * row_bytes : kOOB;
-}
-
-// ------------------------------------------------------------ epilogue
-
-// Store rows r0 .. r0+3 of one token (sorted row p), bias already added:
-// gate_up applies the SwiGLU and writes h, down writes Y (bf16 when the
-// activations are bf16, its only reader being the combine, which sums the
-// k rows of a token in fp32; fp32 in the fp32 mode).
-template <int ACT, int PHASE>
-__device__ __forceinline__ void store_rows_biased(const GemmArgs& a, int r0, int64_t p, float v0, float v1, float v2,
-                                                  float v3) {
-  if constexpr (PHASE == 0) {
-    // rows r0, r0+1 = (gate, up) of h column r0/2; rows r0+2, r0+3 the next
-    const float h0 = clamped_swiglu(v0, v1);
-    const float h1 = clamped_swiglu(v2, v3);
-    const int64_t I = a.R / 2;
-    const int64_t o = p * I + r0 / 2;
-    if constexpr (ACT == ACT_BF16 || ACT == ACT_INT8) {  // int8: h stays bf16 until its per-row quantisation
-      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + o) = pack_bf16x2(h0, h1);
-    } else if constexpr (ACT == ACT_F32) {
-      *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o) = make_float2(h0, h1);
-    } else {
-      const uint32_t q = pack_e4m3x4(h0 * a.out_inv_scale, h1 * a.out_inv_scale, 0.f, 0.f);
-      *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.out) + o) = uint16_t(q & 0xFFFFu);
-    }
-  } else if constexpr (ACT == ACT_F32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + p * a.R + r0) = make_float4(v0, v1, v2, v3);
-  } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + p * a.R + r0) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-  }
-}
-
-// Scale, add the bias of rows r0 .. r0+3 of expert e, and store.
-template <int ACT, int PHASE>
-__device__ __forceinline__ void store_rows(const GemmArgs& a, int e, int r0, int64_t p, float v0, float v1, float v2,
-                                           float v3) {
-  const int64_t bo = int64_t(e) * a.R + r0;
-  store_rows_biased<ACT, PHASE>(a, r0, p, v0 * a.acc_scale + load_param(a.bias, bo + 0, a.bias_bf16),
-                                v1 * a.acc_scale + load_param(a.bias, bo + 1, a.bias_bf16),
-                                v2 * a.acc_scale + load_param(a.bias, bo + 2, a.bias_bf16),
-                                v3 * a.acc_scale + load_param(a.bias, bo + 3, a.bias_bf16));
-}
-
-template <int N>
-using IC = std::integral_constant<int, N>;
-
-// Workgroup barrier that orders LDS traffic only: the global prefetches of
-// later chunks stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // =====================================================================
 // Decode-shaped GEMM: few tokens per expert.  The bound is streaming the
@@ -1174,197 +1010,18 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   }
 }
 
-// =====================================================================
-// Decode-shaped GEMM on the tiled weight order (bf16 and FP8 activations).
-//
-// Bound by streaming the routed experts' packed weights.  A workgroup owns
-// one 64-row group (4 row tiles, one scale group) of one active expert; its
-// 4 waves split the K chunks (c = wave, wave + 4, ...) and every wave covers
-// all 4 row tiles, so each activation fragment it loads feeds 4 MFMAs.  Per
-// chunk a wave loads 4 contiguous 1 KB weight pieces, one scale dword (the
-// 4 row tiles' scale bytes of its lane) and its token fragments, and keeps D
-// chunks in flight in a register ring with explicit vmcnt waits.  A pass
-// covers up to 32 tokens.  Partial sums meet in LDS in a fixed wave order,
-// one token sub-tile at a time.
-// =====================================================================
-
-template <int ACT, int NA>
-struct DecodeStage {
-  static constexpr int BL = ACT == ACT_BF16 ? 4 : 2;  // 16-byte B loads per token sub-tile
-  uint4 aq[4];
-  uint32_t sw;
-  uint4 bq[NA][BL];
-};
-
+// Decode-shaped GEMM on the tiled weight order (bf16 and FP8 activations):
+// one workgroup per (64-row group, active expert slot); the tile itself is
+// decode_tile (decode_tile.h).
 template <int ACT, int PHASE>
 __global__ __launch_bounds__(256, 2) void gemm_decode_tiled_kernel(GemmArgs a) {
-  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "bf16 or fp8 activations");
-  __shared__ f32x4_t red[4][4][64];  // [wave][row tile][lane] of one token sub-tile
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, r16 = lane & 15;
   const int slot = blockIdx.y;
   if (slot >= a.active[0]) return;
   const int e = a.active[1 + slot];
   const int row_start = a.offsets[e];
   const int n_e = a.offsets[e + 1] - row_start;
-  const WBuf wb = expert_weights<true>(a, e);
-  const int q = blockIdx.x;  // row group
-  const int t0 = 4 * q;      // its first row tile
-  const int nb = a.nb, nc = wb.nc, K = nb * 32;
-  constexpr int EB = ACT == ACT_BF16 ? 2 : 1;
-  const uint32_t row_bytes = uint32_t(K) * EB;
-  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
-  const int nj = (nc - wave + 3) >> 2;  // chunks of this wave (0 when nc <= wave)
-  const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
-  // bias of the 4 output rows this lane stores (row tile t0 + wave, rows
-  // 4g .. 4g+3), fetched before the K loop as raw bf16 bits
-  const int r0 = 16 * (t0 + wave) + 4 * g;
-  const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
-  const uint2 biasq = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, r0 < a.R ? uint32_t(r0) * 2u : kOOB, 0, 0));
-
-  // up to 32 tokens per pass over the weights (registers bound the tile)
-  for (int tg = 0; tg < n_e; tg += 32) {
-    uint32_t boff[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) boff[nt] = act_row_offset(a, PHASE, row_start, tg + nt * 16 + r16, n_e, row_bytes);
-    const int nt_active = min(2, (n_e - tg + 15) >> 4);
-
-    auto pass = [&](auto ntc) __attribute__((always_inline)) {
-      constexpr int NA = decltype(ntc)::value;
-      constexpr int D = NA == 1 ? 3 : 2;  // chunks in flight per wave (3 measured faster than 2 and 4)
-      using St = DecodeStage<ACT, NA>;
-      constexpr int LOADS = 4 + 1 + NA * St::BL;        // VMEM instructions per chunk
-      St st[D];
-      f32x4_t acc[4][NA];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-      // chunk j of this wave is c = wave + 4j; past the wave's last chunk
-      // every load reads zeros
-      auto issue = [&](int j, St& s) __attribute__((always_inline)) {
-        const int c = wave + 4 * j;
-        const bool ok = j < nj;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          s.aq[rt] = buf_load_b128(wb.blk, ok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
-        s.sw = buf_load_b32(wb.sc, ok ? uint32_t((q * nc + c) * 256 + lane * 4) : kOOB);
-        if constexpr (ACT == ACT_BF16) {
-          const uint32_t kofs = (ok && 4 * c + g < nb) ? uint32_t(128 * c + 32 * g) * 2 : kOOB;
-#pragma unroll
-          for (int nt = 0; nt < NA; ++nt)
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) s.bq[nt][s4] = buf_load_b128(bsrc, oob_add(boff[nt], oob_add(kofs, 16u * s4)));
-        } else {
-          // FP8 B: lane group g holds K = 128c + 16g .. +16 and 128c + 64 + 16g .. +16
-          const uint32_t k0 = (ok && 4 * c + (g >> 1) < nb) ? uint32_t(128 * c + 16 * g) : kOOB;
-          const uint32_t k1 = (ok && 4 * c + 2 + (g >> 1) < nb) ? uint32_t(128 * c + 64 + 16 * g) : kOOB;
-#pragma unroll
-          for (int nt = 0; nt < NA; ++nt) {
-            s.bq[nt][0] = buf_load_b128(bsrc, oob_add(boff[nt], k0));
-            s.bq[nt][1] = buf_load_b128(bsrc, oob_add(boff[nt], k1));
-          }
-        }
-      };
-      auto compute = [&](const St& s) __attribute__((always_inline)) {
-        if constexpr (ACT == ACT_BF16) {
-#pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-              const bf16x8_t av = fp4x8_to_bf16x8(dword(s.aq[rt], s4), e8m0_as_scale_operand((s.sw >> (8 * rt)) & 0xFFu));
-#pragma unroll
-              for (int nt = 0; nt < NA; ++nt)
-                acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, s.bq[nt][s4]),
-                                                                      acc[rt][nt], 0, 0, 0);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            const uint4 q4 = s.aq[rt];
-            const i32x8_t av = i32x8_t{int(q4.x), int(q4.y), int(q4.z), int(q4.w), 0, 0, 0, 0};
-#pragma unroll
-            for (int nt = 0; nt < NA; ++nt) {
-              const uint4 p0 = s.bq[nt][0], p1 = s.bq[nt][1];
-              const i32x8_t bv = i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
-              acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[rt][nt], 4, 0, 0,
-                                                                             int((s.sw >> (8 * rt)) & 0xFFu), 0, 127);
-            }
-          }
-        }
-      };
-
-      // prologue: chunks 0 .. D-2 in flight, issued in order
-      order_point();
-      issue(0, st[0]);
-      order_point();
-      if constexpr (D > 2) { issue(1, st[1]); order_point(); }
-      if constexpr (D > 3) { issue(2, st[2]); order_point(); }
-      // iteration j: wait for chunk j (D-2 later chunks may stay in flight),
-      // issue chunk j + D - 1 into the stage chunk j-1 used, compute chunk j
-      auto iteration = [&](int j, auto uc) __attribute__((always_inline)) {
-        constexpr int u = decltype(uc)::value;  // j % D
-        wait_vmcnt<(D - 2) * LOADS>();
-        issue(j + D - 1, st[(u + D - 1) % D]);
-        order_point();
-        compute(st[u]);
-      };
-      int j0 = 0;
-      for (; j0 + D <= nj; j0 += D) {
-        iteration(j0, IC<0>{});
-        iteration(j0 + 1, IC<1>{});
-        if constexpr (D > 2) iteration(j0 + 2, IC<2 % D>{});
-        if constexpr (D > 3) iteration(j0 + 3, IC<3 % D>{});
-      }
-      if (j0 < nj) iteration(j0, IC<0>{});
-      if (j0 + 1 < nj) iteration(j0 + 1, IC<1 % D>{});
-      if constexpr (D > 3) if (j0 + 2 < nj) iteration(j0 + 2, IC<2 % D>{});
-      wait_vmcnt<0>();
-      // Never true (slot counts are non-negative).  It keeps every prefetch
-      // live: the vmcnt waits above count loads, so none may be dropped as
-      // dead even when its chunk lies past the end.
-      if (a.n_slots < 0) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-          x ^= st[d].aq[0].x ^ st[d].aq[1].y ^ st[d].aq[2].z ^ st[d].aq[3].w ^ st[d].sw;
-#pragma unroll
-          for (int nt = 0; nt < NA; ++nt)
-#pragma unroll
-            for (int b = 0; b < St::BL; ++b) x ^= st[d].bq[nt][b].x;
-        }
-        static_cast<uint32_t*>(a.out)[0] = x;
-      }
-
-      // fixed-order sum of the 4 waves' partials, one token sub-tile at a
-      // time; wave w finishes row tile w
-#pragma unroll
-      for (int nt = 0; nt < NA; ++nt) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt][nt];
-        __syncthreads();
-        const int j = tg + nt * 16 + r16;
-        if (j < n_e && r0 < a.R) {
-          f32x4_t sum = red[0][wave][lane];
-          sum += red[1][wave][lane];
-          sum += red[2][wave][lane];
-          sum += red[3][wave][lane];
-          store_rows_biased<ACT, PHASE>(a, r0, row_start + j, sum[0] * a.acc_scale + __uint_as_float(biasq.x << 16),
-                                        sum[1] * a.acc_scale + __uint_as_float(biasq.x & 0xFFFF0000u),
-                                        sum[2] * a.acc_scale + __uint_as_float(biasq.y << 16),
-                                        sum[3] * a.acc_scale + __uint_as_float(biasq.y & 0xFFFF0000u));
-        }
-        __syncthreads();
-      }
-    };
-    if (nt_active == 1)
-      pass(IC<1>{});
-    else
-      pass(IC<2>{});
-  }
+  __shared__ f32x4_t red[kDecodeTileLds / 16];
+  decode_tile<ACT, PHASE>(a, e, blockIdx.x, row_start, n_e, red);
 }
 
 template <int ACT, int PHASE, bool TILED>

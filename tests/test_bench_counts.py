@@ -36,3 +36,14 @@ def test_fp8_mode_activation_bytes():
     c = _case(32, 4, 2880, 2880, 2048, fp8=True)
     w = 5760 * 90 * 17 + 5760 * 2
     assert bench.expert_gemm_bytes(c, 0, 32) == 32 * w + 2048 * 2880 + 2048 * 4 * 2880
+
+
+def test_decode_step_bytes_20b_one_token():
+    """A whole one-token step: the router (32 x 2880 bf16 weights + 32 bf16
+    biases), 4 routed experts of 13,236,480 bytes each (both matrices'
+    nibbles, scales and biases), x in and out (2880 bf16 each)."""
+    c = _case(32, 4, 2880, 2880, 1)
+    expert = 5760 * 90 * 17 + 5760 * 2 + 2880 * 90 * 17 + 2880 * 2
+    assert expert == 13_236_480
+    assert bench.step_bytes(c, 4) == 32 * 2880 * 2 + 32 * 2 + 4 * expert + 2 * 2880 * 2 == 53_141_824
+

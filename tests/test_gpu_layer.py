@@ -291,6 +291,28 @@ def test_deterministic_bits(dev):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_workspace_reused_across_batches(dev):
+    """One workspace through a sequence of forwards of different sizes, decode
+    batches and one larger batch: every output equals that of a fresh
+    workspace, bit for bit (nothing a forward leaves in its workspace may
+    change the next one's result)."""
+    import torch
+    import mxfp4_quantized_moe_amd as mx
+
+    c64 = W.decode_20b(T=64)
+    wts = W.layer_to_torch(c64.layer, dev).tiled()
+    x = W.array_to_torch(c64.x, dev)
+    xl = W.array_to_torch(W.bf16_20b(300).x, dev)
+    ws = mx.alloc_workspace(wts, 300, x.dtype)
+    for T in (1, 64, 8, 300, 3, 64, 1):
+        note(f"reused workspace T={T}")
+        xt = (xl if T > 64 else x)[:T].contiguous()
+        a = mx.moe_mxfp4_forward(wts, xt, workspace=ws)
+        b = mx.moe_mxfp4_forward(wts, xt)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), T
+
+
 def test_decode_prefixes_agree(dev):
     """T=1 and T=8 decode batches are prefixes of T=64; per-token results may
     only differ by the kernel path's rounding, not by routing."""
