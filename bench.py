@@ -46,6 +46,7 @@ METRIC = "MXFP4 MoE layer tokens/s; % HBM roofline (decode), % MFMA peak (prefil
 PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp8_TFLOPs": 5000.0, "int8_TOPs": 5000.0, "fp32_TFLOPs": 157.3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EV_EVERY = 4  # timed steps between two recordings of the dominant stage's events
+GRAPH_STEPS = 20  # forwards captured per HIP graph in the graph launch mode
 KERNEL_SOURCES = ["mxfp4_quantized_moe_amd/csrc/moe_gemm.hip", "mxfp4_quantized_moe_amd/csrc/codec.hip",
                   "mxfp4_quantized_moe_amd/csrc/device_common.h"]
 
@@ -285,17 +286,48 @@ def bench_layer(args, dev):
     # stream time (a few microseconds, a fifth of a one-token step)
     GU = STAGES.index("gate_up_swiglu")
     timed = list(range(0, args.steps, EV_EVERY))
-    ev = {i: HipEvents(STAGE_EVENTS, only=(GU, GU + 1)) for i in timed}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        plans[i % copies](stage_events=ev[i].arr if i in ev else None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gu_ms = np.array([e.elapsed_ms(GU, GU + 1) for e in ev.values()])
-    for e in ev.values():
-        e.close()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    def run_steps(launch: str):
+        """K timed forwards; returns (seconds, gate_up ms of the recorded
+        steps).  graph: the forwards are captured GRAPH_STEPS at a time into
+        HIP graphs before the clock starts and the timed region replays the
+        graphs, so the host's per-launch cost leaves the measurement (events
+        recorded inside a graph give no elapsed times, so none are);
+        eager: one library call per forward, with the gate_up events."""
+        ev = {i: HipEvents(STAGE_EVENTS, only=(GU, GU + 1)) for i in timed} if launch == "eager" else {}
+        graphs = []
+        if launch == "graph":
+            cs = torch.cuda.Stream()
+            for g0 in range(0, args.steps, GRAPH_STEPS):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    for i in range(g0, min(args.steps, g0 + GRAPH_STEPS)):
+                        plans[i % copies](stage_events=ev[i].arr if i in ev else None)
+                graphs.append(g)
+            for g in graphs[:1]:  # one untimed replay (first-launch set-up of the graph)
+                g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if launch == "graph":
+            for g in graphs:
+                g.replay()
+        else:
+            for i in range(args.steps):
+                plans[i % copies](stage_events=ev[i].arr if i in ev else None)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gu = np.array([e.elapsed_ms(GU, GU + 1) for e in ev.values()])
+        for e in ev.values():
+            e.close()
+        del graphs
+        return t1 - t0, gu
+
+    # the eager steps time the dominant kernel; in the graph mode the
+    # graph replays then give the throughput
+    te, gu_ms = run_steps("eager")
+    eager = {"value": T * args.steps / te, "ms_per_step": te * 1e3 / args.steps}
+    dt = run_steps("graph")[0] if args.launch == "graph" else te
+    ms_step = dt * 1e3 / args.steps
 
     # per-stage breakdown from a separate, untimed pass with every event
     nb = min(args.steps, 10)
@@ -324,12 +356,12 @@ def bench_layer(args, dev):
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
         algo = f"{fl} flop per launch"
     roof["kernel"] = gate_up_kernel_name(case, decode_shaped, args.layout == "tiled")
-    roof["launches_timed"] = f"{len(gu_ms)} of the {args.steps} timed steps (every {EV_EVERY}th)"
+    roof["launches_timed"] = f"{len(gu_ms)} of the {args.steps} timed eager steps (every {EV_EVERY}th)"
     roof["algorithmic"] = algo
     roof["traffic"] = measured_traffic(args.workload, roof["kernel"]) if not dense else None
     res = {
         "metric": METRIC,
-        "value": T * args.steps / (t1 - t0),
+        "value": T * args.steps / dt,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -344,11 +376,15 @@ def bench_layer(args, dev):
                    "act": "fp8" if case.fp8 else case.act_dtype, "weight_layout": args.layout,
                    "weight_copies": copies,
                    "expert_path": args.path,
-                   "routed_experts": n_active},
+                   "routed_experts": n_active,
+                   "launch": (f"hip_graph ({GRAPH_STEPS} forwards per graph)" if args.launch == "graph"
+                              else "eager (one library call per forward)")},
         "roofline": roof,
         "stages_us": {name: float(v * 1e3) for name, v in zip(STAGES, avg)},
         "stages_note": "separate untimed pass with all stage events (each record adds a few us)",
     }
+    if args.launch == "graph":
+        res["eager"] = eager
     if decode_shaped and not dense:
         # the whole step against HBM: its algorithmic bytes over the wall
         # time per step (launch gaps and the small stages included)
@@ -572,11 +608,12 @@ def bench_int8(args, dev):
 
 def gate_up_kernel_name(case, decode_shaped: bool, tiled: bool) -> str:
     """The gate_up kernel the library launches for this case, as rocprofv3
-    names it (template arguments: activation code, phase[, tiled])."""
+    names it (template arguments: activation code, phase, then token
+    sub-tiles per pass (decode, tiled) or tiled (row order))."""
     act = 2 if case.fp8 else (1 if case.act_dtype == "bf16" else 0)
     if decode_shaped:
         if tiled and act != 0:
-            return f"mxmoe::gemm_decode_tiled_kernel<{act}, 0>"
+            return f"mxmoe::gemm_decode_tiled_kernel<{act}, 0, {1 if case.T <= 16 else 2}>"
         return f"mxmoe::gemm_decode_kernel<{act}, 0, {'true' if tiled else 'false'}>"
     if tiled:
         return f"mxmoe::gemm_prefill_tiled_kernel<{act}, 0>"
@@ -608,6 +645,8 @@ def main():
                     help="expert weight order: tiled by mxfp4_tile at load (default) or the checkpoint row order")
     ap.add_argument("--path", choices=("routed", "dense"), default="routed",
                     help="experts per token: the routed top_k, or all of them (dense all-experts path)")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="forwards replayed from HIP graphs (default) or one library call each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     args = ap.parse_args()

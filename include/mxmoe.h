@@ -285,7 +285,9 @@ typedef struct {
    * each record takes a few microseconds of stream time, so a caller timing
    * one stage passes only the two handles around it.  A batch of at most 16
    * tokens runs router and grouping as one launch unless event 1 (between
-   * them) is given. */
+   * them) is given.  A decode-shaped batch of at most 64 tokens on tiled
+   * weights (bf16 or FP8 activations) forms the combine inside the down
+   * launch: its combine stage is empty. */
   void* const* stage_events;
   int32_t expert_path;   /* mxmoe_path_t: which experts each token passes through */
 } mxmoe_fwd_opts_t;

@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Workspace {
-  size_t idx, wts, counts, offsets, active, tile_off, tiles, sorted, sorted_tok, pos, calib, xq, h, y, total;
+  size_t idx, wts, counts, offsets, active, tile_off, tiles, sorted, sorted_tok, pos, cmb, calib, xq, h, y, total;
 };
 
 // Rows of the two GEMMs: the T*k routed (token, expert) pairs, or all T*E
@@ -55,13 +55,14 @@ Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8,
   w.wts = take(slots * 4);
   w.counts = take(size_t(E) * 4);
   w.offsets = take(size_t(E + 1) * 4);
-  w.active = take(size_t(E + 1) * 4);
+  w.active = take(size_t(E + 1) * 16);
   w.tile_off = take(size_t(E + 1) * 4);
   const size_t active_max = grows < size_t(E) ? grows : size_t(E);
   w.tiles = take((grows + kPrefillTokens - 1) / kPrefillTokens * 16 + active_max * 16);
   w.sorted = take(slots * 4);
   w.sorted_tok = take(grows * 4);
   w.pos = take(slots * 4);
+  w.cmb = take(size_t((H + 63) / 64) * 4);  // arrival counters of the folded combine
   w.calib = take(16);
   w.xq = take(fp8 ? size_t(T) * size_t(H) : 0);
   const size_t hb = fp8 ? 1 : (act_dtype == MXMOE_BF16 ? 2 : 4);
@@ -165,7 +166,7 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
     da.offsets = at<int32_t>(ws, w.offsets);
     da.sorted_tok = at<int32_t>(ws, w.sorted_tok);
     da.pos = at<int32_t>(ws, w.pos);
-    da.active = at<int32_t>(ws, w.active);
+    da.active = at<int4>(ws, w.active);
     da.tile_off = at<int32_t>(ws, w.tile_off);
     da.tiles = at<int4>(ws, w.tiles);
     return launch_dense_group(da, s);
@@ -180,7 +181,7 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   pa.pos = pos_buf ? pos_buf : at<int32_t>(ws, w.pos);
   pa.sorted_tok = at<int32_t>(ws, w.sorted_tok);
   pa.top_k = L->top_k;
-  pa.active = at<int32_t>(ws, w.active);
+  pa.active = at<int4>(ws, w.active);
   pa.tile_off = at<int32_t>(ws, w.tile_off);
   pa.tiles = at<int4>(ws, w.tiles);
   pa.counts_out = counts_out;
@@ -205,7 +206,7 @@ GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t
   g.sorted = at<int32_t>(ws, w.sorted);
   g.sorted_tok = at<int32_t>(ws, w.sorted_tok);
   g.offsets = at<int32_t>(ws, w.offsets);
-  g.active = at<int32_t>(ws, w.active);
+  g.active = at<int4>(ws, w.active);
   g.tile_off = at<int32_t>(ws, w.tile_off);
   g.tiles = at<int4>(ws, w.tiles);
   const int64_t slots = gemm_rows(L, T, dense);
@@ -214,6 +215,7 @@ GemmArgs gemm_args(const mxmoe_layer_t* L, const Workspace& w, void* ws, int64_t
   g.max_tiles = int((slots + kPrefillTokens - 1) / kPrefillTokens + g.max_active);
   g.acc_scale = 1.0f;
   g.out_inv_scale = 1.0f;
+  g.T = int(T);
   g.tiled = L->weight_layout == MXMOE_LAYOUT_TILED;
   if (phase == 0) {
     g.wblk = L->gate_up_blocks;
@@ -277,18 +279,30 @@ mxmoe_status_t forward_impl(const mxmoe_layer_t* L, const void* x, int64_t T, vo
   }
   if (mark(3) != hipSuccess) return MXMOE_ERR_HIP;
   const bool prefill = use_prefill(L, T, act, dense);
+  // decode-shaped batches on the tiled decode kernels fold the combine
+  // into the down GEMM (Y read back through a 32-bit buffer window)
+  const bool fold = !prefill && L->weight_layout == MXMOE_LAYOUT_TILED && act != ACT_F32 && T <= kFusedCombineTokens &&
+                    gemm_rows(L, T, dense) * L->H * 2 <= kMaxWindow;
   GemmArgs g0 = gemm_args(L, w, ws, T, act, 0, dense);
   g0.bsrc = fp8 ? at<void>(ws, w.xq) : x;
   if (fp8) {
     g0.acc_scale = o->x_scale;
     g0.out_inv_scale = inv_h;
   }
-  if ((e = launch_moe_gemm(g0, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
-  if (mark(4) != hipSuccess) return MXMOE_ERR_HIP;
   GemmArgs g1 = gemm_args(L, w, ws, T, act, 1, dense);
   if (fp8) g1.acc_scale = o->h_scale;
+  if (fold) {
+    g0.cmb_count = g1.cmb_count = at<uint32_t>(ws, w.cmb);
+    g0.n_cmb = g1.n_cmb = (L->H + 63) / 64;
+    g1.cmb_out = out;
+    g1.pos = at<int32_t>(ws, w.pos);
+    g1.wts = at<float>(ws, w.wts);
+  }
+  if ((e = launch_moe_gemm(g0, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
+  if (mark(4) != hipSuccess) return MXMOE_ERR_HIP;
   if ((e = launch_moe_gemm(g1, prefill, s)) != hipSuccess) return MXMOE_ERR_HIP;
   if (mark(5) != hipSuccess) return MXMOE_ERR_HIP;
+  if (fold) return hip_status(mark(6));
   CombineArgs ca{};
   ca.Y = at<void>(ws, w.y);
   ca.y_bf16 = act != ACT_F32;
@@ -450,7 +464,7 @@ LinearWorkspace linear_layout(int64_t T, int64_t N, int act_dtype) {
     return at;
   };
   w.offsets = take(2 * 4);
-  w.active = take(2 * 4);
+  w.active = take(2 * 16);
   w.tile_off = take(2 * 4);
   w.tiles = take(size_t((T + kPrefillTokens - 1) / kPrefillTokens) * 16 + 16);
   w.bias = take(size_t(N) * (act_dtype == MXMOE_BF16 ? 2 : 4));
@@ -495,7 +509,7 @@ mxmoe_status_t mxfp4_linear(const void* x, int64_t T, int64_t K, const uint8_t* 
   if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ebytes = act_dtype == MXMOE_BF16 ? 2 : 4;
-  if (launch_linear_setup(int(T), at<int32_t>(ws, w.offsets), at<int32_t>(ws, w.active), at<int32_t>(ws, w.tile_off),
+  if (launch_linear_setup(int(T), at<int32_t>(ws, w.offsets), at<int4>(ws, w.active), at<int32_t>(ws, w.tile_off),
                           at<int4>(ws, w.tiles), bias ? nullptr : at<void>(ws, w.bias), int(N), ebytes, s) != hipSuccess)
     return MXMOE_ERR_HIP;
   // the down-projection epilogue of the grouped GEMM (bias added, no
@@ -514,8 +528,9 @@ mxmoe_status_t mxfp4_linear(const void* x, int64_t T, int64_t K, const uint8_t* 
   g.E = 1;
   g.bsrc = x;
   g.b_rows = T;
+  g.T = int(T);
   g.offsets = at<int32_t>(ws, w.offsets);
-  g.active = at<int32_t>(ws, w.active);
+  g.active = at<int4>(ws, w.active);
   g.tile_off = at<int32_t>(ws, w.tile_off);
   g.tiles = at<int4>(ws, w.tiles);
   g.out = out;
@@ -549,7 +564,7 @@ Fp8LinearWorkspace fp8_linear_layout(int64_t T, int64_t K, int64_t N) {
     return at;
   };
   w.offsets = take(2 * 4);
-  w.active = take(2 * 4);
+  w.active = take(2 * 16);
   w.tile_off = take(2 * 4);
   w.tiles = take(size_t((T + kPrefillTokens - 1) / kPrefillTokens) * 16 + 16);
   w.bias = take(size_t(N) * 2);
@@ -606,7 +621,7 @@ mxmoe_status_t fp8_linear(const void* x, int64_t T, int64_t K, const uint8_t* w_
   const Fp8LinearWorkspace w = fp8_linear_layout(T, K, N);
   if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_linear_setup(int(T), at<int32_t>(ws, w.offsets), at<int32_t>(ws, w.active), at<int32_t>(ws, w.tile_off),
+  if (launch_linear_setup(int(T), at<int32_t>(ws, w.offsets), at<int4>(ws, w.active), at<int32_t>(ws, w.tile_off),
                           at<int4>(ws, w.tiles), bias ? nullptr : at<void>(ws, w.bias), int(N), 2, s) != hipSuccess)
     return MXMOE_ERR_HIP;
   // x -> e4m3 codes with the static input scale (the MoE FP8 mode's rule)
@@ -627,8 +642,9 @@ mxmoe_status_t fp8_linear(const void* x, int64_t T, int64_t K, const uint8_t* w_
   g.E = 1;
   g.bsrc = at<void>(ws, w.xq);
   g.b_rows = T;
+  g.T = int(T);
   g.offsets = at<int32_t>(ws, w.offsets);
-  g.active = at<int32_t>(ws, w.active);
+  g.active = at<int4>(ws, w.active);
   g.tile_off = at<int32_t>(ws, w.tile_off);
   g.tiles = at<int4>(ws, w.tiles);
   g.out = out;

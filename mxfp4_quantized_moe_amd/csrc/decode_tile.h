@@ -30,11 +30,15 @@ struct DecodeStage {
 constexpr int kDecodeTileLds = 4 * 4 * 64 * 16;
 
 // Tile (expert e, row group q) for the n_e tokens in sorted rows row_start
-// .. row_start + n_e - 1.  red: kDecodeTileLds bytes of LDS.
-template <int ACT, int PHASE>
+// .. row_start + n_e - 1.  red: kDecodeTileLds bytes of LDS.  MAXNA: token
+// sub-tiles of 16 per pass (1 or 2); batches of at most 16 tokens (no
+// expert sees more) take 1, which keeps the 32-token pass and its
+// registers out of the kernel.
+template <int ACT, int PHASE, int MAXNA>
 __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int row_start, int n_e,
                                             f32x4_t* red_lds) {
   static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "bf16 or fp8 activations");
+  static_assert(MAXNA == 1 || MAXNA == 2, "one or two token sub-tiles per pass");
   // [wave][row tile][lane] of one token sub-tile
   f32x4_t (*red)[4][64] = reinterpret_cast<f32x4_t (*)[4][64]>(red_lds);
   const int lane = threadIdx.x & 63;
@@ -54,19 +58,27 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
   const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
   const uint2 biasq = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, r0 < a.R ? uint32_t(r0) * 2u : kOOB, 0, 0));
 
-  // up to 32 tokens per pass over the weights (registers bound the tile)
-  for (int tg = 0; tg < n_e; tg += 32) {
-    uint32_t boff[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      boff[nt] = act_row_offset(a, PHASE, row_start, tg + nt * 16 + r16, n_e, row_bytes);
-    const int nt_active = min(2, (n_e - tg + 15) >> 4);
+  // up to 16 * MAXNA tokens per pass over the weights (registers bound
+  // the tile)
+  for (int tg = 0; tg < n_e; tg += 16 * MAXNA) {
+    const int nt_active = min(MAXNA, (n_e - tg + 15) >> 4);
 
     auto pass = [&](auto ntc) __attribute__((always_inline)) {
       constexpr int NA = decltype(ntc)::value;
       constexpr int D = NA == 1 ? 3 : 2;  // chunks in flight per wave (3 measured faster than 2 and 4)
+      static_assert(D == 2 || D == 3, "ring of 2 or 3 chunks");
       using St = DecodeStage<ACT, NA>;
       constexpr int LOADS = 4 + 1 + NA * St::BL;        // VMEM instructions per chunk
+      // token rows of the pass: gate_up gathers x rows through the token
+      // table (its loads go out first, see the prologue), down reads h in
+      // sorted order
+      int src[NA];
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt) {
+        const int p = row_start + min(tg + nt * 16 + r16, n_e - 1);
+        src[nt] = PHASE == 0 ? a.sorted_tok[p] : p;
+      }
+      uint32_t boff[NA];
       St st[D];
       f32x4_t acc[4][NA];
 #pragma unroll
@@ -75,30 +87,45 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
         for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
       // chunk j of this wave is c = wave + 4j; past the wave's last chunk
-      // every load reads zeros
-      auto issue = [&](int j, St& s) __attribute__((always_inline)) {
+      // every load reads zeros.  issue_a: its weights and scales; issue_b:
+      // its token fragments.
+      // The chunk's offsets are split into a per-lane part and a
+      // wave-uniform part (chunk and row-tile strides, in scalar registers).
+      auto issue_a = [&](int j, St& s) __attribute__((always_inline)) {
         const int c = wave + 4 * j;
         const bool ok = j < nj;
+        const uint32_t va = ok ? aslot : kOOB;
+        const uint32_t sa = ok ? uint32_t((t0 * nc + c) * 1024) : 0u;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          s.aq[rt] = buf_load_b128(wb.blk, ok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
-        s.sw = buf_load_b32(wb.sc, ok ? uint32_t((q * nc + c) * 256 + lane * 4) : kOOB);
+        for (int rt = 0; rt < 4; ++rt) s.aq[rt] = buf_load_b128(wb.blk, va, sa + uint32_t(rt * nc * 1024));
+        s.sw = buf_load_b32(wb.sc, ok ? uint32_t(lane * 4) : kOOB, ok ? uint32_t((q * nc + c) * 256) : 0u);
+      };
+      auto issue_b = [&](int j, St& s) __attribute__((always_inline)) {
+        const int c = wave + 4 * j;
+        const bool ok = j < nj;
+        const uint32_t sb = ok ? uint32_t(128 * c) * EB : 0u;
         if constexpr (ACT == ACT_BF16) {
-          const uint32_t kofs = (ok && 4 * c + g < nb) ? uint32_t(128 * c + 32 * g) * 2 : kOOB;
-#pragma unroll
-          for (int nt = 0; nt < NA; ++nt)
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) s.bq[nt][s4] = buf_load_b128(bsrc, oob_add(boff[nt], oob_add(kofs, 16u * s4)));
-        } else {
-          // FP8 B: lane group g holds K = 128c + 16g .. +16 and 128c + 64 + 16g .. +16
-          const uint32_t k0 = (ok && 4 * c + (g >> 1) < nb) ? uint32_t(128 * c + 16 * g) * EB : kOOB;
-          const uint32_t k1 = (ok && 4 * c + 2 + (g >> 1) < nb) ? uint32_t(128 * c + 64 + 16 * g) * EB : kOOB;
+          // lane group g holds K = 128c + 32g .. +32 (4 loads of 8 values)
+          const bool okg = ok && 4 * c + g < nb;
 #pragma unroll
           for (int nt = 0; nt < NA; ++nt) {
-            s.bq[nt][0] = buf_load_b128(bsrc, oob_add(boff[nt], k0));
-            s.bq[nt][1] = buf_load_b128(bsrc, oob_add(boff[nt], k1));
+            const uint32_t vb = okg ? oob_add(boff[nt], 64u * g) : kOOB;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) s.bq[nt][s4] = buf_load_b128(bsrc, vb + 16u * s4, sb);
+          }
+        } else {
+          // FP8 B: lane group g holds K = 128c + 16g .. +16 and 128c + 64 + 16g .. +16
+          const bool ok0 = ok && 4 * c + (g >> 1) < nb, ok1 = ok && 4 * c + 2 + (g >> 1) < nb;
+#pragma unroll
+          for (int nt = 0; nt < NA; ++nt) {
+            s.bq[nt][0] = buf_load_b128(bsrc, ok0 ? oob_add(boff[nt], 16u * g * EB) : kOOB, sb);
+            s.bq[nt][1] = buf_load_b128(bsrc, ok1 ? oob_add(boff[nt], (64u + 16u * g) * EB) : kOOB, sb);
           }
         }
+      };
+      auto issue = [&](int j, St& s) __attribute__((always_inline)) {
+        issue_a(j, s);
+        issue_b(j, s);
       };
       auto compute = [&](const St& s) __attribute__((always_inline)) {
         if constexpr (ACT == ACT_BF16) {
@@ -132,17 +159,35 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
         }
       };
 
-      // prologue: chunks 0 .. D-2 in flight, issued in order
+      // Prologue: the token ids (gate_up) are the oldest loads, then the
+      // weights of chunks 0 .. D-2, whose streaming need not wait for the
+      // ids; the token fragments of those chunks follow once the ids are
+      // in.  Queue: ids, A0 .. A(D-2), B0 .. B(D-2).
       order_point();
-      issue(0, st[0]);
+      issue_a(0, st[0]);
       order_point();
-      if constexpr (D > 2) { issue(1, st[1]); order_point(); }
-      if constexpr (D > 3) { issue(2, st[2]); order_point(); }
+      if constexpr (D > 2) { issue_a(1, st[1]); order_point(); }
+      __builtin_amdgcn_sched_barrier(0);  // nothing that needs the ids moves above the weight loads
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt) hold(src[nt]);
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt) boff[nt] = tg + nt * 16 + r16 < n_e ? uint32_t(src[nt]) * row_bytes : kOOB;
+      issue_b(0, st[0]);
+      order_point();
+      if constexpr (D > 2) { issue_b(1, st[1]); order_point(); }
       // iteration j: wait for chunk j (D-2 later chunks may stay in flight),
-      // issue chunk j + D - 1 into the stage chunk j-1 used, compute chunk j
+      // issue chunk j + D - 1 into the stage chunk j-1 used, compute chunk
+      // j.  Chunk 0 is complete once only the token fragments of chunks 1 ..
+      // D-2 are outstanding; from chunk 1 on the loads of every chunk were
+      // issued together.
       auto iteration = [&](int j, auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;  // j % D
-        wait_vmcnt<(D - 2) * LOADS>();
+        if constexpr (u == 0) {
+          if (j == 0) wait_vmcnt<(D - 2) * NA * St::BL>();
+          else wait_vmcnt<(D - 2) * LOADS>();
+        } else {
+          wait_vmcnt<(D - 2) * LOADS>();
+        }
         issue(j + D - 1, st[(u + D - 1) % D]);
         order_point();
         compute(st[u]);
@@ -151,12 +196,10 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
       for (; j0 + D <= nj; j0 += D) {
         iteration(j0, IC<0>{});
         iteration(j0 + 1, IC<1>{});
-        if constexpr (D > 2) iteration(j0 + 2, IC<2 % D>{});
-        if constexpr (D > 3) iteration(j0 + 3, IC<3 % D>{});
+        if constexpr (D > 2) iteration(j0 + 2, IC<2>{});
       }
       if (j0 < nj) iteration(j0, IC<0>{});
-      if (j0 + 1 < nj) iteration(j0 + 1, IC<1 % D>{});
-      if constexpr (D > 3) if (j0 + 2 < nj) iteration(j0 + 2, IC<2 % D>{});
+      if constexpr (D > 2) if (j0 + 1 < nj) iteration(j0 + 1, IC<1>{});
       wait_vmcnt<0>();
       // Never true (slot counts are non-negative).  It keeps every prefetch
       // live: the vmcnt waits above count loads, so none may be dropped as
@@ -175,7 +218,12 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
       }
 
       // fixed-order sum of the 4 waves' partials, one token sub-tile at a
-      // time; wave w finishes row tile w
+      // time; wave w finishes row tile w.  The bias is unpacked only here
+      // (hoisted to the top, its unpacking would wait for its load before
+      // the first weight load went out).
+      uint32_t bx = biasq.x, by = biasq.y;
+      hold(bx);
+      hold(by);
 #pragma unroll
       for (int nt = 0; nt < NA; ++nt) {
 #pragma unroll
@@ -187,18 +235,26 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
           sum += red[1][wave][lane];
           sum += red[2][wave][lane];
           sum += red[3][wave][lane];
-          store_rows_biased<ACT, PHASE>(a, r0, row_start + j, sum[0] * a.acc_scale + __uint_as_float(biasq.x << 16),
-                                             sum[1] * a.acc_scale + __uint_as_float(biasq.x & 0xFFFF0000u),
-                                             sum[2] * a.acc_scale + __uint_as_float(biasq.y << 16),
-                                             sum[3] * a.acc_scale + __uint_as_float(biasq.y & 0xFFFF0000u));
+          const float v0 = sum[0] * a.acc_scale + __uint_as_float(bx << 16);
+          const float v1 = sum[1] * a.acc_scale + __uint_as_float(bx & 0xFFFF0000u);
+          const float v2 = sum[2] * a.acc_scale + __uint_as_float(by << 16);
+          const float v3 = sum[3] * a.acc_scale + __uint_as_float(by & 0xFFFF0000u);
+          if (PHASE == 1 && a.cmb_out) {
+            // Y rows for the folded combine: read by another workgroup
+            const rsrc_t ys = make_rsrc(a.out, uint32_t(a.n_slots) * uint32_t(a.R) * 2u);
+            buf_store_dev_b64(ys, uint32_t((int64_t(row_start + j) * a.R + r0) * 2),
+                              make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
+          } else {
+            store_rows_biased<ACT, PHASE>(a, r0, row_start + j, v0, v1, v2, v3);
+          }
         }
         __syncthreads();
       }
     };
-    if (nt_active == 1)
+    if (MAXNA == 1 || nt_active == 1)
       pass(IC<1>{});
     else
-      pass(IC<2>{});
+      pass(IC<MAXNA>{});
   }
 }
 

@@ -12,6 +12,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Largest top_k the kernels handle (the ABI limit).
 constexpr int MAX_TOPK_DEV = 8;
@@ -21,6 +22,17 @@ constexpr int MAX_TOPK_DEV = 8;
 // of loads is in flight together, and from moving a load across an explicit
 // vmcnt wait that counts the loads of one pipeline stage.
 __device__ __forceinline__ void order_point() { __asm__ __volatile__("" ::: "memory"); }
+
+// A value the compiler must treat as produced at this point: its uses (and
+// the wait for the load that produced it) stay below it.  Keeps address
+// arithmetic from being hoisted above loads that should go out first.
+__device__ __forceinline__ void hold(uint32_t& v) { __asm__ __volatile__("" : "+v"(v)); }
+__device__ __forceinline__ void hold(int& v) { __asm__ __volatile__("" : "+v"(v)); }
+// All fields of a wave-uniform record in registers here (one load, before
+// any branch on one of them).
+__device__ __forceinline__ void hold_uniform(const int4& r) {
+  __asm__ __volatile__("" ::"s"(r.x), "s"(r.y), "s"(r.z), "s"(r.w));
+}
 
 // s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their maxima)
 template <int N>
@@ -116,6 +128,48 @@ __device__ __forceinline__ uint4 buf_load_b128(rsrc_t r, uint32_t off) {
 
 __device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Offset split into a per-lane part (voff, a VGPR) and a wave-uniform part
+// (soff, an SGPR): the address arithmetic shared by the wave stays in
+// scalar registers.  Range checking: a voff of kOOB (plus any small
+// constant) reads zeros whatever soff is; otherwise voff + soff must lie
+// inside the buffer.
+__device__ __forceinline__ uint4 buf_load_b128(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// ------------------------------------------- device-scope hand-off
+//
+// Rows that one workgroup hands to another workgroup of the same launch
+// (which may run on another XCD, behind another L2) are stored and loaded
+// at device scope: stores with the sc1 cache policy write through to the
+// device's point of coherence, and loads with sc1 read from it, so a reader
+// never sees a line its own L2 kept from earlier.  The producer waits for
+// its stores (vmcnt 0) before it signals through a device-scope atomic
+// counter; the consumer issues its loads only after it has read the
+// signal.  (Plain stores would need a write-back of the producer's L2 and
+// an invalidate of the consumer's.)
+
+constexpr int kAuxDev = 16;  // cache-policy operand of buffer loads / stores: sc1
+
+__device__ __forceinline__ void buf_store_dev_b64(rsrc_t r, uint32_t off, uint2 v) {
+  const u32x2_t w = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kAuxDev);
+}
+
+__device__ __forceinline__ uint4 buf_load_dev_b128(rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxDev);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t add_dev(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------- misc

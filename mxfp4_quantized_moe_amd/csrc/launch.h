@@ -46,7 +46,10 @@ struct PermuteArgs {
   int32_t* sorted_tok;  // (T*k): token id (slot / top_k) of each sorted row
   int top_k;
   int32_t* pos;         // (T*k)
-  int32_t* active;      // (E + 1): active[0] = count, active[1..] = expert ids ascending
+  int4* active;         // (E + 1) slot records: active[0].x = number of active experts;
+                        // active[1 + i] = {expert, first sorted row, rows, number of active
+                        // experts} of the i-th active expert, ids ascending, and {0, 0, 0, 0} for the slots
+                        // past them up to min(E, n_slots) (the decode grids' bound)
   int32_t* tile_off;    // (E+1): prefix of ceil(count / kPrefillTokens)
   int4* tiles;          // (tile_off[E]): {expert, first sorted row, tokens, 0} per prefill tile
   int32_t* counts_out;  // optional copies
@@ -80,7 +83,7 @@ struct DenseGroupArgs {
   int32_t* offsets;     // (E+1)
   int32_t* sorted_tok;  // (T*E)
   int32_t* pos;         // (T*k)
-  int32_t* active;      // (E+1)
+  int4* active;         // (E+1) slot records (as PermuteArgs::active)
   int32_t* tile_off;    // (E+1)
   int4* tiles;          // (E * ceil(T / kPrefillTokens))
 };
@@ -110,7 +113,7 @@ struct GemmArgs {
   const int32_t* sorted;      // (T*k) flat slot ids in expert order
   const int32_t* sorted_tok;  // (T*k) their token ids
   const int32_t* offsets;     // (E+1)
-  const int32_t* active;      // (E+1)
+  const int4* active;         // (E+1) slot records (as PermuteArgs::active)
   const int32_t* tile_off;    // (E+1)
   const int4* tiles;          // prefill tile table
   void* out;                  // phase 0: h (T*k, R/2) act storage; phase 1: Y (T*k, R), fp32 or bf16 (act != fp32)
@@ -121,13 +124,26 @@ struct GemmArgs {
   int n_slots;                // T*k
   const float* row_scale;     // ACT_INT8: (E, R) weight scale per output row
   const float* tok_scale;     // ACT_INT8: activation scale per token (phase 0, by token id) or per row (phase 1)
+  // Combine folded into the decode-shaped down GEMM (tiled weights, bf16 or
+  // FP8 activations, at most kFusedCombineTokens tokens): the last of the
+  // active experts' workgroups to finish a 64-row group of Y forms the
+  // output rows of that group.  cmb_count: one arrival counter per row
+  // group (n_cmb of them), cleared by the gate_up launch (which then needs
+  // only cmb_count and n_cmb) and counted by the down launch.
+  uint32_t* cmb_count;
+  int n_cmb;
+  void* cmb_out;              // down: (T, R) bf16 output; null = Y is left for combine_kernel
+  const int32_t* pos;         // down: (T*k) sorted row of each routed slot
+  const float* wts;           // down: (T, k) routing weights
+  int T;                      // tokens of the batch (no expert sees more)
 };
+constexpr int kFusedCombineTokens = 64;
 hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream);
 
 // The routing tables of a dense layer seen as one expert with all T tokens
 // (offsets, active list, prefill tiles) and, if zero_bias is set, N zero
 // bias values of zero_bias_bytes each.
-hipError_t launch_linear_setup(int T, int32_t* offsets, int32_t* active, int32_t* tile_off, int4* tiles,
+hipError_t launch_linear_setup(int T, int32_t* offsets, int4* active, int32_t* tile_off, int4* tiles,
                                void* zero_bias, int N, int zero_bias_bytes, hipStream_t stream);
 
 struct CombineArgs {

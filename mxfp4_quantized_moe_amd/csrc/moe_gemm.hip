@@ -67,10 +67,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int slot = blockIdx.y;
-  if (slot >= a.active[0]) return;
-  const int e = a.active[1 + slot];
-  const int row_start = a.offsets[e];
-  const int n_e = a.offsets[e + 1] - row_start;
+  // one round trip: slots past the active experts hold empty records
+  const int4 rec = a.active[1 + slot];
+  hold_uniform(rec);
+  if (rec.z == 0) return;
+  const int e = rec.x, row_start = rec.y, n_e = rec.z;
   const int nb = a.nb, K = nb * 32;
   const int nchunks = (nb + 3) >> 2;
   const int rbase = blockIdx.x * (16 * RT);
@@ -1010,18 +1011,78 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   }
 }
 
+// The folded combine of row group q (64 rows of H) once every active
+// expert's Y rows of the group are in: out[t] = sum_j w[t, j] * Y[pos[t, j]]
+// over j = 0 .. k-1 in that order, in fp32 (the arithmetic of
+// combine_kernel), for all T tokens; 8 threads per token, 8 columns each.
+__device__ void combine_group(const GemmArgs& a, int q) {
+  const int H = a.R, k = a.top_k;
+  const int c0 = 64 * q;
+  const rsrc_t ys = make_rsrc(a.out, uint32_t(a.n_slots) * uint32_t(H) * 2u);
+  for (int i = threadIdx.x; i < a.T * 8; i += blockDim.x) {
+    const int t = i >> 3, c = c0 + 8 * (i & 7);
+    if (c >= H) continue;
+    int64_t row[MAX_TOPK_DEV];
+    float w[MAX_TOPK_DEV];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK_DEV; ++j) {
+      row[j] = j < k ? a.pos[int64_t(t) * k + j] : 0;
+      w[j] = j < k ? a.wts[int64_t(t) * k + j] : 0.f;
+    }
+    uint4 y[MAX_TOPK_DEV];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK_DEV; ++j)
+      y[j] = j < k ? buf_load_dev_b128(ys, uint32_t((row[j] * H + c) * 2)) : make_uint4(0, 0, 0, 0);
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK_DEV; ++j) {
+      if (j < k) {
+        const uint32_t yw[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          s[2 * m] += w[j] * __uint_as_float(yw[m] << 16);
+          s[2 * m + 1] += w[j] * __uint_as_float(yw[m] & 0xFFFF0000u);
+        }
+      }
+    }
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.cmb_out) + int64_t(t) * H + c) =
+        make_uint4(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7]));
+  }
+}
+
 // Decode-shaped GEMM on the tiled weight order (bf16 and FP8 activations):
 // one workgroup per (64-row group, active expert slot); the tile itself is
-// decode_tile (decode_tile.h).
-template <int ACT, int PHASE>
+// decode_tile (decode_tile.h).  With the combine folded in (cmb_out set),
+// the gate_up launch clears the arrival counters and each down workgroup
+// signals its row group once its Y rows are stored; the last of the
+// group's rec.w workgroups forms the output rows.
+// Batches up to this many tokens run the decode tile with one 16-token
+// sub-tile per pass (fewer registers, more waves per SIMD); an expert with
+// more tokens then takes several passes over its weights (sweep knob).
+#ifndef MXMOE_DECODE_ONE_SUBTILE
+#define MXMOE_DECODE_ONE_SUBTILE 16
+#endif
+constexpr int kDecodeOneSubtile = MXMOE_DECODE_ONE_SUBTILE;
+
+template <int ACT, int PHASE, int MAXNA>
 __global__ __launch_bounds__(256, 2) void gemm_decode_tiled_kernel(GemmArgs a) {
   const int slot = blockIdx.y;
-  if (slot >= a.active[0]) return;
-  const int e = a.active[1 + slot];
-  const int row_start = a.offsets[e];
-  const int n_e = a.offsets[e + 1] - row_start;
+  if (PHASE == 0 && a.cmb_count && slot == 0 && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.n_cmb; i += blockDim.x) a.cmb_count[i] = 0;
+  // one round trip: slots past the active experts hold empty records
+  const int4 rec = a.active[1 + slot];
+  hold_uniform(rec);
+  if (rec.z == 0) return;
   __shared__ f32x4_t red[kDecodeTileLds / 16];
-  decode_tile<ACT, PHASE>(a, e, blockIdx.x, row_start, n_e, red);
+  decode_tile<ACT, PHASE, MAXNA>(a, rec.x, blockIdx.x, rec.y, rec.z, red);
+  if (PHASE == 1 && a.cmb_out) {
+    __shared__ int last;
+    wait_vmcnt<0>();  // this wave's Y stores have reached the point of coherence
+    __syncthreads();
+    if (threadIdx.x == 0) last = add_dev(a.cmb_count + blockIdx.x, 1u) == uint32_t(rec.w - 1);
+    __syncthreads();
+    if (last) combine_group(a, blockIdx.x);
+  }
 }
 
 template <int ACT, int PHASE, bool TILED>
@@ -1041,7 +1102,13 @@ static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
     }
   } else if constexpr (TILED && ACT != ACT_F32) {
     const unsigned gx = unsigned((a.R + 63) / 64);  // row groups
-    gemm_decode_tiled_kernel<ACT, PHASE><<<dim3(gx, unsigned(a.max_active)), dim3(256), 0, stream>>>(a);
+    const dim3 grid(gx, unsigned(a.max_active));
+    // tokens per expert <= tokens per batch: batches of at most
+    // kDecodeOneSubtile tokens never need the 32-token pass
+    if (a.T <= kDecodeOneSubtile)
+      gemm_decode_tiled_kernel<ACT, PHASE, 1><<<grid, dim3(256), 0, stream>>>(a);
+    else
+      gemm_decode_tiled_kernel<ACT, PHASE, 2><<<grid, dim3(256), 0, stream>>>(a);
   } else {
     const unsigned gx = unsigned((a.R + 16 * kDecodeRowTiles - 1) / (16 * kDecodeRowTiles));
     gemm_decode_kernel<ACT, PHASE, TILED><<<dim3(gx, unsigned(a.max_active)), dim3(256), 0, stream>>>(a);

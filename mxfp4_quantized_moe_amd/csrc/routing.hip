@@ -306,7 +306,7 @@ __device__ void permute_block(const PermuteArgs& a) {
         toff[e] = tbase;
         if (a.counts_out) a.counts_out[e] = c[j];
         if (a.offsets_out) a.offsets_out[e] = cbase;
-        if (c[j] > 0) a.active[1 + abase++] = e;
+        if (c[j] > 0) a.active[1 + abase++] = make_int4(e, cbase, c[j], atot);
       }
       cbase += c[j];
       tbase += t[j];
@@ -315,9 +315,10 @@ __device__ void permute_block(const PermuteArgs& a) {
       off[E] = ctot;
       a.offsets[E] = ctot;
       a.tile_off[E] = ttot;
-      a.active[0] = atot;
+      a.active[0] = make_int4(atot, 0, 0, 0);
       if (a.offsets_out) a.offsets_out[E] = ctot;
     }
+    for (int i = atot + lane; i < min(E, N); i += 64) a.active[1 + i] = make_int4(0, 0, 0, 0);
   }
   __syncthreads();
 
@@ -389,7 +390,7 @@ constexpr int kPermLdsSlots = 1 << 16;
 
 __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(PermuteArgs a) {
   __shared__ int cnt[256];
-  __shared__ int s_off, s_toff, s_act;
+  __shared__ int s_off, s_toff, s_act, s_atot;
   __shared__ int wsum[kPermWaves];
   __shared__ uint8_t sidx[kPermLdsSlots];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -452,12 +453,15 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
       tbase += (c[j] + kPrefillTokens - 1) / kPrefillTokens;
       abase += c[j] > 0;
     }
+    if (lane == 0) s_atot = atot;
     if (me == 0 && lane == 0) {
       a.offsets[E] = ctot;
       a.tile_off[E] = ttot;
-      a.active[0] = atot;
+      a.active[0] = make_int4(atot, 0, 0, 0);
       if (a.offsets_out) a.offsets_out[E] = ctot;
     }
+    if (me == 0)
+      for (int i = atot + lane; i < min(E, N); i += 64) a.active[1 + i] = make_int4(0, 0, 0, 0);
   }
   __syncthreads();
   const int c_me = cnt[me], off_me = s_off, toff_me = s_toff;
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
     a.tile_off[me] = toff_me;
     if (a.counts_out) a.counts_out[me] = c_me;
     if (a.offsets_out) a.offsets_out[me] = off_me;
-    if (c_me > 0) a.active[1 + s_act] = me;
+    if (c_me > 0) a.active[1 + s_act] = make_int4(me, off_me, c_me, s_atot);
   }
   for (int j = tid; j * kPrefillTokens < c_me; j += kPermThreads)
     a.tiles[toff_me + j] = make_int4(me, off_me + j * kPrefillTokens, min(kPrefillTokens, c_me - j * kPrefillTokens), 0);
@@ -556,15 +560,15 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint4* __restrict_
 // token routes to once: expert 0 owns sorted rows 0 .. T-1 (the token rows
 // themselves), in ceil(T / kPrefillTokens) prefill tiles.
 
-__global__ __launch_bounds__(256) void linear_setup_kernel(int T, int32_t* offsets, int32_t* active, int32_t* tile_off,
+__global__ __launch_bounds__(256) void linear_setup_kernel(int T, int32_t* offsets, int4* active, int32_t* tile_off,
                                                            int4* tiles, void* zero_bias, int N, int zero_bias_bytes) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int ntiles = (T + kPrefillTokens - 1) / kPrefillTokens;
   if (i == 0) {
     offsets[0] = 0;
     offsets[1] = T;
-    active[0] = 1;
-    active[1] = 0;
+    active[0] = make_int4(1, 0, 0, 0);
+    active[1] = make_int4(0, 0, T, 1);
     tile_off[0] = 0;
     tile_off[1] = ntiles;
   }
@@ -577,7 +581,7 @@ __global__ __launch_bounds__(256) void linear_setup_kernel(int T, int32_t* offse
   }
 }
 
-hipError_t launch_linear_setup(int T, int32_t* offsets, int32_t* active, int32_t* tile_off, int4* tiles,
+hipError_t launch_linear_setup(int T, int32_t* offsets, int4* active, int32_t* tile_off, int4* tiles,
                                void* zero_bias, int N, int zero_bias_bytes, hipStream_t stream) {
   const int ntiles = (T + kPrefillTokens - 1) / kPrefillTokens;
   const int n = ntiles > N ? ntiles : N;
@@ -608,9 +612,9 @@ __global__ __launch_bounds__(256) void dense_group_kernel(DenseGroupArgs a) {
     a.tile_off[i] = int(i) * ntiles;
     if (i < E) {
       a.counts[i] = T;
-      a.active[1 + i] = int(i);
+      a.active[1 + i] = make_int4(int(i), int(i) * T, T, E);
     } else {
-      a.active[0] = E;
+      a.active[0] = make_int4(E, 0, 0, 0);
     }
   }
   if (i < int64_t(E) * ntiles) {
