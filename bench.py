@@ -48,7 +48,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EV_EVERY = 4  # timed steps between two recordings of the dominant stage's events
 GRAPH_STEPS = 20  # forwards captured per HIP graph in the graph launch mode
 KERNEL_SOURCES = ["mxfp4_quantized_moe_amd/csrc/moe_gemm.hip", "mxfp4_quantized_moe_amd/csrc/codec.hip",
-                  "mxfp4_quantized_moe_amd/csrc/device_common.h"]
+                  "mxfp4_quantized_moe_amd/csrc/device_common.h", "mxfp4_quantized_moe_amd/csrc/gemm_common.h",
+                  "mxfp4_quantized_moe_amd/csrc/decode_tile.h", "mxfp4_quantized_moe_amd/csrc/launch.h"]
 
 
 def kernel_source_hash() -> str:
@@ -406,6 +407,10 @@ def bench_unpack(args, dev):
     tens = [(W.array_to_torch(b, dev), W.array_to_torch(s, dev)) for b, s in case.tensors]
     outs = [torch.empty(b.shape[:-2] + (b.shape[-2] * 32,), dtype=torch.bfloat16, device=dev) for b, _ in tens]
     byts = sum(b.numel() + s.numel() + o.numel() * 2 for (b, s), o in zip(tens, outs))
+    # the plain 256 MiB copy that scales the HBM byte counters of a profiled run
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    torch.empty_like(src).copy_(src)
+    del src
     for _ in range(args.warmup):
         for (b, s), o in zip(tens, outs):
             mx.mxfp4_unpack(b, s, out=o)
@@ -433,7 +438,9 @@ def bench_unpack(args, dev):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8->bf16",
             "data": "synthetic", "config": {"workload": case.name, "bytes_per_step": byts},
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK["hbm_GBps"], "unit": "GB/s",
-                         "frac": gbps / PEAK["hbm_GBps"], "traffic": measured_traffic("unpack_20b", "unpack_kernel")}}
+                         "frac": gbps / PEAK["hbm_GBps"], "kernel": "mxmoe::unpack_bf16_kernel",
+                         "traffic": measured_traffic("unpack_20b", "mxmoe::unpack_bf16_kernel"),
+                         "traffic_unit": "HBM bytes per step (its 2 launches)"}}
 
 
 def bench_linear(args, dev):
@@ -613,7 +620,7 @@ def gate_up_kernel_name(case, decode_shaped: bool, tiled: bool) -> str:
     act = 2 if case.fp8 else (1 if case.act_dtype == "bf16" else 0)
     if decode_shaped:
         if tiled and act != 0:
-            return f"mxmoe::gemm_decode_tiled_kernel<{act}, 0, {1 if case.T <= 16 else 2}>"
+            return f"mxmoe::gemm_decode_tiled_kernel<{act}, 0, {1 if case.T <= 64 else 2}>"
         return f"mxmoe::gemm_decode_kernel<{act}, 0, {'true' if tiled else 'false'}>"
     if tiled:
         return f"mxmoe::gemm_prefill_tiled_kernel<{act}, 0>"
