@@ -49,7 +49,7 @@ EV_EVERY = 4  # timed steps between two recordings of the dominant stage's event
 GRAPH_STEPS = 20  # forwards captured per HIP graph in the graph launch mode
 KERNEL_SOURCES = ["mxfp4_quantized_moe_amd/csrc/moe_gemm.hip", "mxfp4_quantized_moe_amd/csrc/codec.hip",
                   "mxfp4_quantized_moe_amd/csrc/device_common.h", "mxfp4_quantized_moe_amd/csrc/gemm_common.h",
-                  "mxfp4_quantized_moe_amd/csrc/decode_tile.h", "mxfp4_quantized_moe_amd/csrc/launch.h"]
+                  "mxfp4_quantized_moe_amd/csrc/decode_tile.h"]
 
 
 def kernel_source_hash() -> str:

@@ -334,7 +334,8 @@ size_t moe_mxfp4_workspace_bytes(const mxmoe_layer_t* layer, int64_t T, const mx
  * FP8 mode (fp8_act = 1): x and h are quantised to float8_e4m3fn as
  * code = sat448(rne(fp32(v) * (1 / scale))), 1/scale computed once in fp32,
  * and both GEMMs run on scaled MXFP4 x FP8 matrix instructions with fp32
- * accumulation; the router still reads the unquantised x.
+ * accumulation; the router still reads the unquantised x (and writes the
+ * e4m3 codes of x as it reads it, so the quantisation stage is empty).
  *
  * With expert_path = MXMOE_PATH_DENSE the two GEMMs run over all T*E
  * (expert, token) pairs, row e*T + t, and the combine reads the top_k rows

@@ -139,7 +139,7 @@ T* at(void* base, size_t off) {
 hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act_dtype, const Workspace& w,
                        void* ws, int32_t* idx_out, float* w_out, int32_t* counts_out, int32_t* offsets_out,
                        int32_t* sorted_buf, int32_t* pos_buf, hipStream_t s, hipEvent_t mid = nullptr,
-                       bool dense = false) {
+                       bool dense = false, uint8_t* xq = nullptr, float x_inv = 1.0f) {
   RouteArgs ra{};
   ra.x = x;
   ra.w_r = L->router_w;
@@ -153,6 +153,8 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   ra.wts = at<float>(ws, w.wts);
   ra.idx_out = idx_out;
   ra.wts_out = w_out;
+  ra.xq = xq;
+  ra.x_inv = x_inv;
   if (dense) {
     hipError_t e = launch_route(ra, s);
     if (e != hipSuccess) return e;
@@ -266,17 +268,15 @@ mxmoe_status_t forward_impl(const mxmoe_layer_t* L, const void* x, int64_t T, vo
   void* const* ev = o->stage_events;
   auto mark = [&](int i) { return ev && ev[i] ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   if (mark(0) != hipSuccess) return MXMOE_ERR_HIP;
-  hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
-                             nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr, dense);
-  if (e != hipSuccess) return MXMOE_ERR_HIP;
-  if (mark(2) != hipSuccess) return MXMOE_ERR_HIP;
   const int act = fp8 ? ACT_FP8 : (o->act_dtype == MXMOE_BF16 ? ACT_BF16 : ACT_F32);
   const float inv_x = fp8 ? 1.0f / o->x_scale : 1.0f;
   const float inv_h = fp8 ? 1.0f / o->h_scale : 1.0f;
-  if (fp8) {
-    e = launch_quant_fp8(static_cast<const uint16_t*>(x), T * L->H, inv_x, at<uint8_t>(ws, w.xq), s);
-    if (e != hipSuccess) return MXMOE_ERR_HIP;
-  }
+  // FP8 mode: the router quantises x to e4m3 as it reads it
+  hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
+                             nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr, dense,
+                             fp8 ? at<uint8_t>(ws, w.xq) : nullptr, inv_x);
+  if (e != hipSuccess) return MXMOE_ERR_HIP;
+  if (mark(2) != hipSuccess) return MXMOE_ERR_HIP;
   if (mark(3) != hipSuccess) return MXMOE_ERR_HIP;
   const bool prefill = use_prefill(L, T, act, dense);
   // decode-shaped batches on the tiled decode kernels fold the combine

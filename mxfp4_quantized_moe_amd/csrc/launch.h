@@ -65,6 +65,10 @@ struct RouteArgs {
   float* wts;           // (T, k) workspace
   int32_t* idx_out;     // optional copies
   float* wts_out;
+  // FP8 activation mode: (T, H) e4m3 codes of x, quantised with x_inv as
+  // the router reads x (bf16 only); null: none
+  uint8_t* xq;
+  float x_inv;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 // Router then grouping; one launch when one 16-wave router workgroup covers

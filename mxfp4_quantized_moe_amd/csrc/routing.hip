@@ -14,6 +14,19 @@
 
 namespace mxmoe {
 
+// Eight bf16 values (a 16-byte load) -> eight e4m3 codes (8 bytes) with the
+// static per-tensor rule sat448(rne(fp32(v) * inv)), in the input's order.
+__device__ __forceinline__ uint2 bf16x8_to_e4m3x8(uint4 v, float inv) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __uint_as_float(w[j] << 16) * inv;
+    f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u) * inv;
+  }
+  return make_uint2(pack_e4m3x4(f[0], f[1], f[2], f[3]), pack_e4m3x4(f[4], f[5], f[6], f[7]));
+}
+
 // ------------------------------------------------------------------ router
 //
 // One workgroup per 16 tokens.  The logits^T tile (E x 16) is an MFMA
@@ -71,6 +84,10 @@ __device__ __forceinline__ void topk_softmax(const RouteArgs& a, const float* lg
 
 // The grouping of one workgroup of kPermThreads threads (defined below).
 __device__ void permute_block(const PermuteArgs& a);
+
+// The top-k, softmax and grouping of a batch of at most 16 tokens and 64
+// experts, by the router's one workgroup (defined below).
+__device__ void finish_small_batch(const RouteArgs& a, const PermuteArgs& pa, const float* part);
 
 // RG row tiles of 16 experts have their loads issued together, NG groups
 // cover E <= 16 * RG * NG.  FUSE: the workgroup (the only one, 16 waves)
@@ -136,6 +153,17 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a, PermuteArgs
         // neither loads nor MFMAs cross this point
         __builtin_amdgcn_sched_barrier(0);
         if (grp == 0) {
+          // FP8 mode: the e4m3 codes of these x values (the first
+          // quantisation of the path), stored before the lane transpose, 8
+          // values per load; the weight loads are already in flight
+          if constexpr (BF16) {
+            if (a.xq && tok < a.T) {
+#pragma unroll
+              for (int s = 0; s < XL; ++s)
+                if (kofs[s] != kOOB)
+                  *reinterpret_cast<uint2*>(a.xq + int64_t(tok) * H + kofs[s] / 2) = bf16x8_to_e4m3x8(xq[s], a.x_inv);
+            }
+          }
 #pragma unroll
           for (int s = 0; s < XL; ++s) xq[s] = lane_permute(xq[s], perm);
         }
@@ -184,15 +212,15 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(RouteArgs a, PermuteArgs
   }
   __syncthreads();
 
-  // top-k + softmax: 4*KW lanes per token, all 16 tokens at once
-  const int tl = threadIdx.x / kLanesPerToken;
-  if (t0 + tl < a.T) {
-    if (a.top_k <= 4) topk_softmax<4, kLanesPerToken>(a, part + 4 * tl, t0 + tl);
-    else topk_softmax<MAX_TOPK_DEV, kLanesPerToken>(a, part + 4 * tl, t0 + tl);
-  }
   if constexpr (FUSE) {
-    __syncthreads();  // the expert ids written above are visible to the whole workgroup
-    permute_block(pa);
+    finish_small_batch(a, pa, part);
+  } else {
+    // top-k + softmax: 4*KW lanes per token, all 16 tokens at once
+    const int tl = threadIdx.x / kLanesPerToken;
+    if (t0 + tl < a.T) {
+      if (a.top_k <= 4) topk_softmax<4, kLanesPerToken>(a, part + 4 * tl, t0 + tl);
+      else topk_softmax<MAX_TOPK_DEV, kLanesPerToken>(a, part + 4 * tl, t0 + tl);
+    }
   }
 }
 
@@ -375,6 +403,98 @@ __device__ void permute_block(const PermuteArgs& a) {
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) { permute_block(a); }
 
+// A batch of at most 16 tokens (E <= 64, one router workgroup of 16
+// waves, logits final in `part`).  Wave t takes token t with lane e on
+// expert e: each key's rank among its token's E keys (the keys are
+// distinct) places the k best in order, so no merge network runs on the
+// one or few waves that have a token.  The softmax then follows
+// topk_softmax_terms over those k in rank order.  The grouping is the one
+// permute_block makes, for at most 16 * 8 slots: per-expert counts by
+// wave 0 over the slots' ids in LDS, a wave scan for the offsets, the
+// active-slot records and one prefill tile per active expert (an expert
+// sees at most 16 tokens), then each slot's stable position from the
+// earlier slots of its expert.
+__device__ void finish_small_batch(const RouteArgs& a, const PermuteArgs& pa, const float* part) {
+  __shared__ uint64_t skey[kRouteTokens][64];
+  __shared__ uint64_t stop[kRouteTokens][MAX_TOPK_DEV];
+  __shared__ int sids[kRouteTokens * MAX_TOPK_DEV];
+  __shared__ int soff[64];
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  const int E = a.E, k = a.top_k, T = a.T, N = T * k;
+  const bool live = t < T && lane < E;
+  const uint64_t key =
+      live ? expert_key(part[4 * t + 256 * (lane >> 4) + 64 * ((lane >> 2) & 3) + (lane & 3)], lane) : 0;
+  skey[t][lane] = key;
+  __syncthreads();
+  if (live) {
+    int rank = 0;
+    for (int e = 0; e < E; ++e) rank += skey[t][e] > key;
+    if (rank < k) stop[t][rank] = key;
+  }
+  __syncthreads();
+  if (t < T && lane < k) {
+    uint64_t l[MAX_TOPK_DEV];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK_DEV; ++j) l[j] = j < k ? stop[t][j] : 0;
+    float ex[MAX_TOPK_DEV];
+    const float den = topk_softmax_terms<MAX_TOPK_DEV>(l, k, ex);
+    float w = 0.f;
+    int e = 0;
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK_DEV; ++j)
+      if (j == lane) {
+        w = ex[j] / den;
+        e = key_expert(l[j]);
+      }
+    const int o = t * k + lane;
+    a.idx[o] = e;
+    a.wts[o] = w;
+    if (a.idx_out) a.idx_out[o] = e;
+    if (a.wts_out) a.wts_out[o] = w;
+    sids[o] = e;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int c = 0;
+    if (lane < E)
+      for (int s = 0; s < N; ++s) c += sids[s] == lane;
+    int tot;
+    const int off = wave_excl_scan(c, lane, &tot);
+    const uint64_t act = __ballot(c > 0);
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int arank = __popcll(act & lt), atot = __popcll(act);
+    if (lane < E) {
+      soff[lane] = off;
+      pa.offsets[lane] = off;
+      pa.counts[lane] = c;
+      pa.tile_off[lane] = arank;
+      if (pa.counts_out) pa.counts_out[lane] = c;
+      if (pa.offsets_out) pa.offsets_out[lane] = off;
+      if (c > 0) {
+        pa.active[1 + arank] = make_int4(lane, off, c, atot);
+        pa.tiles[arank] = make_int4(lane, off, c, 0);
+      }
+    }
+    if (lane == 0) {
+      pa.offsets[E] = tot;
+      pa.tile_off[E] = atot;
+      pa.active[0] = make_int4(atot, 0, 0, 0);
+      if (pa.offsets_out) pa.offsets_out[E] = tot;
+    }
+    for (int i = atot + lane; i < min(E, N); i += 64) pa.active[1 + i] = make_int4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < N; s += blockDim.x) {
+    const int e = sids[s];
+    int r = 0;
+    for (int s2 = 0; s2 < s; ++s2) r += sids[s2] == e;
+    const int p = soff[e] + r;
+    pa.sorted[p] = s;
+    pa.sorted_tok[p] = s / k;
+    pa.pos[s] = p;
+  }
+}
+
 // Expert-parallel grouping for large batches: workgroup e handles expert e.
 // Every workgroup builds the full histogram in LDS (integer counts, order
 // free) and scans it, which gives all offsets without a second launch; it
@@ -543,15 +663,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint4* __restrict_
                                                         uint2* __restrict__ q) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n8) return;
-  const uint4 v = x[i];
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float f[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f[2 * j] = __uint_as_float(w[j] << 16) * inv;
-    f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u) * inv;
-  }
-  q[i] = make_uint2(pack_e4m3x4(f[0], f[1], f[2], f[3]), pack_e4m3x4(f[4], f[5], f[6], f[7]));
+  q[i] = bf16x8_to_e4m3x8(x[i], inv);
 }
 
 // ------------------------------------------------------------- dense layer
