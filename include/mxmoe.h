@@ -300,8 +300,8 @@ typedef enum {
    * dense all-experts path of the KerasFormers "mxfp4" page ("As GPT-OSS's
    * native format"), which its long prefills take when cheaper.  The output
    * equals the routed path's up to the fp32 summation order inside the
-   * GEMMs (E/top_k times the GEMM work; rows T*E must fit the 32-bit
-   * buffer windows, else MXMOE_ERR_SHAPE). */
+   * GEMMs (E/top_k times the GEMM work, and a workspace for T*E rows of h
+   * and Y). */
   MXMOE_PATH_DENSE = 1
 } mxmoe_path_t;
 

@@ -110,15 +110,16 @@ mxmoe_status_t check_opts(const mxmoe_layer_t* L, const mxmoe_fwd_opts_t* o, boo
   return MXMOE_OK;
 }
 
-// The kernels address each expert's weights, x and the intermediate h
-// through 32-bit range-checked buffer windows below 2^31 bytes.
+// The kernels address each expert's weights, x, and each tile's rows of the
+// intermediate h through 32-bit range-checked buffer windows below 2^31
+// bytes (h as a whole may be larger: a dense layer's T*E rows).
 constexpr int64_t kMaxWindow = (int64_t(1) << 31) - 1;
 
 mxmoe_status_t check_tokens(const mxmoe_layer_t* L, int64_t T, bool dense = false) {
   if (T < 0) return MXMOE_ERR_SHAPE;
   if (T * int64_t(dense ? L->E : L->top_k) > kMaxSlots) return MXMOE_ERR_SHAPE;
-  const int64_t slots = gemm_rows(L, T, dense);
-  if (T * int64_t(L->H) * 4 > kMaxWindow || slots * int64_t(L->I) * 4 > kMaxWindow) return MXMOE_ERR_SHAPE;
+  // x; and an expert's rows of h (at most T: a token meets an expert once)
+  if (T * int64_t(L->H) * 4 > kMaxWindow || T * int64_t(L->I) * 4 > kMaxWindow) return MXMOE_ERR_SHAPE;
   if (int64_t(2) * L->I * L->H / 2 > kMaxWindow) return MXMOE_ERR_SHAPE;
   int64_t bb, sb;  // one expert's tiled gate_up (the larger of the two matrices)
   tiled_sizes(1, int64_t(2) * L->I, L->H, &bb, &sb);

@@ -49,7 +49,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
   const int nb = a.nb, nc = wb.nc, K = nb * 32;
   constexpr int EB = ACT == ACT_BF16 ? 2 : 1;  // bytes per B element
   const uint32_t row_bytes = uint32_t(K) * EB;
-  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
+  const rsrc_t bsrc = act_rows(a, PHASE, row_start, n_e, row_bytes);
   const int nj = (nc - wave + 3) >> 2;  // chunks of this wave (0 when nc <= wave)
   const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
   // bias of the 4 output rows this lane stores (row tile t0 + wave, rows
@@ -75,8 +75,8 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
       int src[NA];
 #pragma unroll
       for (int nt = 0; nt < NA; ++nt) {
-        const int p = row_start + min(tg + nt * 16 + r16, n_e - 1);
-        src[nt] = PHASE == 0 ? a.sorted_tok[p] : p;
+        const int jc = min(tg + nt * 16 + r16, n_e - 1);
+        src[nt] = PHASE == 0 ? a.sorted_tok[row_start + jc] : jc;
       }
       uint32_t boff[NA];
       St st[D];

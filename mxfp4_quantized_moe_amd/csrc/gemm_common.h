@@ -111,13 +111,22 @@ __device__ __forceinline__ uint32_t dword(const uint4& q, int i) {
   return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
 }
 
-// Byte offset of token row j (of n >= 1) of a tile inside bsrc, or kOOB.
-// gate_up gathers x rows by token id; down reads h rows in sorted order.
-// The token-id load is unconditional (clamped index) so it needs no branch.
+// The activation rows of a tile as a range-checked buffer: gate_up gathers
+// x rows (any of the b_rows tokens) by token id; down reads its own n
+// contiguous h rows from sorted row row_start on, so its window starts
+// there (a dense layer's T*E rows of h can outgrow one 32-bit window).
+__device__ __forceinline__ rsrc_t act_rows(const GemmArgs& a, int phase, int row_start, int n, uint32_t row_bytes) {
+  if (phase == 0) return make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
+  return make_rsrc(static_cast<const uint8_t*>(a.bsrc) + int64_t(row_start) * row_bytes, uint32_t(n) * row_bytes);
+}
+
+// Byte offset of token row j (of n >= 1) of a tile inside act_rows(...),
+// or kOOB.  The token-id load is unconditional (clamped index) so it needs
+// no branch.
 __device__ __forceinline__ uint32_t act_row_offset(const GemmArgs& a, int phase, int row_start, int j, int n,
                                                    uint32_t row_bytes) {
-  const int p = row_start + min(j, n - 1);
-  const int src_row = phase == 0 ? a.sorted_tok[p] : p;
+  const int jc = min(j, n - 1);
+  const int src_row = phase == 0 ? a.sorted_tok[row_start + jc] : jc;
   return j < n ? uint32_t(src_row) * row_bytes : kOOB;
 }
 

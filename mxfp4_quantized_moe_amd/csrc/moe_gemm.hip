@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   const WBuf wb = expert_weights<TILED>(a, e);
   constexpr int EB = ACT == ACT_F32 ? 4 : (ACT == ACT_BF16 ? 2 : 1);  // bytes per B element
   const uint32_t row_bytes = uint32_t(K) * EB;
-  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
+  const rsrc_t bsrc = act_rows(a, PHASE, row_start, n_e, row_bytes);
 
   for (int tg = 0; tg < n_e; tg += 64) {
     // byte offset of this lane's token row for each of the 4 token sub-tiles
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs 
   const bool busy = rt_active > 0;  // wave-uniform
   const WBuf wb = expert_weights<TILED>(a, e);
   const uint32_t row_bytes = uint32_t(K) * EB;
-  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
+  const rsrc_t bsrc = act_rows(a, PHASE, row_start, ntok, row_bytes);
 
   // bias of this lane's 4 output rows per row tile (bf16: the parameters
   // share the activations' dtype), fetched early as one 8-byte load each
@@ -745,7 +745,7 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   const bool busy = rt_active > 0;  // wave-uniform
   const bool wok = t0 < wb.rt4;
   const uint32_t row_bytes = uint32_t(K) * EB;
-  const rsrc_t bsrc = make_rsrc(a.bsrc, uint32_t(a.b_rows) * row_bytes);
+  const rsrc_t bsrc = act_rows(a, PHASE, row_start, ntok, row_bytes);
   const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
 
   // The workgroup's kTiledRows bias values go to LDS by one DMA of wave 0,

@@ -184,12 +184,19 @@ def test_dense_path_validation(lib):
     # h and Y for all T*E (expert, token) rows instead of T*k
     assert dense >= routed + 64 * (32 - 4) * (2880 * 2 + 2880 * 2)
     assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(L), 64, ctypes.byref(_opts(expert_path=3))) == 0
-    # T*E rows of h beyond the 32-bit buffer window: the dense path refuses
-    # a long prefill over many experts that the routed path takes
+    # the 120b prefill: T*E = 524288 rows of h and Y (3 GB each in bf16) are
+    # more than one 32-bit buffer window reaches, but the kernels address h
+    # one tile's rows at a time, so the dense path takes it
     big = _layer(E=128, H=2880, I=2880, top_k=4)
-    assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(big), 4096, ctypes.byref(_opts())) > 0
-    assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(big), 4096, ctypes.byref(_opts(expert_path=1))) == 0
-    assert _fwd(lib, big, T=4096, opts=_opts(expert_path=1)) == SHAPE
+    routed_big = lib.moe_mxfp4_workspace_bytes(ctypes.byref(big), 4096, ctypes.byref(_opts()))
+    dense_big = lib.moe_mxfp4_workspace_bytes(ctypes.byref(big), 4096, ctypes.byref(_opts(expert_path=1)))
+    assert routed_big > 0
+    assert dense_big >= routed_big + 4096 * (128 - 4) * (2880 * 2 + 2880 * 2)
+    # x past one window: both paths refuse
+    huge_t = (1 << 31) // (2880 * 4) + 1
+    for path in (0, 1):
+        assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(big), huge_t, ctypes.byref(_opts(expert_path=path))) == 0
+        assert _fwd(lib, big, T=huge_t, opts=_opts(expert_path=path)) == SHAPE
     # routing only: the grouping is always the routed one
     assert lib.moe_mxfp4_route(ctypes.byref(big), P, 4096, ctypes.byref(_opts(expert_path=7)), None, None, None,
                                None, None, None, P, 0, None) == WS

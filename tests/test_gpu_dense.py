@@ -78,3 +78,14 @@ def test_dense_matches_routed_on_gpu(dev):
     a = O.bf16_from_bits(rd["out"])
     b = O.bf16_from_bits(rr["out"])
     assert np.max(np.abs(a - b)) <= 1e-2 * np.max(np.abs(b))
+
+
+def test_dense_prefill_120b(dev):
+    """The 120b prefill (T=4096, 128 experts) on the dense path: 524288 GEMM
+    rows, whose h and Y (3 GB each) lie beyond one 32-bit buffer window, so
+    the down GEMM's tiles address h through windows of their own rows.
+    Every token against the routed oracle."""
+    case = W.prefill_120b()
+    note(f"{case.name} tiled dense")
+    res, _, _ = run_gpu(case, dev, want_route=False, layout="tiled", dense=True)
+    check_layer(case, res, full_ref=oracle_full(case))
