@@ -26,7 +26,8 @@ Workloads (synthetic, seeded; see workloads/):
   linear_t4096_k2880_n5760  weight-only MXFP4 dense layer y = x W^T + b, bf16
   fp8_linear_t4096_k2880_n5760  FP8 E4M3 W8A8 dense layer, static per-tensor scales
   bf16_20b_t{T}        the 20b layer at any T (with --path dense: the all-experts path)
-  int8_20b_t2048       INT8 W8A8 MoE layer (per-channel weights, per-token activations), 20b shape
+  int8_20b_t{T}        INT8 W8A8 MoE layer (per-channel weights, per-token activations), 20b shape
+                       (T=2048 prefill; T <= 128 runs the decode-shaped kernels)
 """
 from __future__ import annotations
 
@@ -558,15 +559,17 @@ def bench_fp8_linear(args, dev):
 
 def bench_int8(args, dev):
     """The INT8 W8A8 MoE layer at the 20b shape: tokens/s of whole forwards,
-    and the two grouped GEMMs' int8 ops over the forward's duration (HIP
-    events around each call on its stream) against the dense int8 peak."""
+    and against the roofline over the forward's duration (HIP events around
+    each call on its stream): the two grouped GEMMs' int8 ops against the
+    dense int8 peak for a prefill batch, the routed experts' int8 weights
+    and scales against HBM for a decode batch."""
     import numpy as np
     import torch
 
     import mxfp4_quantized_moe_amd as mx
     import workloads as W
 
-    T = 2048
+    T = int(args.workload.rsplit("t", 1)[1])
     case = W.int8_20b(T)
     L = case.layer
     w0 = W.int8_layer_to_torch(L, dev)
@@ -578,6 +581,9 @@ def bench_int8(args, dev):
                      for _ in range(copies - 1)]
     out = torch.empty_like(x)
     ws = torch.empty(max(mx.moe_int8_workspace_bytes(w0, T), 256), dtype=torch.uint8, device=dev)
+    idx = torch.empty((T, L.top_k), dtype=torch.int32, device=dev)
+    mx.moe_int8_forward(w0, x, out=out, workspace=ws, topk_idx_out=idx)
+    n_active = len(np.unique(W.torch_to_array(idx)))
     for i in range(args.warmup):
         mx.moe_int8_forward(layers[i % copies], x, out=out, workspace=ws)
     torch.cuda.synchronize()
@@ -592,7 +598,21 @@ def bench_int8(args, dev):
     t1 = time.perf_counter()
     call_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
     ops = 2 * T * L.top_k * (2 * L.I * L.H + L.H * L.I)
-    achieved = ops / call_s / 1e12
+    rows = T * L.top_k
+    if rows <= 16 * min(L.E, rows):
+        # decode-shaped: the routed experts' int8 codes, fp32 row scales and
+        # bf16 biases of both matrices, x in and out
+        byts = n_active * (3 * L.I * L.H + (2 * L.I + L.H) * (4 + 2)) + 2 * T * L.H * 2
+        achieved = byts / call_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_GBps"], "unit": "GB/s",
+                "frac": achieved / PEAK["hbm_GBps"],
+                "algorithmic": f"{byts} B per forward ({n_active} routed experts)"}
+    else:
+        achieved = ops / call_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK["int8_TOPs"], "unit": "TOP/s",
+                "frac": achieved / PEAK["int8_TOPs"], "algorithmic": f"{ops} int8 ops per forward (gate_up + down)"}
+    roof.update({"kernel": "whole forward: routing, int8 quantisation of x and h, both grouped GEMMs, combine",
+                 "traffic": None})
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
@@ -606,11 +626,8 @@ def bench_int8(args, dev):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
             "data": "synthetic (seeded random int8 codes, per-row scales, bf16 activations)",
             "config": {"workload": f"int8_20b_t{T}", "E": L.E, "top_k": L.top_k, "H": L.H, "I": L.I, "T": T,
-                       "weight_copies": copies},
-            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK["int8_TOPs"], "unit": "TOP/s",
-                         "frac": achieved / PEAK["int8_TOPs"],
-                         "kernel": "whole forward: routing, int8 quantisation of x and h, both grouped GEMMs, combine",
-                         "algorithmic": f"{ops} int8 ops per forward (gate_up + down)", "traffic": None}}
+                       "weight_copies": copies, "routed_experts": n_active},
+            "roofline": roof}
 
 
 def gate_up_kernel_name(case, decode_shaped: bool, tiled: bool) -> str:
@@ -679,7 +696,7 @@ def main():
         res = bench_linear(args, dev)
     elif args.workload == "fp8_linear_t4096_k2880_n5760":
         res = bench_fp8_linear(args, dev)
-    elif args.workload == "int8_20b_t2048":
+    elif args.workload.startswith("int8_20b_t"):
         res = bench_int8(args, dev)
     else:
         res = bench_layer(args, dev)

@@ -780,23 +780,34 @@ mxmoe_status_t moe_int8_forward(const mxmoe_int8_layer_t* L, const void* x, int6
   if (launch_quant_rows_int8(static_cast<const uint16_t*>(x), T, L->H, at<int8_t>(ws, w.xq), at<float>(ws, w.sx), s) !=
       hipSuccess)
     return MXMOE_ERR_HIP;
-  // gate_up + SwiGLU -> h (bf16)
+  // gate_up + SwiGLU -> h (bf16); decode-shaped batches take the decode
+  // tile and fold the combine into the down GEMM, as the MXFP4 forward
+  const bool prefill = use_prefill(&R, T, ACT_INT8);
+  const bool fold = !prefill && T <= kFusedCombineTokens && T * L->top_k * int64_t(L->H) * 2 <= kMaxWindow;
   GemmArgs g0 = gemm_args(&R, b, ws, T, ACT_INT8, 0);
   g0.bsrc = at<void>(ws, w.xq);
   g0.row_scale = L->gate_up_scale;
   g0.tok_scale = at<float>(ws, w.sx);
-  if (launch_moe_gemm(g0, true, s) != hipSuccess) return MXMOE_ERR_HIP;
+  GemmArgs g1 = gemm_args(&R, b, ws, T, ACT_INT8, 1);
+  g1.bsrc = at<void>(ws, w.hq);
+  g1.row_scale = L->down_scale;
+  g1.tok_scale = at<float>(ws, w.sh);
+  if (fold) {
+    g0.cmb_count = g1.cmb_count = at<uint32_t>(ws, b.cmb);
+    g0.n_cmb = g1.n_cmb = (L->H + 63) / 64;
+    g1.cmb_out = out;
+    g1.pos = at<int32_t>(ws, b.pos);
+    g1.wts = at<float>(ws, b.wts);
+  }
+  if (launch_moe_gemm(g0, prefill, s) != hipSuccess) return MXMOE_ERR_HIP;
   // per-row int8 h
   const int64_t slots = T * L->top_k;
   if (launch_quant_rows_int8(at<uint16_t>(ws, b.h), slots, L->I, at<int8_t>(ws, w.hq), at<float>(ws, w.sh), s) !=
       hipSuccess)
     return MXMOE_ERR_HIP;
-  // down -> Y (bf16)
-  GemmArgs g1 = gemm_args(&R, b, ws, T, ACT_INT8, 1);
-  g1.bsrc = at<void>(ws, w.hq);
-  g1.row_scale = L->down_scale;
-  g1.tok_scale = at<float>(ws, w.sh);
-  if (launch_moe_gemm(g1, true, s) != hipSuccess) return MXMOE_ERR_HIP;
+  // down -> Y (bf16), and the output when the combine is folded in
+  if (launch_moe_gemm(g1, prefill, s) != hipSuccess) return MXMOE_ERR_HIP;
+  if (fold) return MXMOE_OK;
   CombineArgs ca{};
   ca.Y = at<void>(ws, b.y);
   ca.y_bf16 = 1;

@@ -1,6 +1,7 @@
-// Decode-shaped tile of the MXFP4 expert GEMMs on the tiled weight order
-// (bf16 and FP8 activations), for gfx950: one 64-row group of one routed
-// expert against that expert's tokens.
+// Decode-shaped tile of the expert GEMMs on the tiled weight orders, for
+// gfx950: one 64-row group of one routed expert against that expert's
+// tokens.  MXFP4 weights with bf16 or FP8 activations, or int8 weights (the
+// 8-bit tile order) with int8 activations.
 //
 // Bound by streaming the routed experts' packed weights.  The workgroup's 4
 // waves split the K chunks (c = wave, wave + 4, ...) and every wave covers
@@ -19,10 +20,11 @@ namespace mxmoe {
 template <int ACT, int NA>
 struct DecodeStage {
   // 16-byte B loads per token sub-tile: 4 for bf16 tokens (32 values), 2
-  // for FP8 codes
+  // for FP8 or int8 codes
   static constexpr int BL = ACT == ACT_BF16 ? 4 : 2;
-  uint4 aq[4];
-  uint32_t sw;
+  uint4 aq[4];                             // MXFP4: 32 nibbles per row tile; int8: K 16g .. 16g+15
+  uint4 aq2[ACT == ACT_INT8 ? 4 : 1];      // int8: K 64+16g .. 64+16g+15
+  uint32_t sw;                             // MXFP4: the 4 row tiles' scale bytes
   uint4 bq[NA][BL];
 };
 
@@ -37,14 +39,15 @@ constexpr int kDecodeTileLds = 4 * 4 * 64 * 16;
 template <int ACT, int PHASE, int MAXNA>
 __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int row_start, int n_e,
                                             f32x4_t* red_lds) {
-  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8, "bf16 or fp8 activations");
+  static_assert(ACT == ACT_BF16 || ACT == ACT_FP8 || ACT == ACT_INT8, "bf16, fp8 or int8 activations");
   static_assert(MAXNA == 1 || MAXNA == 2, "one or two token sub-tiles per pass");
+  constexpr bool I8 = ACT == ACT_INT8;  // int8 x int8 -> exact int32 sums, scales in the epilogue
   // [wave][row tile][lane] of one token sub-tile
   f32x4_t (*red)[4][64] = reinterpret_cast<f32x4_t (*)[4][64]>(red_lds);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const WBuf wb = expert_weights<true>(a, e);
+  const WBuf wb = I8 ? byte_weights(a, e) : expert_weights<true>(a, e);
   const int t0 = 4 * q;  // first row tile of the group
   const int nb = a.nb, nc = wb.nc, K = nb * 32;
   constexpr int EB = ACT == ACT_BF16 ? 2 : 1;  // bytes per B element
@@ -68,7 +71,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
       constexpr int D = NA == 1 ? 3 : 2;  // chunks in flight per wave (3 measured faster than 2 and 4)
       static_assert(D == 2 || D == 3, "ring of 2 or 3 chunks");
       using St = DecodeStage<ACT, NA>;
-      constexpr int LOADS = 4 + 1 + NA * St::BL;        // VMEM instructions per chunk
+      constexpr int LOADS = (I8 ? 8 : 5) + NA * St::BL;  // VMEM instructions per chunk
       // token rows of the pass: gate_up gathers x rows through the token
       // table (its loads go out first, see the prologue), down reads h in
       // sorted order
@@ -94,11 +97,22 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
       auto issue_a = [&](int j, St& s) __attribute__((always_inline)) {
         const int c = wave + 4 * j;
         const bool ok = j < nj;
-        const uint32_t va = ok ? aslot : kOOB;
-        const uint32_t sa = ok ? uint32_t((t0 * nc + c) * 1024) : 0u;
+        if constexpr (I8) {
+          // 2 KB per (row tile, chunk); lane l's 32 bytes at 32 l
+          const uint32_t va = ok ? uint32_t(lane * 32) : kOOB;
+          const uint32_t sa = ok ? uint32_t((t0 * nc + c) * 2048) : 0u;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) s.aq[rt] = buf_load_b128(wb.blk, va, sa + uint32_t(rt * nc * 1024));
-        s.sw = buf_load_b32(wb.sc, ok ? uint32_t(lane * 4) : kOOB, ok ? uint32_t((q * nc + c) * 256) : 0u);
+          for (int rt = 0; rt < 4; ++rt) {
+            s.aq[rt] = buf_load_b128(wb.blk, va, sa + uint32_t(rt * nc * 2048));
+            s.aq2[rt] = buf_load_b128(wb.blk, va + 16u, sa + uint32_t(rt * nc * 2048));
+          }
+        } else {
+          const uint32_t va = ok ? aslot : kOOB;
+          const uint32_t sa = ok ? uint32_t((t0 * nc + c) * 1024) : 0u;
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) s.aq[rt] = buf_load_b128(wb.blk, va, sa + uint32_t(rt * nc * 1024));
+          s.sw = buf_load_b32(wb.sc, ok ? uint32_t(lane * 4) : kOOB, ok ? uint32_t((q * nc + c) * 256) : 0u);
+        }
       };
       auto issue_b = [&](int j, St& s) __attribute__((always_inline)) {
         const int c = wave + 4 * j;
@@ -114,7 +128,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
             for (int s4 = 0; s4 < 4; ++s4) s.bq[nt][s4] = buf_load_b128(bsrc, vb + 16u * s4, sb);
           }
         } else {
-          // FP8 B: lane group g holds K = 128c + 16g .. +16 and 128c + 64 + 16g .. +16
+          // FP8 / int8 B: lane group g holds K = 128c + 16g .. +16 and 128c + 64 + 16g .. +16
           const bool ok0 = ok && 4 * c + (g >> 1) < nb, ok1 = ok && 4 * c + 2 + (g >> 1) < nb;
 #pragma unroll
           for (int nt = 0; nt < NA; ++nt) {
@@ -138,6 +152,20 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
               for (int nt = 0; nt < NA; ++nt)
                 acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, s.bq[nt][s4]),
                                                                       acc[rt][nt], 0, 0, 0);
+            }
+          }
+        } else if constexpr (I8) {
+          // two K = 64 halves; the int32 sums live in the float accumulator registers
+          typedef int i32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const i32x4_t alo = __builtin_bit_cast(i32x4_t, s.aq[rt]), ahi = __builtin_bit_cast(i32x4_t, s.aq2[rt]);
+#pragma unroll
+            for (int nt = 0; nt < NA; ++nt) {
+              i32x4_t c4 = __builtin_bit_cast(i32x4_t, acc[rt][nt]);
+              c4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, __builtin_bit_cast(i32x4_t, s.bq[nt][0]), c4, 0, 0, 0);
+              c4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, __builtin_bit_cast(i32x4_t, s.bq[nt][1]), c4, 0, 0, 0);
+              acc[rt][nt] = __builtin_bit_cast(f32x4_t, c4);
             }
           }
         } else {
@@ -208,7 +236,9 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
         uint32_t x = 0;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-          x ^= st[d].aq[0].x ^ st[d].aq[1].y ^ st[d].aq[2].z ^ st[d].aq[3].w ^ st[d].sw;
+          x ^= st[d].aq[0].x ^ st[d].aq[1].y ^ st[d].aq[2].z ^ st[d].aq[3].w;
+          if constexpr (I8) x ^= st[d].aq2[0].x ^ st[d].aq2[1].y ^ st[d].aq2[2].z ^ st[d].aq2[3].w;
+          else x ^= st[d].sw;
 #pragma unroll
           for (int nt = 0; nt < NA; ++nt)
 #pragma unroll
@@ -231,10 +261,26 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
         __syncthreads();
         const int j = tg + nt * 16 + r16;
         if (j < n_e && r0 < a.R) {
-          f32x4_t sum = red[0][wave][lane];
-          sum += red[1][wave][lane];
-          sum += red[2][wave][lane];
-          sum += red[3][wave][lane];
+          f32x4_t sum;
+          if constexpr (I8) {
+            // exact int32 sums of the 4 waves -> fp32, times the row's and
+            // the token's scales (the prefill tile's int8 epilogue)
+            typedef int i32x4_t __attribute__((ext_vector_type(4)));
+            i32x4_t is = __builtin_bit_cast(i32x4_t, red[0][wave][lane]);
+            is += __builtin_bit_cast(i32x4_t, red[1][wave][lane]);
+            is += __builtin_bit_cast(i32x4_t, red[2][wave][lane]);
+            is += __builtin_bit_cast(i32x4_t, red[3][wave][lane]);
+            const float4 rs = *reinterpret_cast<const float4*>(a.row_scale + int64_t(e) * a.R + r0);
+            const int p = row_start + j;
+            const float ts = a.tok_scale[PHASE == 0 ? a.sorted_tok[p] : p];
+            sum = f32x4_t{float(is[0]) * rs.x * ts, float(is[1]) * rs.y * ts, float(is[2]) * rs.z * ts,
+                          float(is[3]) * rs.w * ts};
+          } else {
+            sum = red[0][wave][lane];
+            sum += red[1][wave][lane];
+            sum += red[2][wave][lane];
+            sum += red[3][wave][lane];
+          }
           const float v0 = sum[0] * a.acc_scale + __uint_as_float(bx << 16);
           const float v1 = sum[1] * a.acc_scale + __uint_as_float(bx & 0xFFFF0000u);
           const float v2 = sum[2] * a.acc_scale + __uint_as_float(by << 16);

@@ -1090,7 +1090,7 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_tiled_kernel(GemmArgs a) {
 
 template <int ACT, int PHASE, bool TILED>
 static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
-  if constexpr (ACT == ACT_W8A8 || ACT == ACT_INT8) {  // 8-bit weights: the tiled LDS-staged kernel only
+  if constexpr (ACT == ACT_W8A8) {  // FP8 weights: the tiled LDS-staged kernel only
     const int64_t items = (int64_t(a.max_tiles) * ((a.R + kTiledRows - 1) / kTiledRows) + 7) / 8 * 8;
     gemm_prefill_tiled_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kTiledThreads), 0, stream>>>(a);
   } else if (prefill) {
@@ -1142,9 +1142,9 @@ hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream) 
       break;
     case ACT_INT8 * 2 + 0:
     case ACT_INT8 * 2 + 1:
-      if (!a.tiled || !prefill) return hipErrorInvalidValue;
-      if (a.phase == 0) launch_layout<ACT_INT8, 0, true>(a, true, stream);
-      else launch_layout<ACT_INT8, 1, true>(a, true, stream);
+      if (!a.tiled) return hipErrorInvalidValue;  // the 8-bit tile order only
+      if (a.phase == 0) launch_layout<ACT_INT8, 0, true>(a, prefill, stream);
+      else launch_layout<ACT_INT8, 1, true>(a, prefill, stream);
       break;
     default: return hipErrorInvalidValue;
   }

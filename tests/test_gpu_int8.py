@@ -107,8 +107,10 @@ def test_int8_small_shapes(dev, seed, E, H, I, k, T):
     _check(case, _run(case, dev))
 
 
-@pytest.mark.parametrize("T", [1, 64])
+@pytest.mark.parametrize("T", [1, 8, 64])
 def test_int8_20b_decode_sizes(dev, T):
+    """Decode batches at the 20b shape: the decode-shaped int8 tile, with
+    the combine folded into the down GEMM."""
     case = W.int8_20b(T)
     note(case.name)
     _check(case, _run(case, dev))
