@@ -32,7 +32,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Workspace {
-  size_t idx, wts, counts, offsets, active, tile_off, tiles, sorted, sorted_tok, pos, cmb, calib, xq, h, y, total;
+  size_t idx, wts, counts, offsets, active, tile_off, tiles, rec0, rec1, sorted, sorted_tok, pos, cmb, calib, xq, h, y,
+      total;
 };
 
 // Rows of the two GEMMs: the T*k routed (token, expert) pairs, or all T*E
@@ -58,7 +59,12 @@ Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8,
   w.active = take(size_t(E + 1) * 16);
   w.tile_off = take(size_t(E + 1) * 4);
   const size_t active_max = grows < size_t(E) ? grows : size_t(E);
-  w.tiles = take((grows + kPrefillTokens - 1) / kPrefillTokens * 16 + active_max * 16);
+  const int max_tiles = int((grows + kPrefillTokens - 1) / kPrefillTokens + active_max);
+  w.tiles = take(size_t(max_tiles) * 16);
+  // per-workgroup item records of the tiled prefill gate_up (2I rows) and
+  // down (H rows) launches
+  w.rec0 = take(size_t(tiled_prefill_blocks(2 * I, max_tiles)) * 16);
+  w.rec1 = take(size_t(tiled_prefill_blocks(H, max_tiles)) * 16);
   w.sorted = take(slots * 4);
   w.sorted_tok = take(grows * 4);
   w.pos = take(slots * 4);
@@ -140,7 +146,7 @@ T* at(void* base, size_t off) {
 hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act_dtype, const Workspace& w,
                        void* ws, int32_t* idx_out, float* w_out, int32_t* counts_out, int32_t* offsets_out,
                        int32_t* sorted_buf, int32_t* pos_buf, hipStream_t s, hipEvent_t mid = nullptr,
-                       bool dense = false, uint8_t* xq = nullptr, float x_inv = 1.0f) {
+                       bool dense = false, uint8_t* xq = nullptr, float x_inv = 1.0f, bool item_records = false) {
   RouteArgs ra{};
   ra.x = x;
   ra.w_r = L->router_w;
@@ -189,6 +195,16 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
   pa.tiles = at<int4>(ws, w.tiles);
   pa.counts_out = counts_out;
   pa.offsets_out = offsets_out;
+  if (item_records) {  // a tiled prefill forward follows: resolve its workgroups' items here
+    const int64_t rows = T * L->top_k;
+    const int max_tiles = int((rows + kPrefillTokens - 1) / kPrefillTokens + (rows < L->E ? rows : L->E));
+    pa.blk_rec[0] = at<int4>(ws, w.rec0);
+    pa.blk_rec[1] = at<int4>(ws, w.rec1);
+    pa.rec_stripes[0] = (2 * L->I + kTiledRows - 1) / kTiledRows;
+    pa.rec_stripes[1] = (L->H + kTiledRows - 1) / kTiledRows;
+    pa.rec_blocks[0] = int(tiled_prefill_blocks(2 * L->I, max_tiles));
+    pa.rec_blocks[1] = int(tiled_prefill_blocks(L->H, max_tiles));
+  }
   if (mid) {  // the stage boundary is recorded: two launches
     hipError_t e = launch_route(ra, s);
     if (e != hipSuccess) return e;
@@ -270,19 +286,23 @@ mxmoe_status_t forward_impl(const mxmoe_layer_t* L, const void* x, int64_t T, vo
   auto mark = [&](int i) { return ev && ev[i] ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   if (mark(0) != hipSuccess) return MXMOE_ERR_HIP;
   const int act = fp8 ? ACT_FP8 : (o->act_dtype == MXMOE_BF16 ? ACT_BF16 : ACT_F32);
+  const bool prefill = use_prefill(L, T, act, dense);
+  const bool tiled = L->weight_layout == MXMOE_LAYOUT_TILED;
+  // a routed prefill on tiled weights: the grouping resolves every GEMM
+  // workgroup's item
+  const bool records = prefill && tiled && !dense;
   const float inv_x = fp8 ? 1.0f / o->x_scale : 1.0f;
   const float inv_h = fp8 ? 1.0f / o->h_scale : 1.0f;
   // FP8 mode: the router quantises x to e4m3 as it reads it
   hipError_t e = run_routing(L, x, T, o->act_dtype, w, ws, o->topk_idx_out, o->topk_w_out, nullptr, nullptr, nullptr,
                              nullptr, s, ev ? static_cast<hipEvent_t>(ev[1]) : nullptr, dense,
-                             fp8 ? at<uint8_t>(ws, w.xq) : nullptr, inv_x);
+                             fp8 ? at<uint8_t>(ws, w.xq) : nullptr, inv_x, records);
   if (e != hipSuccess) return MXMOE_ERR_HIP;
   if (mark(2) != hipSuccess) return MXMOE_ERR_HIP;
   if (mark(3) != hipSuccess) return MXMOE_ERR_HIP;
-  const bool prefill = use_prefill(L, T, act, dense);
   // decode-shaped batches on the tiled decode kernels fold the combine
   // into the down GEMM (Y read back through a 32-bit buffer window)
-  const bool fold = !prefill && L->weight_layout == MXMOE_LAYOUT_TILED && act != ACT_F32 && T <= kFusedCombineTokens &&
+  const bool fold = !prefill && tiled && act != ACT_F32 && T <= kFusedCombineTokens &&
                     gemm_rows(L, T, dense) * L->H * 2 <= kMaxWindow;
   GemmArgs g0 = gemm_args(L, w, ws, T, act, 0, dense);
   g0.bsrc = fp8 ? at<void>(ws, w.xq) : x;
@@ -292,6 +312,10 @@ mxmoe_status_t forward_impl(const mxmoe_layer_t* L, const void* x, int64_t T, vo
   }
   GemmArgs g1 = gemm_args(L, w, ws, T, act, 1, dense);
   if (fp8) g1.acc_scale = o->h_scale;
+  if (records) {
+    g0.blk_rec = at<int4>(ws, w.rec0);
+    g1.blk_rec = at<int4>(ws, w.rec1);
+  }
   if (fold) {
     g0.cmb_count = g1.cmb_count = at<uint32_t>(ws, w.cmb);
     g0.n_cmb = g1.n_cmb = (L->H + 63) / 64;
@@ -434,11 +458,15 @@ mxmoe_status_t moe_mxfp4_calibrate_fp8(const mxmoe_layer_t* L, const void* x, in
   const Workspace w = layout(L->E, L->H, L->I, L->top_k, T, MXMOE_BF16, false, gemm_rows(L, T, false));
   if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = run_routing(L, x, T, MXMOE_BF16, w, ws, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  const bool prefill = use_prefill(L, T, ACT_BF16);
+  const bool records = prefill && L->weight_layout == MXMOE_LAYOUT_TILED;
+  hipError_t e = run_routing(L, x, T, MXMOE_BF16, w, ws, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s,
+                             nullptr, false, nullptr, 1.0f, records);
   if (e != hipSuccess) return MXMOE_ERR_HIP;
   GemmArgs g0 = gemm_args(L, w, ws, T, ACT_BF16, 0);
   g0.bsrc = x;
-  if (launch_moe_gemm(g0, use_prefill(L, T, ACT_BF16), s) != hipSuccess) return MXMOE_ERR_HIP;
+  if (records) g0.blk_rec = at<int4>(ws, w.rec0);
+  if (launch_moe_gemm(g0, prefill, s) != hipSuccess) return MXMOE_ERR_HIP;
   uint32_t* slots = at<uint32_t>(ws, w.calib);
   if (launch_calib_init(slots, s) != hipSuccess) return MXMOE_ERR_HIP;
   if (launch_amax_bf16(static_cast<const uint16_t*>(x), T * L->H, slots, s) != hipSuccess) return MXMOE_ERR_HIP;
@@ -773,8 +801,9 @@ mxmoe_status_t moe_int8_forward(const mxmoe_int8_layer_t* L, const void* x, int6
   if (ws_bytes < w.total) return MXMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace& b = w.base;
-  if (run_routing(&R, x, T, MXMOE_BF16, b, ws, topk_idx_out, topk_w_out, nullptr, nullptr, nullptr, nullptr, s) !=
-      hipSuccess)
+  const bool prefill = use_prefill(&R, T, ACT_INT8);
+  if (run_routing(&R, x, T, MXMOE_BF16, b, ws, topk_idx_out, topk_w_out, nullptr, nullptr, nullptr, nullptr, s,
+                  nullptr, false, nullptr, 1.0f, prefill) != hipSuccess)
     return MXMOE_ERR_HIP;
   // per-token int8 x
   if (launch_quant_rows_int8(static_cast<const uint16_t*>(x), T, L->H, at<int8_t>(ws, w.xq), at<float>(ws, w.sx), s) !=
@@ -782,7 +811,6 @@ mxmoe_status_t moe_int8_forward(const mxmoe_int8_layer_t* L, const void* x, int6
     return MXMOE_ERR_HIP;
   // gate_up + SwiGLU -> h (bf16); decode-shaped batches take the decode
   // tile and fold the combine into the down GEMM, as the MXFP4 forward
-  const bool prefill = use_prefill(&R, T, ACT_INT8);
   const bool fold = !prefill && T <= kFusedCombineTokens && T * L->top_k * int64_t(L->H) * 2 <= kMaxWindow;
   GemmArgs g0 = gemm_args(&R, b, ws, T, ACT_INT8, 0);
   g0.bsrc = at<void>(ws, w.xq);
@@ -792,6 +820,10 @@ mxmoe_status_t moe_int8_forward(const mxmoe_int8_layer_t* L, const void* x, int6
   g1.bsrc = at<void>(ws, w.hq);
   g1.row_scale = L->down_scale;
   g1.tok_scale = at<float>(ws, w.sh);
+  if (prefill) {  // the grouping resolved every prefill workgroup's item
+    g0.blk_rec = at<int4>(ws, b.rec0);
+    g1.blk_rec = at<int4>(ws, b.rec1);
+  }
   if (fold) {
     g0.cmb_count = g1.cmb_count = at<uint32_t>(ws, b.cmb);
     g0.n_cmb = g1.n_cmb = (L->H + 63) / 64;

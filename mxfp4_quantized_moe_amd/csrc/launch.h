@@ -29,6 +29,25 @@ enum Act : int { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2, ACT_W8A8 = 3, ACT_INT8 
 constexpr int kPrefillRows = MXMOE_PREFILL_ROWS;
 constexpr int kPrefillTokens = MXMOE_PREFILL_TOKENS;
 
+// Estimated cost of streaming one weight stripe, in units of one 16-token
+// sub-tile's MFMA work (splits the tiled kernel's items over the XCDs).
+#ifndef MXMOE_TILE_COST
+#define MXMOE_TILE_COST 4
+#endif
+constexpr int kTileCost = MXMOE_TILE_COST;
+
+// Rows per workgroup (64 per wave) of the tiled-order prefill kernel.
+#ifndef MXMOE_PREFILL_TILED_ROWS
+#define MXMOE_PREFILL_TILED_ROWS 256
+#endif
+constexpr int kTiledRows = MXMOE_PREFILL_TILED_ROWS;
+
+// Workgroups of a tiled prefill launch over R weight rows with at most
+// max_tiles token tiles: 8 G, G per XCD.
+__host__ __device__ inline int64_t tiled_prefill_blocks(int R, int max_tiles) {
+  return (int64_t(max_tiles) * ((R + kTiledRows - 1) / kTiledRows) + 7) / 8 * 8;
+}
+
 hipError_t launch_unpack(const uint8_t* blocks, const uint8_t* scales, int64_t nblocks, void* out, bool out_bf16,
                          hipStream_t stream);
 hipError_t launch_pack(const void* w, bool in_bf16, int64_t nblocks, uint8_t* blocks, uint8_t* scales,
@@ -54,6 +73,14 @@ struct PermuteArgs {
   int4* tiles;          // (tile_off[E]): {expert, first sorted row, tokens, 0} per prefill tile
   int32_t* counts_out;  // optional copies
   int32_t* offsets_out;
+  // Optional: the work item of every workgroup of the two tiled prefill
+  // launches that follow (gate_up, down), resolved here: blk_rec[g][b] =
+  // {expert, first sorted row, tokens, row stripe} for workgroup b, tokens
+  // 0 for a workgroup without an item; rec_stripes[g] row stripes and
+  // rec_blocks[g] workgroups (tiled_prefill_blocks).
+  int4* blk_rec[2];
+  int rec_stripes[2];
+  int rec_blocks[2];
 };
 struct RouteArgs {
   const void* x;        // (T, H) act dtype
@@ -140,6 +167,9 @@ struct GemmArgs {
   const int32_t* pos;         // down: (T*k) sorted row of each routed slot
   const float* wts;           // down: (T, k) routing weights
   int T;                      // tokens of the batch (no expert sees more)
+  // tiled prefill launch: each workgroup's item resolved by the grouping
+  // (PermuteArgs::blk_rec); null: the workgroup resolves it itself
+  const int4* blk_rec;
 };
 constexpr int kFusedCombineTokens = 64;
 hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream);

@@ -11,6 +11,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "topk.h"
+#include "xcd_split.h"
 
 namespace mxmoe {
 
@@ -84,6 +85,9 @@ __device__ __forceinline__ void topk_softmax(const RouteArgs& a, const float* lg
 
 // The grouping of one workgroup of kPermThreads threads (defined below).
 __device__ void permute_block(const PermuteArgs& a);
+
+// The work items of the tiled prefill launches that follow (defined below).
+__device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_lo, int e_hi, bool write_empty);
 
 // The top-k, softmax and grouping of a batch of at most 16 tokens and 64
 // experts, by the router's one workgroup (defined below).
@@ -357,6 +361,7 @@ __device__ void permute_block(const PermuteArgs& a) {
     for (int j = 0; j * kPrefillTokens < c; ++j)
       a.tiles[t0 + j] = make_int4(e, off[e] + j * kPrefillTokens, min(kPrefillTokens, c - j * kPrefillTokens), 0);
   }
+  write_item_records(a, cnt, 0, E, true);
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = 0; base < N; base += kPermThreads) {
@@ -402,6 +407,92 @@ __device__ void permute_block(const PermuteArgs& a) {
 }
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) { permute_block(a); }
+
+// The work item of every workgroup of the tiled prefill launches that
+// follow (PermuteArgs::blk_rec), resolved once here instead of by each
+// workgroup: the per-expert prefixes of token tiles, sorted rows and
+// per-stripe costs (wave 0, 4 experts per lane), the XCD ranges
+// (xcd_split.h), then one record per item of experts [e_lo, e_hi) at the
+// workgroup that takes it, and (write_empty) an empty record for every
+// workgroup past its XCD's range.  cnt: the experts' counts in LDS.  Every
+// thread of the workgroup calls it.
+__device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_lo, int e_hi, bool write_empty) {
+  if (!a.blk_rec[0] && !a.blk_rec[1]) return;  // uniform
+  __shared__ int s_tp[257], s_wp[257], s_cp[257], s_bx[9];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E;
+  if (wave == 0) {
+    int tc[4], wc[4], cc[4], ts = 0, ws = 0, cs = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      const int n = e < E ? cnt[e] : 0;
+      tc[j] = (n + kPrefillTokens - 1) / kPrefillTokens;
+      wc[j] = e < E ? expert_stripe_cost(n) : 0;
+      cc[j] = n;
+      ts += tc[j];
+      ws += wc[j];
+      cs += cc[j];
+    }
+    int ttot, wtot, ctot;
+    int tb = wave_excl_scan(ts, lane, &ttot), wb = wave_excl_scan(ws, lane, &wtot), cb = wave_excl_scan(cs, lane, &ctot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      if (e < E) {
+        s_tp[e] = tb;
+        s_wp[e] = wb;
+        s_cp[e] = cb;
+      }
+      tb += tc[j];
+      wb += wc[j];
+      cb += cc[j];
+    }
+    if (lane == 0) {
+      s_tp[E] = ttot;
+      s_wp[E] = wtot;
+      s_cp[E] = ctot;
+    }
+  }
+  __syncthreads();
+  for (int gi = 0; gi < 2; ++gi) {
+    int4* rec = a.blk_rec[gi];
+    if (!rec) continue;  // uniform
+    const int ns = a.rec_stripes[gi], nblk = a.rec_blocks[gi];
+    const int nvalid = s_tp[E] * ns;
+    if (wave == 0) {
+      int bx[9];
+      xcd_bounds(s_wp, s_tp, E, ns, nblk >> 3, nvalid, lane, bx);
+      if (lane == 0) {
+#pragma unroll
+        for (int xx = 0; xx < 9; ++xx) s_bx[xx] = bx[xx];
+      }
+    }
+    __syncthreads();
+    const int i1 = s_tp[e_hi] * ns;
+    for (int item = s_tp[e_lo] * ns + tid; item < i1; item += kPermThreads) {
+      int lo = e_lo, hi = e_hi;  // s_tp[lo] * ns <= item < s_tp[hi] * ns
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tp[mid] * ns <= item) lo = mid;
+        else hi = mid;
+      }
+      const int nt = s_tp[lo + 1] - s_tp[lo];
+      const int local = item - s_tp[lo] * ns;
+      const int st = local / nt, q = local - st * nt;
+      int x = 0;
+      while (x < 7 && item >= s_bx[x + 1]) ++x;
+      rec[8 * (item - s_bx[x]) + x] =
+          make_int4(lo, s_cp[lo] + q * kPrefillTokens, min(kPrefillTokens, cnt[lo] - q * kPrefillTokens), st);
+    }
+    if (write_empty)
+      for (int b = tid; b < nblk; b += kPermThreads) {
+        const int x = b & 7;
+        if ((b >> 3) >= s_bx[x + 1] - s_bx[x]) rec[b] = make_int4(0, 0, 0, 0);
+      }
+    __syncthreads();
+  }
+}
 
 // A batch of at most 16 tokens (E <= 64, one router workgroup of 16
 // waves, logits final in `part`).  Wave t takes token t with lane e on
@@ -595,6 +686,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
   }
   for (int j = tid; j * kPrefillTokens < c_me; j += kPermThreads)
     a.tiles[toff_me + j] = make_int4(me, off_me + j * kPrefillTokens, min(kPrefillTokens, c_me - j * kPrefillTokens), 0);
+
+  write_item_records(a, cnt, me, me + 1, me == 0);
 
   // stable positions of this expert's slots
   const int per_wave = ((N + kPermWaves - 1) / kPermWaves + 63) & ~63;
