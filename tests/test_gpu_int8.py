@@ -116,6 +116,23 @@ def test_int8_20b_decode_sizes(dev, T):
     _check(case, _run(case, dev))
 
 
+@pytest.mark.parametrize("seed,E,k,T", [
+    (226, 8, 2, 60),    # one 16-token sub-tile per pass; experts with 32, 39 and 49 tokens
+    (205, 32, 4, 100),  # two sub-tiles per pass (more than 64 tokens); 19 and 100 tokens
+])
+def test_int8_decode_many_tokens_per_expert(dev, seed, E, k, T):
+    """Decode-shaped INT8 batches with a strongly biased router: experts past
+    one token pass and with 17..32 tokens, on the int8 decode tile."""
+    case = W.int8_case(seed, E, 128, 96, k, T, router_bias_std=3.0)
+    L = case.layer
+    idx, _, _ = O.route(O.bf16_from_bits(case.x), O.bf16_from_bits(L.router_w), O.bf16_from_bits(L.router_b), k)
+    cnt = np.bincount(idx.ravel(), minlength=E)
+    assert T * k <= 16 * min(E, T * k)
+    assert cnt.max() > 32 and np.any((cnt > 16) & (cnt <= 32))
+    note(f"{case.name} counts {sorted(cnt.tolist())}")
+    _check(case, _run(case, dev))
+
+
 def test_int8_20b_full_size(dev):
     """T=2048 at the 20b shape: routing and the output of every token."""
     case = W.int8_20b(2048)

@@ -264,6 +264,31 @@ def test_decode_kernels_many_tokens_per_expert(dev, seed, T, act, fp8, layout):
     check_layer(case, res, tol=1e-4 if act == "f32" else None, **kw)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_two_subtile_passes(dev, fp8):
+    """A decode-shaped batch of more than 64 tokens (T=100, E=32, top-4)
+    takes the decode tile with two 16-token sub-tiles per pass; a strongly
+    biased router puts 100 tokens on some experts (four passes of 32) and
+    17..32 on others (one two-sub-tile pass), and the combine is not folded
+    (more than 64 tokens)."""
+    T = 100
+    case = W.small_case(103, 32, 128, 96, 4, T, act_dtype="bf16", fp8=fp8, router_bias_std=3.0)
+    L = case.layer
+    idx, _, _ = O.route(O.widen(case.x, "bf16"), O.widen(L.router_w, "bf16"), O.widen(L.router_b, "bf16"), L.top_k)
+    cnt = np.bincount(idx.ravel(), minlength=L.E)
+    assert T * L.top_k <= 16 * min(L.E, T * L.top_k)
+    assert cnt.max() > 64 and np.any((cnt > 16) & (cnt <= 32))
+    kw = {}
+    if fp8:
+        s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+        kw = dict(x_scale=s_x, h_scale=s_h)
+    note(f"{case.name} tiled {'fp8' if fp8 else 'bf16'} counts {sorted(cnt.tolist())}")
+    res, _, _ = run_gpu(case, dev, layout="tiled", want_route=not fp8, **kw)
+    if not fp8:
+        check_perm(case, res["route"])
+    check_layer(case, res, **kw)
+
+
 def test_empty_batch_is_noop(dev):
     import torch
     import mxfp4_quantized_moe_amd as mx

@@ -305,9 +305,9 @@ class Int8Case:
         return self.x.shape[0]
 
 
-def int8_case(seed: int, E: int, H: int, I: int, top_k: int, T: int) -> Int8Case:
+def int8_case(seed: int, E: int, H: int, I: int, top_k: int, T: int, router_bias_std: float = 0.01) -> Int8Case:
     rng = np.random.default_rng(seed)
-    layer = int8_layer(rng, E, H, I, top_k)
+    layer = int8_layer(rng, E, H, I, top_k, router_bias_std=router_bias_std)
     x = _real(rng, (T, H), 1.0, BF16)
     return Int8Case(f"int8_s{seed}_e{E}_h{H}_i{I}_k{top_k}_t{T}", layer, x)
 
