@@ -722,7 +722,10 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     constexpr int NA = decltype(ntc)::value;  // 1 .. 8 active sub-tiles
     constexpr bool SMALL = decltype(smc)::value != 0;
     constexpr int SX = SMALL ? SS : S;           // stages of the ring
-    constexpr int BL = SMALL ? SBLOADS : BLOADS;  // B loads per wave per chunk
+    // B loads per wave per chunk: only the tile's 16 NA active token rows
+    // (loads past ntok would read zeros), spread over the waves
+    constexpr int BL = (16 * NA + TPL * kTiledWaves - 1) / (TPL * kTiledWaves);
+    static_assert(BL <= (SMALL ? SBLOADS : BLOADS), "the active rows fit the stage");
     constexpr int LD = (W8 ? 2 * RT : RT + 1) + BL;  // VMEM instructions per wave per chunk
     static_assert(!SMALL || (ACT == ACT_BF16 && NA <= 4), "small ring: bf16 tiles of <= 64 tokens");
     auto stage = [&](auto uc) -> uint8_t* {
@@ -730,8 +733,8 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
       else return stage_b(uc);
     };
 
-    // B DMA: the tile's 128 (64 in the small ring) tokens are loads of TPL
-    // tokens; wave w carries loads BL*w .. BL*w + BL-1; lane i carries token
+    // B DMA: the tile's first 16 NA token rows are loads of TPL tokens;
+    // wave w carries loads BL*w .. BL*w + BL-1; lane i carries token
     // TPL*load + i/PPR, piece slot i%PPR, XOR-swizzled by token
     // (bf16_piece_pos for bf16).  (clast: the last chunk whose part of this
     // piece lies inside K)
