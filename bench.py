@@ -357,7 +357,7 @@ def bench_layer(args, dev):
         achieved = fl / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
         algo = f"{fl} flop per launch"
-    roof["kernel"] = gate_up_kernel_name(case, decode_shaped, args.layout == "tiled")
+    roof["kernel"] = gate_up_kernel_name(case, decode_shaped, args.layout == "tiled", dense)
     roof["launches_timed"] = f"{len(gu_ms)} of the {args.steps} timed eager steps (every {EV_EVERY}th)"
     roof["algorithmic"] = algo
     roof["traffic"] = measured_traffic(args.workload, roof["kernel"]) if not dense else None
@@ -630,17 +630,33 @@ def bench_int8(args, dev):
             "roofline": roof}
 
 
-def gate_up_kernel_name(case, decode_shaped: bool, tiled: bool) -> str:
+# The library's rule for a persistent tiled prefill launch (moe_gemm.hip):
+# at least PERSIST_MIN item records per workgroup of the PERSIST_BLOCKS.
+PERSIST_MIN, PERSIST_BLOCKS, TILED_ROWS, TILE_TOKENS = 4, 512, 256, 128
+
+
+def prefill_persistent(case, R: int) -> bool:
+    """Whether the routed, tiled prefill GEMM over R weight rows runs as a
+    persistent launch (its record grid: max token tiles x row stripes)."""
+    rows = case.T * case.layer.top_k
+    max_tiles = -(-rows // TILE_TOKENS) + min(rows, case.layer.E)
+    blocks = -(-(max_tiles * -(-R // TILED_ROWS)) // 8) * 8
+    return blocks >= PERSIST_MIN * PERSIST_BLOCKS
+
+
+def gate_up_kernel_name(case, decode_shaped: bool, tiled: bool, dense: bool = False) -> str:
     """The gate_up kernel the library launches for this case, as rocprofv3
     names it (template arguments: activation code, phase, then token
-    sub-tiles per pass (decode, tiled) or tiled (row order))."""
+    sub-tiles per pass (decode, tiled), persistent launch (prefill, tiled)
+    or tiled (row order))."""
     act = 2 if case.fp8 else (1 if case.act_dtype == "bf16" else 0)
     if decode_shaped:
         if tiled and act != 0:
             return f"mxmoe::gemm_decode_tiled_kernel<{act}, 0, {1 if case.T <= 64 else 2}>"
         return f"mxmoe::gemm_decode_kernel<{act}, 0, {'true' if tiled else 'false'}>"
     if tiled:
-        return f"mxmoe::gemm_prefill_tiled_kernel<{act}, 0>"
+        persist = not dense and prefill_persistent(case, 2 * case.layer.I)
+        return f"mxmoe::gemm_prefill_tiled_kernel<{act}, 0, {'true' if persist else 'false'}>"
     return f"mxmoe::gemm_prefill_kernel<{act}, 0, false>"
 
 

@@ -32,7 +32,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Workspace {
-  size_t idx, wts, counts, offsets, active, tile_off, tiles, rec0, rec1, sorted, sorted_tok, pos, cmb, calib, xq, h, y,
+  size_t idx, wts, counts, offsets, active, tile_off, tiles, rec0, rec1, heads, sorted, sorted_tok, pos, cmb, calib, xq,
+      h, y,
       total;
 };
 
@@ -65,6 +66,7 @@ Workspace layout(int E, int H, int I, int k, int64_t T, int act_dtype, bool fp8,
   // down (H rows) launches
   w.rec0 = take(size_t(tiled_prefill_blocks(2 * I, max_tiles)) * 16);
   w.rec1 = take(size_t(tiled_prefill_blocks(H, max_tiles)) * 16);
+  w.heads = take(2 * 8 * 4);  // their per-XCD list counters (persistent launches)
   w.sorted = take(slots * 4);
   w.sorted_tok = take(grows * 4);
   w.pos = take(slots * 4);
@@ -200,6 +202,8 @@ hipError_t run_routing(const mxmoe_layer_t* L, const void* x, int64_t T, int act
     const int max_tiles = int((rows + kPrefillTokens - 1) / kPrefillTokens + (rows < L->E ? rows : L->E));
     pa.blk_rec[0] = at<int4>(ws, w.rec0);
     pa.blk_rec[1] = at<int4>(ws, w.rec1);
+    pa.rec_head[0] = at<uint32_t>(ws, w.heads);
+    pa.rec_head[1] = at<uint32_t>(ws, w.heads) + 8;
     pa.rec_stripes[0] = (2 * L->I + kTiledRows - 1) / kTiledRows;
     pa.rec_stripes[1] = (L->H + kTiledRows - 1) / kTiledRows;
     pa.rec_blocks[0] = int(tiled_prefill_blocks(2 * L->I, max_tiles));
@@ -315,6 +319,8 @@ mxmoe_status_t forward_impl(const mxmoe_layer_t* L, const void* x, int64_t T, vo
   if (records) {
     g0.blk_rec = at<int4>(ws, w.rec0);
     g1.blk_rec = at<int4>(ws, w.rec1);
+    g0.item_head = at<uint32_t>(ws, w.heads);
+    g1.item_head = at<uint32_t>(ws, w.heads) + 8;
   }
   if (fold) {
     g0.cmb_count = g1.cmb_count = at<uint32_t>(ws, w.cmb);
@@ -465,7 +471,10 @@ mxmoe_status_t moe_mxfp4_calibrate_fp8(const mxmoe_layer_t* L, const void* x, in
   if (e != hipSuccess) return MXMOE_ERR_HIP;
   GemmArgs g0 = gemm_args(L, w, ws, T, ACT_BF16, 0);
   g0.bsrc = x;
-  if (records) g0.blk_rec = at<int4>(ws, w.rec0);
+  if (records) {
+    g0.blk_rec = at<int4>(ws, w.rec0);
+    g0.item_head = at<uint32_t>(ws, w.heads);
+  }
   if (launch_moe_gemm(g0, prefill, s) != hipSuccess) return MXMOE_ERR_HIP;
   uint32_t* slots = at<uint32_t>(ws, w.calib);
   if (launch_calib_init(slots, s) != hipSuccess) return MXMOE_ERR_HIP;
@@ -823,6 +832,8 @@ mxmoe_status_t moe_int8_forward(const mxmoe_int8_layer_t* L, const void* x, int6
   if (prefill) {  // the grouping resolved every prefill workgroup's item
     g0.blk_rec = at<int4>(ws, b.rec0);
     g1.blk_rec = at<int4>(ws, b.rec1);
+    g0.item_head = at<uint32_t>(ws, b.heads);
+    g1.item_head = at<uint32_t>(ws, b.heads) + 8;
   }
   if (fold) {
     g0.cmb_count = g1.cmb_count = at<uint32_t>(ws, b.cmb);

@@ -81,6 +81,10 @@ struct PermuteArgs {
   int4* blk_rec[2];
   int rec_stripes[2];
   int rec_blocks[2];
+  // optional: the 8 per-XCD list counters of each of those launches, set
+  // here past the first item of each persistent workgroup
+  // (GemmArgs::item_head)
+  uint32_t* rec_head[2];
 };
 struct RouteArgs {
   const void* x;        // (T, H) act dtype
@@ -170,7 +174,14 @@ struct GemmArgs {
   // tiled prefill launch: each workgroup's item resolved by the grouping
   // (PermuteArgs::blk_rec); null: the workgroup resolves it itself
   const int4* blk_rec;
+  // with blk_rec: 8 list counters (PermuteArgs::rec_head) for a persistent
+  // launch of kPersistentBlocks workgroups that take the records as work
+  // lists; null: one workgroup per record
+  uint32_t* item_head;
 };
+// Workgroups of a persistent tiled prefill launch: two per CU of the
+// 256-CU gfx950 parts.
+constexpr int kPersistentBlocks = 512;
 constexpr int kFusedCombineTokens = 64;
 hipError_t launch_moe_gemm(const GemmArgs& a, bool prefill, hipStream_t stream);
 

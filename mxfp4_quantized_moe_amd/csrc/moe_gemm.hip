@@ -566,8 +566,37 @@ constexpr int kTiledThreads = 64 * kTiledWaves;
 #define MXMOE_PREFILL_TILED_STAGES_FP8 2
 #endif
 
-template <int ACT, int PHASE>
-__global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefill_tiled_kernel(GemmArgs a) {
+// Lists a persistent prefill workgroup takes items from: its own XCD's, then
+// (when 8) the other XCDs' in turn.
+#ifndef MXMOE_PERSIST_LISTS
+#define MXMOE_PERSIST_LISTS 1
+#endif
+constexpr int kPersistLists = MXMOE_PERSIST_LISTS;
+// Item records per workgroup from which a tiled prefill launch goes
+// persistent.
+#ifndef MXMOE_PERSIST_MIN
+#define MXMOE_PERSIST_MIN 4
+#endif
+constexpr int kPersistMin = MXMOE_PERSIST_MIN;
+
+// The kernel's GemmArgs argument (the first in its argument segment),
+// loaded through a pointer that is opaque to the optimiser.
+typedef const __attribute__((address_space(4))) GemmArgs* kernarg_args_t;
+template <bool OPAQUE>
+__device__ __forceinline__ GemmArgs item_args(const GemmArgs& args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (OPAQUE) {
+    kernarg_args_t p = (kernarg_args_t)__builtin_amdgcn_kernarg_segment_ptr();
+    __asm__ __volatile__("" : "+s"(p));
+    return *p;
+  }
+#endif
+  return args;
+}
+
+// PERSIST: a persistent launch (below); a.item_head is set exactly then.
+template <int ACT, int PHASE, bool PERSIST>
+__global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefill_tiled_kernel(GemmArgs args) {
   static_assert(ACT == ACT_BF16 || ACT == ACT_FP8 || ACT == ACT_W8A8 || ACT == ACT_INT8,
                 "prefill path takes bf16, fp8 or int8 activations");
   static_assert(ACT != ACT_W8A8 || PHASE == 1, "FP8 weights: dense layer epilogue only");
@@ -608,363 +637,412 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     return (u < 2 ? sB0 : sB1) + (u & 1) * (B_BYTES / 2);
   };
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, r16 = lane & 15;
-
   // Work items (expert, row stripe, token tile), split over the XCDs as
-  // xcd_split.h describes; the grouping may have resolved this workgroup's
-  // item already (one record load instead of the scan and searches below).
+  // xcd_split.h describes.  A persistent launch (a.item_head set, with the
+  // grouping's item records) holds two workgroups per CU; each takes items
+  // one after another from its XCD's record list through a device-scope
+  // counter, so no slot waits for the dispatcher between items.  (Taking
+  // items from the other XCDs' lists once its own is exhausted,
+  // kPersistLists 8, measured slower: their experts' weights miss in this
+  // XCD's L2.)  Otherwise each workgroup runs one item: its record, or one
+  // it resolves itself (one record load instead of the scan and searches
+  // below).
   const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3, G = gridDim.x >> 3;
-  const int nstripes = (a.R + kTiledRows - 1) / kTiledRows;
-  int e, row_start, ntok, stripe;
-  if (a.blk_rec) {
-    const int4 r = a.blk_rec[blockIdx.x];
-    hold_uniform(r);
-    if (r.z == 0) return;  // no item: uniform per workgroup
-    e = r.x;
-    row_start = r.y;
-    ntok = r.z;
-    stripe = r.w;
-  } else {
-    const int nvalid = a.tile_off[a.E] * nstripes;
-    __shared__ int s_toff[257];  // E <= 256, checked on the host
-    __shared__ int s_woff[257];  // prefix of the experts' per-stripe costs
-    __shared__ int s_wtot[kTiledWaves];
-    static_assert(kTiledThreads >= 256, "one thread per expert");
-    int tile;
-    if (a.E == 1) {
-      // One weight matrix (a dense linear): stripe fastest instead, so each
-      // XCD reads an eighth of the activations, which outweigh the 4- or
-      // 8-bit weights, rather than all of them.  Its tiles are full but the
-      // last, so equal item counts are equal work.
-      const int per_xcd = (nvalid + 7) >> 3;
-      const int item = xcd * per_xcd + idx;
-      if (idx >= per_xcd || item >= nvalid) return;  // uniform per workgroup
-      tile = item / nstripes;
-      stripe = item - tile * nstripes;
+  __shared__ int4 s_rec;
+  int kq = 0;  // thread 0 of a persistent workgroup: lists (xcd + 0 .. kq-1) & 7 are exhausted
+  for (bool first_item = true;; first_item = false) {
+    // The arguments and the lane's constants are produced anew for each
+    // item (the arguments re-read from the kernel's argument segment through
+    // a pointer the compiler cannot follow across items): the values derived
+    // from them then live inside one item instead of being hoisted out of
+    // the loop and held, and spilled, across all of it.
+    const GemmArgs a = item_args<PERSIST>(args);
+    uint32_t tid = threadIdx.x;
+    if constexpr (PERSIST) hold(tid);
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, r16 = lane & 15;
+    const int nstripes = (a.R + kTiledRows - 1) / kTiledRows;
+    int e, row_start, ntok, stripe;
+    if constexpr (PERSIST) {
+      if (threadIdx.x == 0) {
+        const int gr = int(tiled_prefill_blocks(a.R, a.max_tiles) >> 3);  // records per XCD
+        int4 r = make_int4(0, 0, 0, 0);
+        // The first item is fixed, list position idx of the workgroup's XCD
+        // (the counters start past the G of them); later ones come from the
+        // counters.
+        if (first_item && idx < gr) r = a.blk_rec[8 * idx + xcd];
+        if (r.z == 0) {
+          for (; kq < kPersistLists; ++kq) {
+            const int y = (xcd + kq) & 7;
+            const uint32_t q = add_dev(a.item_head + y, 1u);
+            if (q < uint32_t(gr)) {
+              r = a.blk_rec[8 * q + y];
+              if (r.z != 0) break;  // list y still has items: start there next time
+            }
+          }
+        }
+        s_rec = r;
+      }
+      // also the barrier between this workgroup's items: the new item's DMAs
+      // reuse LDS the previous one read
+      __syncthreads();
+      const int4 r = s_rec;
+      ntok = __builtin_amdgcn_readfirstlane(r.z);
+      if (ntok == 0) return;  // every list exhausted: uniform per workgroup
+      e = __builtin_amdgcn_readfirstlane(r.x);
+      row_start = __builtin_amdgcn_readfirstlane(r.y);
+      stripe = __builtin_amdgcn_readfirstlane(r.w);
+    } else if (a.blk_rec) {
+      const int4 r = a.blk_rec[blockIdx.x];
+      hold_uniform(r);
+      if (r.z == 0) return;  // no item: uniform per workgroup
+      e = r.x;
+      row_start = r.y;
+      ntok = r.z;
+      stripe = r.w;
     } else {
-      // per-stripe costs of the experts: block-wide scan
-      const int t = threadIdx.x;
-      const int c = t < a.E ? expert_stripe_cost(a.offsets[t + 1] - a.offsets[t]) : 0;
-      for (int i = t; i <= a.E; i += kTiledThreads) s_toff[i] = a.tile_off[i];
-      int x = c;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      if (lane == 63) s_wtot[wave] = x;
-      __syncthreads();
-      for (int w = 0; w < wave; ++w) x += s_wtot[w];
-      if (t < a.E) s_woff[t + 1] = x;
-      if (t == 0) s_woff[0] = 0;
-      __syncthreads();
-      int bx[9];
-      xcd_bounds(s_woff, s_toff, a.E, nstripes, G, nvalid, lane, bx);
-      int first = bx[0], last = bx[1];
-#pragma unroll
-      for (int xx = 1; xx < 8; ++xx)
-        if (xcd == xx) {
-          first = bx[xx];
-          last = bx[xx + 1];
-        }
-      const int item = first + idx;
-      if (item >= last) return;  // uniform per workgroup
-      // Expert e owns items [tile_off[e], tile_off[e+1]) * nstripes
-      int lo = 0, hi = a.E;  // s_toff[lo] * nstripes <= item < s_toff[hi] * nstripes
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_toff[mid] * nstripes <= item) lo = mid;
-        else hi = mid;
-      }
-      const int nt_e = s_toff[lo + 1] - s_toff[lo];
-      const int local = item - s_toff[lo] * nstripes;
-      stripe = local / nt_e;
-      tile = s_toff[lo] + (local - stripe * nt_e);
-    }
-    const int4 ti = a.tiles[tile];  // {expert, first sorted row, tokens}
-    e = ti.x;
-    row_start = ti.y;
-    ntok = ti.z;
-  }
-  const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
-  const int nb = a.nb, K = nb * 32;
-  const WBuf wb = W8 ? byte_weights(a, e) : expert_weights<true>(a, e);
-  const int nc = wb.nc;
-  const int grow = stripe * kTiledRows + wave * (16 * RT);  // first row of this wave
-  const int t0 = grow >> 4;                                   // its first row tile (a scale group start)
-  const int rt_active = max(0, min(RT, (a.R - grow) >> 4));
-  const bool busy = rt_active > 0;  // wave-uniform
-  const bool wok = t0 < wb.rt4;
-  const uint32_t row_bytes = uint32_t(K) * EB;
-  const rsrc_t bsrc = act_rows(a, PHASE, row_start, ntok, row_bytes);
-  const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
-
-  // The workgroup's kTiledRows bias values go to LDS by one DMA of wave 0,
-  // issued before every chunk load: the first chunk's wait covers it and the
-  // first barrier publishes it, so the epilogue finds it without a memory
-  // round trip (lanes past the stripe read zeros).
-  __shared__ __align__(16) uint8_t sBias[1024];
-  static_assert(kTiledRows * 2 <= 1024, "one DMA covers the stripe's bias");
-  if (wave == 0) {
-    const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
-    const int r = stripe * kTiledRows + 8 * lane;
-    dma16(br, (8 * lane < kTiledRows && r < a.R) ? uint32_t(r) * 2u : kOOB, sBias);
-  }
-  auto barrier = [&]() __attribute__((always_inline)) {
-    order_point();
-    __builtin_amdgcn_s_barrier();
-    order_point();
-  };
-
-  auto main_loop = [&](auto ntc, auto smc) __attribute__((always_inline)) {
-    constexpr int NA = decltype(ntc)::value;  // 1 .. 8 active sub-tiles
-    constexpr bool SMALL = decltype(smc)::value != 0;
-    constexpr int SX = SMALL ? SS : S;           // stages of the ring
-    // B loads per wave per chunk: only the tile's 16 NA active token rows
-    // (loads past ntok would read zeros), spread over the waves
-    constexpr int BL = (16 * NA + TPL * kTiledWaves - 1) / (TPL * kTiledWaves);
-    static_assert(BL <= (SMALL ? SBLOADS : BLOADS), "the active rows fit the stage");
-    constexpr int LD = (W8 ? 2 * RT : RT + 1) + BL;  // VMEM instructions per wave per chunk
-    static_assert(!SMALL || (ACT == ACT_BF16 && NA <= 4), "small ring: bf16 tiles of <= 64 tokens");
-    auto stage = [&](auto uc) -> uint8_t* {
-      if constexpr (SMALL) return stage_small(uc);
-      else return stage_b(uc);
-    };
-
-    // B DMA: the tile's first 16 NA token rows are loads of TPL tokens;
-    // wave w carries loads BL*w .. BL*w + BL-1; lane i carries token
-    // TPL*load + i/PPR, piece slot i%PPR, XOR-swizzled by token
-    // (bf16_piece_pos for bf16).  (clast: the last chunk whose part of this
-    // piece lies inside K)
-    uint32_t boff[BL];
-    int clast[BL];
-#pragma unroll
-    for (int jj = 0; jj < BL; ++jj) {
-      const int tok = TPL * (BL * wave + jj) + lane / PPR;
-      const int slot = lane % PPR;
-      const int p = ACT == ACT_BF16 ? bf16_piece_pos(tok, slot) : (slot ^ ((tok >> 1) & 7));
-      clast[jj] = (K - 1 - p * (16 / EB)) >> 7;
-      const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
-      boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
-    }
-    uint4 aq[SX][RT];   // weight pieces per stage
-    uint4 aq2[W8 ? SX : 1][RT];  // FP8 weights: the second 16 bytes of a lane's piece
-    uint32_t sw[SX];    // scale dword per stage
-
-    // weights and scales of chunk c into register stage u
-    auto issue_w = [&](int c, auto stc) __attribute__((always_inline)) {
-      constexpr int u = decltype(stc)::value;
-      const bool cok = c < nc && wok;
-      if constexpr (W8) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const uint32_t o = cok ? uint32_t(((t0 + rt) * nc + c) * 2048 + lane * 32) : kOOB;
-          aq[u][rt] = buf_load_b128(wb.blk, o);
-          aq2[u][rt] = buf_load_b128(wb.blk, oob_add(o, 16u));
-        }
-        sw[u] = 0;
+      const int nvalid = a.tile_off[a.E] * nstripes;
+      __shared__ int s_toff[257];  // E <= 256, checked on the host
+      __shared__ int s_woff[257];  // prefix of the experts' per-stripe costs
+      __shared__ int s_wtot[kTiledWaves];
+      static_assert(kTiledThreads >= 256, "one thread per expert");
+      int tile;
+      if (a.E == 1) {
+        // One weight matrix (a dense linear): stripe fastest instead, so each
+        // XCD reads an eighth of the activations, which outweigh the 4- or
+        // 8-bit weights, rather than all of them.  Its tiles are full but the
+        // last, so equal item counts are equal work.
+        const int per_xcd = (nvalid + 7) >> 3;
+        const int item = xcd * per_xcd + idx;
+        if (idx >= per_xcd || item >= nvalid) return;  // uniform per workgroup
+        tile = item / nstripes;
+        stripe = item - tile * nstripes;
       } else {
+        // per-stripe costs of the experts: block-wide scan
+        const int t = threadIdx.x;
+        const int c = t < a.E ? expert_stripe_cost(a.offsets[t + 1] - a.offsets[t]) : 0;
+        for (int i = t; i <= a.E; i += kTiledThreads) s_toff[i] = a.tile_off[i];
+        int x = c;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          aq[u][rt] = buf_load_b128(wb.blk, cok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
-        sw[u] = buf_load_b32(wb.sc, cok ? uint32_t(((t0 >> 2) * nc + c) * 256 + lane * 4) : kOOB);
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(x, off);
+          if (lane >= off) x += y;
+        }
+        if (lane == 63) s_wtot[wave] = x;
+        __syncthreads();
+        for (int w = 0; w < wave; ++w) x += s_wtot[w];
+        if (t < a.E) s_woff[t + 1] = x;
+        if (t == 0) s_woff[0] = 0;
+        __syncthreads();
+        int bx[9];
+        xcd_bounds(s_woff, s_toff, a.E, nstripes, G, nvalid, lane, bx);
+        int first = bx[0], last = bx[1];
+#pragma unroll
+        for (int xx = 1; xx < 8; ++xx)
+          if (xcd == xx) {
+            first = bx[xx];
+            last = bx[xx + 1];
+          }
+        const int item = first + idx;
+        if (item >= last) return;  // uniform per workgroup
+        // Expert e owns items [tile_off[e], tile_off[e+1]) * nstripes
+        int lo = 0, hi = a.E;  // s_toff[lo] * nstripes <= item < s_toff[hi] * nstripes
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_toff[mid] * nstripes <= item) lo = mid;
+          else hi = mid;
+        }
+        const int nt_e = s_toff[lo + 1] - s_toff[lo];
+        const int local = item - s_toff[lo] * nstripes;
+        stripe = local / nt_e;
+        tile = s_toff[lo] + (local - stripe * nt_e);
       }
+      const int4 ti = a.tiles[tile];  // {expert, first sorted row, tokens}
+      e = ti.x;
+      row_start = ti.y;
+      ntok = ti.z;
+    }
+    const int na = (ntok + 15) >> 4;  // active 16-token sub-tiles
+    const int nb = a.nb, K = nb * 32;
+    const WBuf wb = W8 ? byte_weights(a, e) : expert_weights<true>(a, e);
+    const int nc = wb.nc;
+    const int grow = stripe * kTiledRows + wave * (16 * RT);  // first row of this wave
+    const int t0 = grow >> 4;                                   // its first row tile (a scale group start)
+    const int rt_active = max(0, min(RT, (a.R - grow) >> 4));
+    const bool busy = rt_active > 0;  // wave-uniform
+    const bool wok = t0 < wb.rt4;
+    const uint32_t row_bytes = uint32_t(K) * EB;
+    const rsrc_t bsrc = act_rows(a, PHASE, row_start, ntok, row_bytes);
+    const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
+
+    // The workgroup's kTiledRows bias values go to LDS by one DMA of wave 0,
+    // issued before every chunk load: the first chunk's wait covers it and the
+    // first barrier publishes it, so the epilogue finds it without a memory
+    // round trip (lanes past the stripe read zeros).
+    __shared__ __align__(16) uint8_t sBias[1024];
+    static_assert(kTiledRows * 2 <= 1024, "one DMA covers the stripe's bias");
+    if (wave == 0) {
+      const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
+      const int r = stripe * kTiledRows + 8 * lane;
+      dma16(br, (8 * lane < kTiledRows && r < a.R) ? uint32_t(r) * 2u : kOOB, sBias);
+    }
+    auto barrier = [&]() __attribute__((always_inline)) {
+      order_point();
+      __builtin_amdgcn_s_barrier();
+      order_point();
     };
-    // tokens of chunk c into LDS stage u
-    auto issue_b = [&](int c, auto stc) __attribute__((always_inline)) {
-      uint8_t* stb = stage(stc);
+
+    auto main_loop = [&](auto ntc, auto smc) __attribute__((always_inline)) {
+      constexpr int NA = decltype(ntc)::value;  // 1 .. 8 active sub-tiles
+      constexpr bool SMALL = decltype(smc)::value != 0;
+      constexpr int SX = SMALL ? SS : S;           // stages of the ring
+      // B loads per wave per chunk: only the tile's 16 NA active token rows
+      // (loads past ntok would read zeros), spread over the waves
+      constexpr int BL = (16 * NA + TPL * kTiledWaves - 1) / (TPL * kTiledWaves);
+      static_assert(BL <= (SMALL ? SBLOADS : BLOADS), "the active rows fit the stage");
+      constexpr int LD = (W8 ? 2 * RT : RT + 1) + BL;  // VMEM instructions per wave per chunk
+      static_assert(!SMALL || (ACT == ACT_BF16 && NA <= 4), "small ring: bf16 tiles of <= 64 tokens");
+      auto stage = [&](auto uc) -> uint8_t* {
+        if constexpr (SMALL) return stage_small(uc);
+        else return stage_b(uc);
+      };
+
+      // B DMA: the tile's first 16 NA token rows are loads of TPL tokens;
+      // wave w carries loads BL*w .. BL*w + BL-1; lane i carries token
+      // TPL*load + i/PPR, piece slot i%PPR, XOR-swizzled by token
+      // (bf16_piece_pos for bf16).  (clast: the last chunk whose part of this
+      // piece lies inside K)
+      uint32_t boff[BL];
+      int clast[BL];
 #pragma unroll
       for (int jj = 0; jj < BL; ++jj) {
-        const bool kok = c <= clast[jj];
-        dma16(bsrc, oob_add(boff[jj], kok ? uint32_t(c) * KB : kOOB), stb + (BL * wave + jj) * 1024);
+        const int tok = TPL * (BL * wave + jj) + lane / PPR;
+        const int slot = lane % PPR;
+        const int p = ACT == ACT_BF16 ? bf16_piece_pos(tok, slot) : (slot ^ ((tok >> 1) & 7));
+        clast[jj] = (K - 1 - p * (16 / EB)) >> 7;
+        const uint32_t r = act_row_offset(a, PHASE, row_start, tok, ntok, row_bytes);
+        boff[jj] = r == kOOB ? kOOB : r + uint32_t(16 * p);
       }
-    };
+      uint4 aq[SX][RT];   // weight pieces per stage
+      uint4 aq2[W8 ? SX : 1][RT];  // FP8 weights: the second 16 bytes of a lane's piece
+      uint32_t sw[SX];    // scale dword per stage
 
-    f32x4_t acc[RT][NA];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // compute stage u; mid() (the next chunk's token DMA) runs once, halfway
-    // through the MFMA steps, so the wave's loads do not all leave in one
-    // burst after the barrier (measured 1-3% faster on the full tiles)
-    auto compute = [&](auto stc, auto mid) __attribute__((always_inline)) {
-      constexpr int u = decltype(stc)::value;
-      if (!busy) mid();
-      if (busy) {
-        const uint8_t* sb = stage(stc);
-        uint32_t ascb[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) ascb[rt] = (sw[u] >> (((t0 + rt) & 3) * 8)) & 0xFFu;
-        if constexpr (ACT == ACT_BF16) {
-#pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            if (st == 2) mid();
-            bf16x8_t b[NA];
-#pragma unroll
-            for (int nt = 0; nt < NA; ++nt)
-              b[nt] = *reinterpret_cast<const bf16x8_t*>(sb + ((nt * 16 + r16) * 16 + bf16_piece_pos(r16, 4 * g + st)) * 16);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-              const bf16x8_t av = fp4x8_to_bf16x8(dword(aq[u][rt], st), e8m0_as_scale_operand(ascb[rt]));
-#pragma unroll
-              for (int nt = 0; nt < NA; ++nt)
-                acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nt], acc[rt][nt], 0, 0, 0);
-            }
-          }
-        } else {
-          // token fragments double-buffered by hand (sub-tile nt+1 is read
-          // before sub-tile nt's MFMAs; the order points keep the compiler
-          // from hoisting all of them, which would cost 8 registers each)
-          const int sw8 = (r16 >> 1) & 7;
-          auto load_b = [&](int nt) __attribute__((always_inline)) {
-            const uint8_t* rowp = sb + (nt * 16 + r16) * 128;
-            const uint4 p0 = *reinterpret_cast<const uint4*>(rowp + (g ^ sw8) * 16);
-            const uint4 p1 = *reinterpret_cast<const uint4*>(rowp + ((4 + g) ^ sw8) * 16);
-            return i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
-          };
-          i32x8_t av[RT];
+      // weights and scales of chunk c into register stage u
+      auto issue_w = [&](int c, auto stc) __attribute__((always_inline)) {
+        constexpr int u = decltype(stc)::value;
+        const bool cok = c < nc && wok;
+        if constexpr (W8) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            const uint4 q = aq[u][rt];
-            if constexpr (W8) {
-              const uint4 q2 = aq2[u][rt];
-              av[rt] = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), int(q2.x), int(q2.y), int(q2.z), int(q2.w)};
-            } else {
-              av[rt] = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
-            }
+            const uint32_t o = cok ? uint32_t(((t0 + rt) * nc + c) * 2048 + lane * 32) : kOOB;
+            aq[u][rt] = buf_load_b128(wb.blk, o);
+            aq2[u][rt] = buf_load_b128(wb.blk, oob_add(o, 16u));
           }
-          i32x8_t bcur = load_b(0);
+          sw[u] = 0;
+        } else {
 #pragma unroll
-          for (int nt = 0; nt < NA; ++nt) {
-            if (nt == NA / 2) mid();
-            i32x8_t bnext = bcur;
-            if (nt + 1 < NA) bnext = load_b(nt + 1);
-            order_point();
+          for (int rt = 0; rt < RT; ++rt)
+            aq[u][rt] = buf_load_b128(wb.blk, cok ? uint32_t(((t0 + rt) * nc + c) * 1024) + aslot : kOOB);
+          sw[u] = buf_load_b32(wb.sc, cok ? uint32_t(((t0 >> 2) * nc + c) * 256 + lane * 4) : kOOB);
+        }
+      };
+      // tokens of chunk c into LDS stage u
+      auto issue_b = [&](int c, auto stc) __attribute__((always_inline)) {
+        uint8_t* stb = stage(stc);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-              if constexpr (I8) {
-                // two K=64 halves (dwords 0-3, then 4-7 of both operands);
-                // the int32 sums live in the float accumulator registers
-                typedef int i32x4_t __attribute__((ext_vector_type(4)));
-                i32x4_t c = __builtin_bit_cast(i32x4_t, acc[rt][nt]);
-                c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_shufflevector(av[rt], av[rt], 0, 1, 2, 3),
-                                                         __builtin_shufflevector(bcur, bcur, 0, 1, 2, 3), c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_shufflevector(av[rt], av[rt], 4, 5, 6, 7),
-                                                         __builtin_shufflevector(bcur, bcur, 4, 5, 6, 7), c, 0, 0, 0);
-                acc[rt][nt] = __builtin_bit_cast(f32x4_t, c);
-              } else {
-                acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    av[rt], bcur, acc[rt][nt], W8 ? 0 : 4, 0, 0, W8 ? 127 : int(ascb[rt]), 0, 127);
+        for (int jj = 0; jj < BL; ++jj) {
+          const bool kok = c <= clast[jj];
+          dma16(bsrc, oob_add(boff[jj], kok ? uint32_t(c) * KB : kOOB), stb + (BL * wave + jj) * 1024);
+        }
+      };
+
+      f32x4_t acc[RT][NA];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NA; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+      // compute stage u; mid() (the next chunk's token DMA) runs once, halfway
+      // through the MFMA steps, so the wave's loads do not all leave in one
+      // burst after the barrier (measured 1-3% faster on the full tiles)
+      auto compute = [&](auto stc, auto mid) __attribute__((always_inline)) {
+        constexpr int u = decltype(stc)::value;
+        if (!busy) mid();
+        if (busy) {
+          const uint8_t* sb = stage(stc);
+          uint32_t ascb[RT];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) ascb[rt] = (sw[u] >> (((t0 + rt) & 3) * 8)) & 0xFFu;
+          if constexpr (ACT == ACT_BF16) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              if (st == 2) mid();
+              bf16x8_t b[NA];
+#pragma unroll
+              for (int nt = 0; nt < NA; ++nt)
+                b[nt] = *reinterpret_cast<const bf16x8_t*>(
+                    sb + ((nt * 16 + r16) * 16 + bf16_piece_pos(r16, 4 * g + st)) * 16);
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt) {
+                const bf16x8_t av = fp4x8_to_bf16x8(dword(aq[u][rt], st), e8m0_as_scale_operand(ascb[rt]));
+#pragma unroll
+                for (int nt = 0; nt < NA; ++nt)
+                  acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nt], acc[rt][nt], 0, 0, 0);
               }
             }
-            bcur = bnext;
-          }
-        }
-      }
-    };
-
-    // prologue: chunks 0 .. SX-2 in flight, issued in chunk order
-    auto issue = [&](int c, auto stc) __attribute__((always_inline)) {
-      issue_w(c, stc);
-      issue_b(c, stc);
-    };
-    order_point();
-    issue(0, IC<0>{});
-    order_point();
-    if constexpr (SX > 2) { issue(1, IC<1>{}); order_point(); }
-    if constexpr (SX > 3) { issue(2, IC<2>{}); order_point(); }
-
-    // iteration c: wait for chunk c, barrier (its tokens have landed for
-    // every wave, and chunk c-1's stage is free), refill that stage with
-    // chunk c+S-1 (weights now, tokens from inside compute), compute chunk
-    // c.  Every iteration issues the same loads (chunks past the end read
-    // zeros), weights before tokens, so the wait count is fixed.
-    auto iteration = [&](int c, auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value;  // c % SX
-      wait_vmcnt<(SX - 2) * LD>();
-      barrier();
-      issue_w(c + SX - 1, IC<(u + SX - 1) % SX>{});
-      order_point();
-      compute(IC<u>{}, [&]() __attribute__((always_inline)) {
-        order_point();
-        issue_b(c + SX - 1, IC<(u + SX - 1) % SX>{});
-        order_point();
-      });
-    };
-    int c0 = 0;
-    for (; c0 + SX <= nc; c0 += SX) {
-      iteration(c0 + 0, IC<0>{});
-      iteration(c0 + 1, IC<1>{});
-      if constexpr (SX > 2) iteration(c0 + 2, IC<2 % SX>{});
-      if constexpr (SX > 3) iteration(c0 + 3, IC<3 % SX>{});
-    }
-    if (c0 + 0 < nc) iteration(c0 + 0, IC<0>{});
-    if (c0 + 1 < nc) iteration(c0 + 1, IC<1 % SX>{});
-    if constexpr (SX > 3) if (c0 + 2 < nc) iteration(c0 + 2, IC<2 % SX>{});
-    wait_vmcnt<0>();
-    // Never true (slot counts are non-negative).  It keeps every weight
-    // prefetch live: the vmcnt waits count loads, so none may be dropped as
-    // dead even when its chunk lies past the end.
-    if (a.n_slots < 0) {
-      uint32_t x = 0;
+          } else {
+            // token fragments double-buffered by hand (sub-tile nt+1 is read
+            // before sub-tile nt's MFMAs; the order points keep the compiler
+            // from hoisting all of them, which would cost 8 registers each)
+            const int sw8 = (r16 >> 1) & 7;
+            auto load_b = [&](int nt) __attribute__((always_inline)) {
+              const uint8_t* rowp = sb + (nt * 16 + r16) * 128;
+              const uint4 p0 = *reinterpret_cast<const uint4*>(rowp + (g ^ sw8) * 16);
+              const uint4 p1 = *reinterpret_cast<const uint4*>(rowp + ((4 + g) ^ sw8) * 16);
+              return i32x8_t{int(p0.x), int(p0.y), int(p0.z), int(p0.w), int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
+            };
+            i32x8_t av[RT];
 #pragma unroll
-      for (int d = 0; d < SX; ++d) x ^= aq[d][0].x ^ aq[d][1].y ^ aq[d][2].z ^ aq[d][3].w ^ sw[d];
-      if constexpr (W8) {
-#pragma unroll
-        for (int d = 0; d < SX; ++d) x ^= aq2[d][0].x ^ aq2[d][1].y ^ aq2[d][2].z ^ aq2[d][3].w;
-      }
-      static_cast<uint32_t*>(a.out)[0] = x;
-    }
-
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (rt < rt_active) {
-        // bias of this lane's 4 output rows (raw bf16 bits)
-        const uint2 q = *reinterpret_cast<const uint2*>(sBias + 2 * (wave * 16 * RT + 16 * rt + 4 * g));
-        float4 rs = make_float4(1.f, 1.f, 1.f, 1.f);  // int8: weight scales of the 4 rows
-        if constexpr (I8)
-          rs = *reinterpret_cast<const float4*>(a.row_scale + int64_t(e) * a.R + grow + 16 * rt + 4 * g);
-#pragma unroll
-        for (int nt = 0; nt < NA; ++nt) {
-          const int j = nt * 16 + r16;
-          if (j < ntok) {
-            f32x4_t v = acc[rt][nt];
-            if constexpr (I8) {
-              // exact int32 sums -> fp32, times the row's and the token's
-              // scales (the whole vector is reinterpreted: a bit cast of one
-              // element of a vector value reads element 0 with this compiler)
-              typedef int i32x4_t __attribute__((ext_vector_type(4)));
-              const i32x4_t iv = __builtin_bit_cast(i32x4_t, acc[rt][nt]);
-              const int p = row_start + j;
-              const float ts = a.tok_scale[PHASE == 0 ? a.sorted_tok[p] : p];
-              v = f32x4_t{float(iv[0]) * rs.x * ts, float(iv[1]) * rs.y * ts, float(iv[2]) * rs.z * ts,
-                          float(iv[3]) * rs.w * ts};
+            for (int rt = 0; rt < RT; ++rt) {
+              const uint4 q = aq[u][rt];
+              if constexpr (W8) {
+                const uint4 q2 = aq2[u][rt];
+                av[rt] = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), int(q2.x), int(q2.y), int(q2.z), int(q2.w)};
+              } else {
+                av[rt] = i32x8_t{int(q.x), int(q.y), int(q.z), int(q.w), 0, 0, 0, 0};
+              }
             }
-            store_rows_biased<ACT, PHASE>(a, grow + 16 * rt + 4 * g, row_start + j,
-                                          v[0] * a.acc_scale + __uint_as_float(q.x << 16),
-                                          v[1] * a.acc_scale + __uint_as_float(q.x & 0xFFFF0000u),
-                                          v[2] * a.acc_scale + __uint_as_float(q.y << 16),
-                                          v[3] * a.acc_scale + __uint_as_float(q.y & 0xFFFF0000u));
+            i32x8_t bcur = load_b(0);
+#pragma unroll
+            for (int nt = 0; nt < NA; ++nt) {
+              if (nt == NA / 2) mid();
+              i32x8_t bnext = bcur;
+              if (nt + 1 < NA) bnext = load_b(nt + 1);
+              order_point();
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt) {
+                if constexpr (I8) {
+                  // two K=64 halves (dwords 0-3, then 4-7 of both operands);
+                  // the int32 sums live in the float accumulator registers
+                  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+                  i32x4_t c = __builtin_bit_cast(i32x4_t, acc[rt][nt]);
+                  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_shufflevector(av[rt], av[rt], 0, 1, 2, 3),
+                                                           __builtin_shufflevector(bcur, bcur, 0, 1, 2, 3), c, 0, 0, 0);
+                  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_shufflevector(av[rt], av[rt], 4, 5, 6, 7),
+                                                           __builtin_shufflevector(bcur, bcur, 4, 5, 6, 7), c, 0, 0, 0);
+                  acc[rt][nt] = __builtin_bit_cast(f32x4_t, c);
+                } else {
+                  acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                      av[rt], bcur, acc[rt][nt], W8 ? 0 : 4, 0, 0, W8 ? 127 : int(ascb[rt]), 0, 127);
+                }
+              }
+              bcur = bnext;
+            }
+          }
+        }
+      };
+
+      // prologue: chunks 0 .. SX-2 in flight, issued in chunk order
+      auto issue = [&](int c, auto stc) __attribute__((always_inline)) {
+        issue_w(c, stc);
+        issue_b(c, stc);
+      };
+      order_point();
+      issue(0, IC<0>{});
+      order_point();
+      if constexpr (SX > 2) { issue(1, IC<1>{}); order_point(); }
+      if constexpr (SX > 3) { issue(2, IC<2>{}); order_point(); }
+
+      // iteration c: wait for chunk c, barrier (its tokens have landed for
+      // every wave, and chunk c-1's stage is free), refill that stage with
+      // chunk c+S-1 (weights now, tokens from inside compute), compute chunk
+      // c.  Every iteration issues the same loads (chunks past the end read
+      // zeros), weights before tokens, so the wait count is fixed.
+      auto iteration = [&](int c, auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;  // c % SX
+        wait_vmcnt<(SX - 2) * LD>();
+        barrier();
+        issue_w(c + SX - 1, IC<(u + SX - 1) % SX>{});
+        order_point();
+        compute(IC<u>{}, [&]() __attribute__((always_inline)) {
+          order_point();
+          issue_b(c + SX - 1, IC<(u + SX - 1) % SX>{});
+          order_point();
+        });
+      };
+      int c0 = 0;
+      for (; c0 + SX <= nc; c0 += SX) {
+        iteration(c0 + 0, IC<0>{});
+        iteration(c0 + 1, IC<1>{});
+        if constexpr (SX > 2) iteration(c0 + 2, IC<2 % SX>{});
+        if constexpr (SX > 3) iteration(c0 + 3, IC<3 % SX>{});
+      }
+      if (c0 + 0 < nc) iteration(c0 + 0, IC<0>{});
+      if (c0 + 1 < nc) iteration(c0 + 1, IC<1 % SX>{});
+      if constexpr (SX > 3) if (c0 + 2 < nc) iteration(c0 + 2, IC<2 % SX>{});
+      wait_vmcnt<0>();
+      // Never true (slot counts are non-negative).  It keeps every weight
+      // prefetch live: the vmcnt waits count loads, so none may be dropped as
+      // dead even when its chunk lies past the end.
+      if (a.n_slots < 0) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int d = 0; d < SX; ++d) x ^= aq[d][0].x ^ aq[d][1].y ^ aq[d][2].z ^ aq[d][3].w ^ sw[d];
+        if constexpr (W8) {
+#pragma unroll
+          for (int d = 0; d < SX; ++d) x ^= aq2[d][0].x ^ aq2[d][1].y ^ aq2[d][2].z ^ aq2[d][3].w;
+        }
+        static_cast<uint32_t*>(a.out)[0] = x;
+      }
+
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if (rt < rt_active) {
+          // bias of this lane's 4 output rows (raw bf16 bits)
+          const uint2 q = *reinterpret_cast<const uint2*>(sBias + 2 * (wave * 16 * RT + 16 * rt + 4 * g));
+          float4 rs = make_float4(1.f, 1.f, 1.f, 1.f);  // int8: weight scales of the 4 rows
+          if constexpr (I8)
+            rs = *reinterpret_cast<const float4*>(a.row_scale + int64_t(e) * a.R + grow + 16 * rt + 4 * g);
+#pragma unroll
+          for (int nt = 0; nt < NA; ++nt) {
+            const int j = nt * 16 + r16;
+            if (j < ntok) {
+              f32x4_t v = acc[rt][nt];
+              if constexpr (I8) {
+                // exact int32 sums -> fp32, times the row's and the token's
+                // scales (the whole vector is reinterpreted: a bit cast of one
+                // element of a vector value reads element 0 with this compiler)
+                typedef int i32x4_t __attribute__((ext_vector_type(4)));
+                const i32x4_t iv = __builtin_bit_cast(i32x4_t, acc[rt][nt]);
+                const int p = row_start + j;
+                const float ts = a.tok_scale[PHASE == 0 ? a.sorted_tok[p] : p];
+                v = f32x4_t{float(iv[0]) * rs.x * ts, float(iv[1]) * rs.y * ts, float(iv[2]) * rs.z * ts,
+                            float(iv[3]) * rs.w * ts};
+              }
+              store_rows_biased<ACT, PHASE>(a, grow + 16 * rt + 4 * g, row_start + j,
+                                            v[0] * a.acc_scale + __uint_as_float(q.x << 16),
+                                            v[1] * a.acc_scale + __uint_as_float(q.x & 0xFFFF0000u),
+                                            v[2] * a.acc_scale + __uint_as_float(q.y << 16),
+                                            v[3] * a.acc_scale + __uint_as_float(q.y & 0xFFFF0000u));
+            }
           }
         }
       }
+    };
+    constexpr int SM = ACT == ACT_BF16 ? 1 : 0;  // tiles of <= 64 tokens take the small ring
+    switch (na) {
+      case 1: main_loop(IC<1>{}, IC<SM>{}); break;
+      case 2: main_loop(IC<2>{}, IC<SM>{}); break;
+      case 3: main_loop(IC<3>{}, IC<SM>{}); break;
+      case 4: main_loop(IC<4>{}, IC<SM>{}); break;
+      case 5: main_loop(IC<5>{}, IC<0>{}); break;
+      case 6: main_loop(IC<6>{}, IC<0>{}); break;
+      case 7: main_loop(IC<7>{}, IC<0>{}); break;
+      default: main_loop(IC<8>{}, IC<0>{}); break;
     }
-  };
-  constexpr int SM = ACT == ACT_BF16 ? 1 : 0;  // tiles of <= 64 tokens take the small ring
-  switch (na) {
-    case 1: main_loop(IC<1>{}, IC<SM>{}); break;
-    case 2: main_loop(IC<2>{}, IC<SM>{}); break;
-    case 3: main_loop(IC<3>{}, IC<SM>{}); break;
-    case 4: main_loop(IC<4>{}, IC<SM>{}); break;
-    case 5: main_loop(IC<5>{}, IC<0>{}); break;
-    case 6: main_loop(IC<6>{}, IC<0>{}); break;
-    case 7: main_loop(IC<7>{}, IC<0>{}); break;
-    default: main_loop(IC<8>{}, IC<0>{}); break;
-  }
+    if constexpr (!PERSIST) return;  // one item per workgroup
+  }  // items
 }
 
 // The folded combine of row group q (64 rows of H) once every active
@@ -1048,13 +1126,23 @@ template <int ACT, int PHASE, bool TILED>
 static void launch_layout(const GemmArgs& a, bool prefill, hipStream_t stream) {
   if constexpr (ACT == ACT_W8A8) {  // FP8 weights: the tiled LDS-staged kernel only
     const int64_t items = tiled_prefill_blocks(a.R, a.max_tiles);
-    gemm_prefill_tiled_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kTiledThreads), 0, stream>>>(a);
+    gemm_prefill_tiled_kernel<ACT, PHASE, false><<<dim3(unsigned(items)), dim3(kTiledThreads), 0, stream>>>(a);
   } else if (prefill) {
     if constexpr (ACT != ACT_F32) {
       if constexpr (TILED) {
-        // the grid the grouping's item records (GemmArgs::blk_rec) assume
+        // the grid the grouping's item records (GemmArgs::blk_rec) assume,
+        // or the persistent grid that takes them as work lists: when the
+        // records allow at least kPersistMin items per workgroup (with
+        // fewer, the launch's tail outweighs the dispatch gaps saved)
         const int64_t items = tiled_prefill_blocks(a.R, a.max_tiles);
-        gemm_prefill_tiled_kernel<ACT, PHASE><<<dim3(unsigned(items)), dim3(kTiledThreads), 0, stream>>>(a);
+        if (a.item_head && items >= int64_t(kPersistMin) * kPersistentBlocks) {
+          gemm_prefill_tiled_kernel<ACT, PHASE, true>
+              <<<dim3(unsigned(kPersistentBlocks)), dim3(kTiledThreads), 0, stream>>>(a);
+        } else {
+          GemmArgs b = a;
+          b.item_head = nullptr;
+          gemm_prefill_tiled_kernel<ACT, PHASE, false><<<dim3(unsigned(items)), dim3(kTiledThreads), 0, stream>>>(b);
+        }
       } else {
         const int64_t items = (int64_t(a.max_tiles) * ((a.R + kPrefillRows - 1) / kPrefillRows) + 7) / 8 * 8;
         gemm_prefill_kernel<ACT, PHASE, TILED><<<dim3(unsigned(items)), dim3(kPrefillThreads), 0, stream>>>(a);

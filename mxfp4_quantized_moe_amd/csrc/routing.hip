@@ -485,6 +485,9 @@ __device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_l
       rec[8 * (item - s_bx[x]) + x] =
           make_int4(lo, s_cp[lo] + q * kPrefillTokens, min(kPrefillTokens, cnt[lo] - q * kPrefillTokens), st);
     }
+    // list counters of a persistent launch: past the first item of each of
+    // its workgroups
+    if (write_empty && a.rec_head[gi] && tid < 8) a.rec_head[gi][tid] = uint32_t(min(nblk, kPersistentBlocks) >> 3);
     if (write_empty)
       for (int b = tid; b < nblk; b += kPermThreads) {
         const int x = b & 7;
