@@ -71,5 +71,12 @@ def test_graph_prefill_rows_layout(dev):
     _replays(W.bf16_20b(T=300), dev, 300, layout="rows")
 
 
+def test_graph_persistent_prefill(dev):
+    """A persistent gate_up launch (E=64, 2I = 5760 rows, T=4096): its list
+    counters are set by the grouping kernel inside the graph, so every
+    replay takes the same items."""
+    _replays(W.small_case(44, 64, 256, 2880, 4, 4096), dev, 4096)
+
+
 def test_graph_dense(dev):
     _replays(W.decode_20b(T=64), dev, 8, dense=True)

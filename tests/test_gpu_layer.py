@@ -375,6 +375,32 @@ def test_skewed_routing_clamped_xcd_ranges(dev):
     check_layer(case, res)
 
 
+# The library runs a tiled prefill GEMM as a persistent launch (512
+# workgroups taking their XCD's item records through a counter) when the
+# record grid holds at least 4 records per workgroup: max token tiles x row
+# stripes of 256, rounded up to 8.
+def record_blocks(case, R):
+    rows = case.T * case.layer.top_k
+    tiles = -(-rows // 128) + min(rows, case.layer.E)
+    return -(-(tiles * -(-R // 256)) // 8) * 8
+
+
+@pytest.mark.parametrize("seed,H,I,bias", [(41, 256, 2880, 0.01), (42, 2880, 256, 0.01), (43, 256, 2880, 1.5)])
+def test_persistent_prefill_launches(dev, seed, H, I, bias):
+    """T=4096, E=64, top-4 with one of the two GEMMs persistent: gate_up (2I
+    = 5760 rows, 23 stripes) or down (H = 2880 rows, 12 stripes); the other
+    runs one workgroup per record.  Every token against the oracle, on a
+    poisoned workspace (an item no workgroup took leaves NaN rows).  Seed
+    43 skews the routing so the XCDs' record lists differ in length."""
+    case = W.small_case(seed, 64, H, I, 4, 4096, router_bias_std=bias)
+    persistent = [record_blocks(case, R) >= 4 * 512 for R in (2 * I, H)]
+    assert persistent == [I > H, H > I], persistent
+    note(f"{case.name} tiled, persistent (gate_up, down) = {persistent}")
+    res, _, _ = run_gpu(case, dev, layout="tiled")
+    check_perm(case, res["route"])
+    check_layer(case, res, full_ref=oracle_full(case))
+
+
 def test_fp8_saturating_activations(dev):
     """FP8 mode with x about 50x beyond the calibrated range: most codes of x
     saturate at +-448 on both sides (decided in fp32 from the same scale)."""
