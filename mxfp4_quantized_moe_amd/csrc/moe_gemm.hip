@@ -566,12 +566,6 @@ constexpr int kTiledThreads = 64 * kTiledWaves;
 #define MXMOE_PREFILL_TILED_STAGES_FP8 2
 #endif
 
-// Lists a persistent prefill workgroup takes items from: its own XCD's, then
-// (when 8) the other XCDs' in turn.
-#ifndef MXMOE_PERSIST_LISTS
-#define MXMOE_PERSIST_LISTS 1
-#endif
-constexpr int kPersistLists = MXMOE_PERSIST_LISTS;
 // Item records per workgroup from which a tiled prefill launch goes
 // persistent.
 #ifndef MXMOE_PERSIST_MIN
@@ -642,14 +636,12 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
   // grouping's item records) holds two workgroups per CU; each takes items
   // one after another from its XCD's record list through a device-scope
   // counter, so no slot waits for the dispatcher between items.  (Taking
-  // items from the other XCDs' lists once its own is exhausted,
-  // kPersistLists 8, measured slower: their experts' weights miss in this
-  // XCD's L2.)  Otherwise each workgroup runs one item: its record, or one
-  // it resolves itself (one record load instead of the scan and searches
-  // below).
+  // items from the other XCDs' lists once its own is exhausted measured
+  // slower: their experts' weights miss in this XCD's L2.)  Otherwise each
+  // workgroup runs one item: its record, or one it resolves itself (one
+  // record load instead of the scan and searches below).
   const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3, G = gridDim.x >> 3;
   __shared__ int4 s_rec;
-  int kq = 0;  // thread 0 of a persistent workgroup: lists (xcd + 0 .. kq-1) & 7 are exhausted
   for (bool first_item = true;; first_item = false) {
     // The arguments and the lane's constants are produced anew for each
     // item (the arguments re-read from the kernel's argument segment through
@@ -666,30 +658,18 @@ __global__ __launch_bounds__(kTiledThreads, 512 / kTiledThreads) void gemm_prefi
     int e, row_start, ntok, stripe;
     if constexpr (PERSIST) {
       if (threadIdx.x == 0) {
-        const int gr = int(tiled_prefill_blocks(a.R, a.max_tiles) >> 3);  // records per XCD
-        int4 r = make_int4(0, 0, 0, 0);
-        // The first item is fixed, list position idx of the workgroup's XCD
-        // (the counters start past the G of them); later ones come from the
-        // counters.
-        if (first_item && idx < gr) r = a.blk_rec[8 * idx + xcd];
-        if (r.z == 0) {
-          for (; kq < kPersistLists; ++kq) {
-            const int y = (xcd + kq) & 7;
-            const uint32_t q = add_dev(a.item_head + y, 1u);
-            if (q < uint32_t(gr)) {
-              r = a.blk_rec[8 * q + y];
-              if (r.z != 0) break;  // list y still has items: start there next time
-            }
-          }
-        }
-        s_rec = r;
+        // this item's position in the XCD's list: idx for the first one (the
+        // counter starts past the G of them), then the counter's next
+        const uint32_t gr = uint32_t(tiled_prefill_blocks(a.R, a.max_tiles) >> 3);  // records per XCD
+        const uint32_t q = first_item ? uint32_t(idx) : add_dev(a.item_head + xcd, 1u);
+        s_rec = q < gr ? a.blk_rec[8 * q + xcd] : make_int4(0, 0, 0, 0);
       }
       // also the barrier between this workgroup's items: the new item's DMAs
       // reuse LDS the previous one read
       __syncthreads();
       const int4 r = s_rec;
       ntok = __builtin_amdgcn_readfirstlane(r.z);
-      if (ntok == 0) return;  // every list exhausted: uniform per workgroup
+      if (ntok == 0) return;  // the list is exhausted: uniform per workgroup
       e = __builtin_amdgcn_readfirstlane(r.x);
       row_start = __builtin_amdgcn_readfirstlane(r.y);
       stripe = __builtin_amdgcn_readfirstlane(r.w);
