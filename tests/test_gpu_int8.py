@@ -100,6 +100,7 @@ def test_int8_tile_bit_exact(dev, mats, rows, k):
     (62, 6, 160, 352, 2, 777),    # several token tiles per expert, K/32 = 5 and 11
     (63, 16, 256, 128, 8, 40),    # top_k = 8
     (64, 3, 128, 96, 3, 5),       # top_k = E
+    (66, 4, 128, 160, 2, 400),    # last stripes of 64 (gate_up) and 128 rows (down), full token tiles
 ])
 def test_int8_small_shapes(dev, seed, E, H, I, k, T):
     case = W.int8_case(seed, E, H, I, k, T)

@@ -200,7 +200,8 @@ def test_fp8_calibration_scales(dev):
     (16, 6, 160, 352, 2, 777, "bf16"),   # prefill: ragged token tiles, K/32 = 5 and 11
     (17, 2, 32, 32, 1, 200, "bf16"),     # smallest dims through prefill
     (18, 4, 64, 64, 2, 130, "f32"),      # fp32 with more than 64 tokens per expert
-    (19, 4, 96, 544, 2, 600, "bf16"),    # prefill: gate_up R = 1088 (2 stripes + a ragged third)
+    (19, 4, 96, 544, 2, 600, "bf16"),    # prefill: gate_up R = 1088 (4 stripes + a ragged fifth of 64 rows)
+    (29, 4, 128, 160, 2, 400, "bf16"),   # prefill: last stripes of 64 (gate_up) and 128 rows (down), full tiles
     (22, 100, 64, 64, 4, 20, "bf16"),    # router: 65 <= E <= 128 with few tokens (8 K-splitting waves)
     (23, 256, 64, 32, 8, 40, "bf16"),    # router: E = 256 (largest), top_k = 8
     (24, 200, 96, 64, 3, 70, "f32"),     # router: fp32 with E > 128
@@ -224,6 +225,7 @@ def test_small_shapes(dev, seed, E, H, I, k, T, act, layout):
 @pytest.mark.parametrize("seed,E,H,I,k,T", [
     (20, 4, 64, 64, 2, 16),     # decode-shaped
     (21, 4, 96, 160, 2, 400),   # prefill-shaped with partial chunks
+    (28, 4, 128, 160, 2, 400),  # last stripes of 64 and 128 rows with full token tiles
 ])
 @pytest.mark.parametrize("layout", ["rows", "tiled"])
 def test_small_fp8(dev, seed, E, H, I, k, T, layout):
