@@ -411,17 +411,25 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(PermuteArgs a) { 
 // The work item of every workgroup of the tiled prefill launches that
 // follow (PermuteArgs::blk_rec), resolved once here instead of by each
 // workgroup: the per-expert prefixes of token tiles, sorted rows and
-// per-stripe costs (wave 0, 4 experts per lane), the XCD ranges
-// (xcd_split.h), then one record per item of experts [e_lo, e_hi) at the
-// workgroup that takes it, and (write_empty) an empty record for every
-// workgroup past its XCD's range.  cnt: the experts' counts in LDS.  Every
-// thread of the workgroup calls it.
+// per-stripe costs (4 experts per lane) and the XCD ranges (xcd_split.h),
+// by wave g for launch g, both at once; then one record per item of
+// experts [e_lo, e_hi) at the workgroup that takes it, and (write_empty)
+// an empty record for every workgroup past its XCD's range.  cnt: the
+// experts' counts in LDS.  Every thread of the workgroup calls it.
 __device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_lo, int e_hi, bool write_empty) {
   if (!a.blk_rec[0] && !a.blk_rec[1]) return;  // uniform
-  __shared__ int s_tp[257], s_wp[257], s_cp[257], s_bx[9];
+  __shared__ int s_tp[2][257], s_wp[2][257], s_cp[257], s_bx[2][9];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
-  if (wave == 0) {
+  static_assert(kPermWaves >= 2, "one wave per launch");
+  const bool mine = wave < 2 && a.blk_rec[wave];  // uniform per wave
+  int* tp = s_tp[wave & 1];
+  int* wp = s_wp[wave & 1];
+  int ttot = 0;
+  if (mine) {
+    // the sorted-row prefix is the same for both launches: the wave of
+    // launch 0 writes it, or that of launch 1 when launch 0 has no records
+    const bool own_cp = wave == 0 || !a.blk_rec[0];
     int tc[4], wc[4], cc[4], ts = 0, ws = 0, cs = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -434,24 +442,37 @@ __device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_l
       ws += wc[j];
       cs += cc[j];
     }
-    int ttot, wtot, ctot;
+    int wtot, ctot;
     int tb = wave_excl_scan(ts, lane, &ttot), wb = wave_excl_scan(ws, lane, &wtot), cb = wave_excl_scan(cs, lane, &ctot);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane * 4 + j;
       if (e < E) {
-        s_tp[e] = tb;
-        s_wp[e] = wb;
-        s_cp[e] = cb;
+        tp[e] = tb;
+        wp[e] = wb;
+        if (own_cp) s_cp[e] = cb;
       }
       tb += tc[j];
       wb += wc[j];
       cb += cc[j];
     }
     if (lane == 0) {
-      s_tp[E] = ttot;
-      s_wp[E] = wtot;
-      s_cp[E] = ctot;
+      tp[E] = ttot;
+      wp[E] = wtot;
+      if (own_cp) s_cp[E] = ctot;
+    }
+  }
+  // the prefixes are read by every lane of the wave below (a barrier, not
+  // program order: the compiler may move a lane's read of another lane's
+  // entry ahead of that lane's write)
+  __syncthreads();
+  if (mine) {
+    const int ns = a.rec_stripes[wave], nblk = a.rec_blocks[wave];
+    int bx[9];
+    xcd_bounds(wp, tp, E, ns, nblk >> 3, ttot * ns, lane, bx);
+    if (lane == 0) {
+#pragma unroll
+      for (int xx = 0; xx < 9; ++xx) s_bx[wave][xx] = bx[xx];
     }
   }
   __syncthreads();
@@ -459,30 +480,22 @@ __device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_l
     int4* rec = a.blk_rec[gi];
     if (!rec) continue;  // uniform
     const int ns = a.rec_stripes[gi], nblk = a.rec_blocks[gi];
-    const int nvalid = s_tp[E] * ns;
-    if (wave == 0) {
-      int bx[9];
-      xcd_bounds(s_wp, s_tp, E, ns, nblk >> 3, nvalid, lane, bx);
-      if (lane == 0) {
-#pragma unroll
-        for (int xx = 0; xx < 9; ++xx) s_bx[xx] = bx[xx];
-      }
-    }
-    __syncthreads();
-    const int i1 = s_tp[e_hi] * ns;
-    for (int item = s_tp[e_lo] * ns + tid; item < i1; item += kPermThreads) {
-      int lo = e_lo, hi = e_hi;  // s_tp[lo] * ns <= item < s_tp[hi] * ns
+    const int* tp = s_tp[gi];
+    const int* bxp = s_bx[gi];
+    const int i1 = tp[e_hi] * ns;
+    for (int item = tp[e_lo] * ns + tid; item < i1; item += kPermThreads) {
+      int lo = e_lo, hi = e_hi;  // tp[lo] * ns <= item < tp[hi] * ns
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (s_tp[mid] * ns <= item) lo = mid;
+        if (tp[mid] * ns <= item) lo = mid;
         else hi = mid;
       }
-      const int nt = s_tp[lo + 1] - s_tp[lo];
-      const int local = item - s_tp[lo] * ns;
+      const int nt = tp[lo + 1] - tp[lo];
+      const int local = item - tp[lo] * ns;
       const int st = local / nt, q = local - st * nt;
       int x = 0;
-      while (x < 7 && item >= s_bx[x + 1]) ++x;
-      rec[8 * (item - s_bx[x]) + x] =
+      while (x < 7 && item >= bxp[x + 1]) ++x;
+      rec[8 * (item - bxp[x]) + x] =
           make_int4(lo, s_cp[lo] + q * kPrefillTokens, min(kPrefillTokens, cnt[lo] - q * kPrefillTokens), st);
     }
     // list counters of a persistent launch: past the first item of each of
@@ -491,9 +504,8 @@ __device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_l
     if (write_empty)
       for (int b = tid; b < nblk; b += kPermThreads) {
         const int x = b & 7;
-        if ((b >> 3) >= s_bx[x + 1] - s_bx[x]) rec[b] = make_int4(0, 0, 0, 0);
+        if ((b >> 3) >= bxp[x + 1] - bxp[x]) rec[b] = make_int4(0, 0, 0, 0);
       }
-    __syncthreads();
   }
 }
 
