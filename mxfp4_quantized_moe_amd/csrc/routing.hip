@@ -618,39 +618,61 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
   __shared__ int cnt[256];
   __shared__ int s_off, s_toff, s_act, s_atot;
   __shared__ int wsum[kPermWaves];
-  __shared__ uint8_t sidx[kPermLdsSlots];
+  __shared__ __align__(16) uint8_t sidx[kPermLdsSlots];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, N = a.n_slots, me = blockIdx.x;
   const bool cached = N <= kPermLdsSlots;
 
   for (int e = tid; e < 256; e += kPermThreads) cnt[e] = 0;
   __syncthreads();
-  // histogram: a thread's loads for kB slots leave together, so the pass
-  // waits on one L2 round trip per kB slots rather than per slot
-  constexpr int kB = 8;
-  for (int base = tid; base < N; base += kB * kPermThreads) {
-    int ev[kB];
+  // histogram: a thread's loads for several slots leave together, so the
+  // pass waits on one L2 round trip per batch rather than per slot
+  if (cached) {
+    // 4 ids per 16-byte load (range-checked: past N reads zeros, which are
+    // not counted), kept in LDS as one dword of 4 bytes
+    const rsrc_t ir = make_rsrc(a.idx, uint32_t(N) * 4u);
+    constexpr int kQ = 4;
+    for (int q0 = tid; 4 * q0 < N; q0 += kQ * kPermThreads) {
+      uint4 v[kQ];
 #pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const int s = base + j * kPermThreads;
-      ev[j] = s < N ? a.idx[s] : 0;
+      for (int j = 0; j < kQ; ++j) {
+        const int q = q0 + j * kPermThreads;
+        v[j] = buf_load_b128(ir, 4 * q < N ? uint32_t(q) * 16u : kOOB);
+      }
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) {
+        const int s = 4 * (q0 + j * kPermThreads);
+        if (s < N) {
+          const int ev[4] = {int(v[j].x), int(v[j].y), int(v[j].z), int(v[j].w)};
+          uint32_t packed = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = ev[i] < 0 ? 0 : (ev[i] >= E ? E - 1 : ev[i]);
+            if (s + i < N) atomicAdd(&cnt[e], 1);
+            packed |= uint32_t(e) << (8 * i);
+          }
+          // s is a multiple of 4 below N <= kPermLdsSlots: inside sidx
+          *reinterpret_cast<uint32_t*>(sidx + s) = packed;
+        }
+      }
     }
+  } else {
+    constexpr int kB = 8;
+    for (int base = tid; base < N; base += kB * kPermThreads) {
+      int ev[kB];
 #pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const int s = base + j * kPermThreads;
-      if (s < N) {
-        const int e = ev[j] < 0 ? 0 : (ev[j] >= E ? E - 1 : ev[j]);
-        if (cached) sidx[s] = uint8_t(e);
-        atomicAdd(&cnt[e], 1);
+      for (int j = 0; j < kB; ++j) {
+        const int s = base + j * kPermThreads;
+        ev[j] = s < N ? a.idx[s] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int s = base + j * kPermThreads;
+        if (s < N) atomicAdd(&cnt[ev[j] < 0 ? 0 : (ev[j] >= E ? E - 1 : ev[j])], 1);
       }
     }
   }
   __syncthreads();
-  auto key_at = [&](int s) -> int {
-    if (cached) return sidx[s];
-    const int e = a.idx[s];
-    return e < 0 ? 0 : (e >= E ? E - 1 : e);
-  };
 
   if (wave == 0) {
     // each lane scans 4 consecutive experts
@@ -704,31 +726,88 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
 
   write_item_records(a, cnt, me, me + 1, me == 0);
 
-  // stable positions of this expert's slots
-  const int per_wave = ((N + kPermWaves - 1) / kPermWaves + 63) & ~63;
-  const int s0 = wave * per_wave, s1 = min(N, s0 + per_wave);
-  int mine = 0;
-  for (int b = s0; b < s1; b += 64) {
-    const int s = b + lane;
-    const int key = s < s1 ? key_at(s) : -1;
-    mine += __popcll(__ballot(key == me));
-  }
-  if (lane == 0) wsum[wave] = mine;
-  __syncthreads();
-  int run = off_me;
-  for (int w = 0; w < wave; ++w) run += wsum[w];
+  // stable positions of this expert's slots: wave w takes a contiguous
+  // range [s0, s1), counts its matches, takes the prefix over the waves and
+  // sweeps the range again writing positions in slot order
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b = s0; b < s1; b += 64) {
-    const int s = b + lane;
-    const int key = s < s1 ? key_at(s) : -1;
-    const uint64_t m = __ballot(key == me);
-    if (key == me) {
-      const int p = run + __popcll(m & lt_mask);
-      a.sorted[p] = s;
-      a.sorted_tok[p] = s / a.top_k;
-      a.pos[s] = p;
+  const int end = off_me + c_me;  // positions stay inside the expert's range
+  if (cached) {
+    // 4 consecutive slots per lane and step: slot s + i of lane l comes
+    // after every slot of the lanes below l and the i' < i of its own
+    const int per_wave = ((N + kPermWaves - 1) / kPermWaves + 255) & ~255;
+    const int s0 = wave * per_wave, s1 = min(N, s0 + per_wave);
+    auto hits = [&](int s, bool (&h)[4]) __attribute__((always_inline)) {
+      const uint32_t w4 = s < s1 ? *reinterpret_cast<const uint32_t*>(sidx + s) : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = s + i < s1 && ((w4 >> (8 * i)) & 0xFFu) == uint32_t(me);
+    };
+    int mine = 0;
+    for (int b = s0; b < s1; b += 256) {
+      bool h[4];
+      hits(b + 4 * lane, h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mine += __popcll(__ballot(h[i]));
     }
-    run += __popcll(m);
+    if (lane == 0) wsum[wave] = mine;
+    __syncthreads();
+    int run = off_me;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+    for (int b = s0; b < s1; b += 256) {
+      const int s = b + 4 * lane;
+      bool h[4];
+      hits(s, h);
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t m = __ballot(h[i]);
+        before += __popcll(m & lt_mask);
+        tot += __popcll(m);
+      }
+      int p = run + before;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (h[i]) {
+          if (p < end) {
+            a.sorted[p] = s + i;
+            a.sorted_tok[p] = (s + i) / a.top_k;
+            a.pos[s + i] = p;
+          }
+          ++p;
+        }
+      }
+      run += tot;
+    }
+  } else {
+    auto key_at = [&](int s) -> int {
+      const int e = a.idx[s];
+      return e < 0 ? 0 : (e >= E ? E - 1 : e);
+    };
+    const int per_wave = ((N + kPermWaves - 1) / kPermWaves + 63) & ~63;
+    const int s0 = wave * per_wave, s1 = min(N, s0 + per_wave);
+    int mine = 0;
+    for (int b = s0; b < s1; b += 64) {
+      const int s = b + lane;
+      const int key = s < s1 ? key_at(s) : -1;
+      mine += __popcll(__ballot(key == me));
+    }
+    if (lane == 0) wsum[wave] = mine;
+    __syncthreads();
+    int run = off_me;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+    for (int b = s0; b < s1; b += 64) {
+      const int s = b + lane;
+      const int key = s < s1 ? key_at(s) : -1;
+      const uint64_t m = __ballot(key == me);
+      if (key == me) {
+        const int p = run + __popcll(m & lt_mask);
+        if (p < end) {
+          a.sorted[p] = s;
+          a.sorted_tok[p] = s / a.top_k;
+          a.pos[s] = p;
+        }
+      }
+      run += __popcll(m);
+    }
   }
 }
 
