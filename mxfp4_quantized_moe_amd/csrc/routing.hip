@@ -511,93 +511,88 @@ __device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_l
 
 // A batch of at most 16 tokens (E <= 64, one router workgroup of 16
 // waves, logits final in `part`).  Wave t takes token t with lane e on
-// expert e: each key's rank among its token's E keys (the keys are
-// distinct) places the k best in order, so no merge network runs on the
-// one or few waves that have a token.  The softmax then follows
-// topk_softmax_terms over those k in rank order.  The grouping is the one
-// permute_block makes, for at most 16 * 8 slots: per-expert counts by
-// wave 0 over the slots' ids in LDS, a wave scan for the offsets, the
-// active-slot records and one prefill tile per active expert (an expert
-// sees at most 16 tokens), then each slot's stable position from the
-// earlier slots of its expert.
-__device__ void finish_small_batch(const RouteArgs& a, const PermuteArgs& pa, const float* part) {
-  __shared__ uint64_t skey[kRouteTokens][64];
-  __shared__ uint64_t stop[kRouteTokens][MAX_TOPK_DEV];
-  __shared__ int sids[kRouteTokens * MAX_TOPK_DEV];
-  __shared__ int soff[64];
-  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
-  const int E = a.E, k = a.top_k, T = a.T, N = T * k;
-  const bool live = t < T && lane < E;
-  const uint64_t key =
-      live ? expert_key(part[4 * t + 256 * (lane >> 4) + 64 * ((lane >> 2) & 3) + (lane & 3)], lane) : 0;
-  skey[t][lane] = key;
-  __syncthreads();
-  if (live) {
-    int rank = 0;
-    for (int e = 0; e < E; ++e) rank += skey[t][e] > key;
-    if (rank < k) stop[t][rank] = key;
-  }
-  __syncthreads();
-  if (t < T && lane < k) {
-    uint64_t l[MAX_TOPK_DEV];
+// expert e and finds the k best keys with the merge network of topk_keys,
+// in registers; the softmax follows topk_softmax_terms over them.  After
+// one barrier, wave 0 makes the grouping permute_block makes, for at most
+// 16 * 8 slots: per-expert counts over the slots' ids in LDS, a wave scan
+// for the offsets, the active-slot records and one prefill tile per active
+// expert (an expert sees at most 16 tokens), then each slot's stable
+// position from the earlier slots of its expert.
+template <int KM>
+__device__ __forceinline__ void small_batch_topk(const RouteArgs& a, const float* part, int t, int lane, int* sids) {
+  const float* pt = part + 4 * t;
+  uint64_t l[KM];
+  topk_keys<KM, 64>(pt, a.E, lane, l);
+  float ex[KM];
+  const float den = topk_softmax_terms<KM>(l, a.top_k, ex);
+  float w = 0.f;
+  int e = 0;
 #pragma unroll
-    for (int j = 0; j < MAX_TOPK_DEV; ++j) l[j] = j < k ? stop[t][j] : 0;
-    float ex[MAX_TOPK_DEV];
-    const float den = topk_softmax_terms<MAX_TOPK_DEV>(l, k, ex);
-    float w = 0.f;
-    int e = 0;
-#pragma unroll
-    for (int j = 0; j < MAX_TOPK_DEV; ++j)
-      if (j == lane) {
-        w = ex[j] / den;
-        e = key_expert(l[j]);
-      }
-    const int o = t * k + lane;
+  for (int j = 0; j < KM; ++j)
+    if (j == lane) {
+      w = ex[j] / den;
+      e = key_expert(l[j]);
+    }
+  if (lane < a.top_k) {
+    const int o = t * a.top_k + lane;
     a.idx[o] = e;
     a.wts[o] = w;
     if (a.idx_out) a.idx_out[o] = e;
     if (a.wts_out) a.wts_out[o] = w;
     sids[o] = e;
   }
-  __syncthreads();
-  if (t == 0) {
-    int c = 0;
-    if (lane < E)
-      for (int s = 0; s < N; ++s) c += sids[s] == lane;
-    int tot;
-    const int off = wave_excl_scan(c, lane, &tot);
-    const uint64_t act = __ballot(c > 0);
-    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    const int arank = __popcll(act & lt), atot = __popcll(act);
-    if (lane < E) {
-      soff[lane] = off;
-      pa.offsets[lane] = off;
-      pa.counts[lane] = c;
-      pa.tile_off[lane] = arank;
-      if (pa.counts_out) pa.counts_out[lane] = c;
-      if (pa.offsets_out) pa.offsets_out[lane] = off;
-      if (c > 0) {
-        pa.active[1 + arank] = make_int4(lane, off, c, atot);
-        pa.tiles[arank] = make_int4(lane, off, c, 0);
-      }
-    }
-    if (lane == 0) {
-      pa.offsets[E] = tot;
-      pa.tile_off[E] = atot;
-      pa.active[0] = make_int4(atot, 0, 0, 0);
-      if (pa.offsets_out) pa.offsets_out[E] = tot;
-    }
-    for (int i = atot + lane; i < min(E, N); i += 64) pa.active[1 + i] = make_int4(0, 0, 0, 0);
+}
+
+__device__ void finish_small_batch(const RouteArgs& a, const PermuteArgs& pa, const float* part) {
+  __shared__ int sids[kRouteTokens * MAX_TOPK_DEV];
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  const int E = a.E, k = a.top_k, T = a.T, N = T * k;
+  if (t < T) {  // uniform per wave
+    if (k <= 4) small_batch_topk<4>(a, part, t, lane, sids);
+    else small_batch_topk<MAX_TOPK_DEV>(a, part, t, lane, sids);
   }
   __syncthreads();
-  for (int s = threadIdx.x; s < N; s += blockDim.x) {
-    const int e = sids[s];
-    int r = 0;
-    for (int s2 = 0; s2 < s; ++s2) r += sids[s2] == e;
-    const int p = soff[e] + r;
-    pa.sorted[p] = s;
-    pa.sorted_tok[p] = s / k;
-    pa.pos[s] = p;
+  if (t != 0) return;  // the rest is wave 0's, with no further barrier
+  int c = 0;
+  if (lane < E)
+    for (int s = 0; s < N; ++s) c += sids[s] == lane;
+  int tot;
+  const int off = wave_excl_scan(c, lane, &tot);
+  const uint64_t act = __ballot(c > 0);
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int arank = __popcll(act & lt), atot = __popcll(act);
+  if (lane < E) {
+    pa.offsets[lane] = off;
+    pa.counts[lane] = c;
+    pa.tile_off[lane] = arank;
+    if (pa.counts_out) pa.counts_out[lane] = c;
+    if (pa.offsets_out) pa.offsets_out[lane] = off;
+    if (c > 0) {
+      pa.active[1 + arank] = make_int4(lane, off, c, atot);
+      pa.tiles[arank] = make_int4(lane, off, c, 0);
+    }
+  }
+  if (lane == 0) {
+    pa.offsets[E] = tot;
+    pa.tile_off[E] = atot;
+    pa.active[0] = make_int4(atot, 0, 0, 0);
+    if (pa.offsets_out) pa.offsets_out[E] = tot;
+  }
+  for (int i = atot + lane; i < min(E, N); i += 64) pa.active[1 + i] = make_int4(0, 0, 0, 0);
+  // stable positions: slot s goes after the earlier slots of its expert,
+  // from that expert's offset (lane e's prefix, taken across lanes)
+  for (int base = 0; base < N; base += 64) {
+    const int s = base + lane;
+    const int e = s < N ? sids[s] : 0;
+    const int o = __shfl(off, e);
+    if (s < N) {
+      int r = 0;
+      for (int s2 = 0; s2 < s; ++s2) r += sids[s2] == e;
+      const int p = o + r;
+      pa.sorted[p] = s;
+      pa.sorted_tok[p] = s / k;
+      pa.pos[s] = p;
+    }
   }
 }
 
