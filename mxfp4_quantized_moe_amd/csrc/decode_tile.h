@@ -10,7 +10,8 @@
 // 4 row tiles' scale bytes of its lane) and its token fragments, and keeps D
 // chunks in flight in a register ring with explicit vmcnt waits.  A pass
 // covers up to 32 tokens.  Partial sums meet in LDS in a fixed wave order,
-// one token sub-tile at a time.
+// one token sub-tile at a time, right after the wave's last chunk (the ring's
+// trailing loads, all past the end, still return meanwhile).
 #pragma once
 
 #include "gemm_common.h"
@@ -28,38 +29,44 @@ struct DecodeStage {
   uint4 bq[NA][BL];
 };
 
-// LDS of one decode tile: the 4 waves' partial sums of one token sub-tile.
-constexpr int kDecodeTileLds = 4 * 4 * 64 * 16;
+// LDS of one decode tile: the 4 waves' partial sums of one token sub-tile,
+// then one 1 KB area per wave that its bias values land in.
+constexpr int kDecodeRedLds = 4 * 4 * 64 * 16;
+constexpr int kDecodeTileLds = kDecodeRedLds + 4 * 1024;
 
 // Tile (expert e, row group q) for the n_e tokens in sorted rows row_start
-// .. row_start + n_e - 1.  red: kDecodeTileLds bytes of LDS.  MAXNA: token
+// .. row_start + n_e - 1.  lds: kDecodeTileLds bytes.  MAXNA: token
 // sub-tiles of 16 per pass (1 or 2); batches of at most 16 tokens (no
 // expert sees more) take 1, which keeps the 32-token pass and its
 // registers out of the kernel.
 template <int ACT, int PHASE, int MAXNA>
-__device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int row_start, int n_e,
-                                            f32x4_t* red_lds) {
+__device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int row_start, int n_e, uint8_t* lds) {
   static_assert(ACT == ACT_BF16 || ACT == ACT_FP8 || ACT == ACT_INT8, "bf16, fp8 or int8 activations");
   static_assert(MAXNA == 1 || MAXNA == 2, "one or two token sub-tiles per pass");
   constexpr bool I8 = ACT == ACT_INT8;  // int8 x int8 -> exact int32 sums, scales in the epilogue
   // [wave][row tile][lane] of one token sub-tile
-  f32x4_t (*red)[4][64] = reinterpret_cast<f32x4_t (*)[4][64]>(red_lds);
+  f32x4_t (*red)[4][64] = reinterpret_cast<f32x4_t (*)[4][64]>(lds);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint8_t* sbias = lds + kDecodeRedLds + wave * 1024;
   const int g = lane >> 4, r16 = lane & 15;
   const WBuf wb = I8 ? byte_weights(a, e) : expert_weights<true>(a, e);
-  const int t0 = 4 * q;  // first row tile of the group
   const int nb = a.nb, nc = wb.nc, K = nb * 32;
   constexpr int EB = ACT == ACT_BF16 ? 2 : 1;  // bytes per B element
   const uint32_t row_bytes = uint32_t(K) * EB;
   const rsrc_t bsrc = act_rows(a, PHASE, row_start, n_e, row_bytes);
+  const int t0 = 4 * q;  // first row tile of the group
   const int nj = (nc - wave + 3) >> 2;  // chunks of this wave (0 when nc <= wave)
   const uint32_t aslot = uint32_t(piece_slot(r16, g)) * 16u;
-  // bias of the 4 output rows this lane stores (row tile t0 + wave, rows
-  // 4g .. 4g+3), fetched before the K loop as raw bf16 bits
-  const int r0 = 16 * (t0 + wave) + 4 * g;
-  const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
-  const uint2 biasq = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, r0 < a.R ? uint32_t(r0) * 2u : kOOB, 0, 0));
+  // The bias of the wave's row tile (rows 16 (t0 + wave) .. +16, raw bf16
+  // bits) goes to LDS by one DMA before any other load, so every later wait
+  // covers it and no register holds it through the K loop.  Lane h < 2
+  // carries rows 8h .. 8h+7.
+  {
+    const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(a.bias) + int64_t(e) * a.R, uint32_t(a.R) * 2u);
+    const int r = 16 * (t0 + wave) + 8 * lane;
+    dma16(br, (lane < 2 && r < a.R) ? uint32_t(r) * 2u : kOOB, sbias);
+  }
 
   // up to 16 * MAXNA tokens per pass over the weights (registers bound
   // the tile)
@@ -187,10 +194,60 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
         }
       };
 
-      // Prologue: the token ids (gate_up) are the oldest loads, then the
-      // weights of chunks 0 .. D-2, whose streaming need not wait for the
-      // ids; the token fragments of those chunks follow once the ids are
-      // in.  Queue: ids, A0 .. A(D-2), B0 .. B(D-2).
+      // The fixed-order sum of the 4 waves' partials, one token sub-tile at
+      // a time; wave w finishes row tile w.  Its bias comes from the wave's
+      // LDS area (landed before the first chunk's wait returned).
+      auto finish = [&]() __attribute__((always_inline)) {
+        const int r0 = 16 * (t0 + wave) + 4 * g;
+        const uint2 biasq = *reinterpret_cast<const uint2*>(sbias + 8 * g);
+#pragma unroll
+        for (int nt = 0; nt < NA; ++nt) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt][nt];
+          __syncthreads();
+          const int j = tg + nt * 16 + r16;
+          if (j < n_e && r0 < a.R) {
+            f32x4_t sum;
+            if constexpr (I8) {
+              // exact int32 sums of the 4 waves -> fp32, times the row's and
+              // the token's scales (the prefill tile's int8 epilogue)
+              typedef int i32x4_t __attribute__((ext_vector_type(4)));
+              i32x4_t is = __builtin_bit_cast(i32x4_t, red[0][wave][lane]);
+              is += __builtin_bit_cast(i32x4_t, red[1][wave][lane]);
+              is += __builtin_bit_cast(i32x4_t, red[2][wave][lane]);
+              is += __builtin_bit_cast(i32x4_t, red[3][wave][lane]);
+              const float4 rs = *reinterpret_cast<const float4*>(a.row_scale + int64_t(e) * a.R + r0);
+              const int p = row_start + j;
+              const float ts = a.tok_scale[PHASE == 0 ? a.sorted_tok[p] : p];
+              sum = f32x4_t{float(is[0]) * rs.x * ts, float(is[1]) * rs.y * ts, float(is[2]) * rs.z * ts,
+                            float(is[3]) * rs.w * ts};
+            } else {
+              sum = red[0][wave][lane];
+              sum += red[1][wave][lane];
+              sum += red[2][wave][lane];
+              sum += red[3][wave][lane];
+            }
+            const float v0 = sum[0] * a.acc_scale + __uint_as_float(biasq.x << 16);
+            const float v1 = sum[1] * a.acc_scale + __uint_as_float(biasq.x & 0xFFFF0000u);
+            const float v2 = sum[2] * a.acc_scale + __uint_as_float(biasq.y << 16);
+            const float v3 = sum[3] * a.acc_scale + __uint_as_float(biasq.y & 0xFFFF0000u);
+            if (PHASE == 1 && a.cmb_out) {
+              // Y rows for the folded combine: read by another workgroup
+              const rsrc_t ys = make_rsrc(a.out, uint32_t(a.n_slots) * uint32_t(a.R) * 2u);
+              buf_store_dev_b64(ys, uint32_t((int64_t(row_start + j) * a.R + r0) * 2),
+                                make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
+            } else {
+              store_rows_biased<ACT, PHASE>(a, r0, row_start + j, v0, v1, v2, v3);
+            }
+          }
+          __syncthreads();
+        }
+      };
+
+      // Prologue: the token ids (gate_up) are the oldest loads after the
+      // bias DMA, then the weights of chunks 0 .. D-2, whose streaming need
+      // not wait for the ids; the token fragments of those chunks follow
+      // once the ids are in.  Queue: bias, ids, A0 .. A(D-2), B0 .. B(D-2).
       order_point();
       issue_a(0, st[0]);
       order_point();
@@ -205,9 +262,9 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
       if constexpr (D > 2) { issue_b(1, st[1]); order_point(); }
       // iteration j: wait for chunk j (D-2 later chunks may stay in flight),
       // issue chunk j + D - 1 into the stage chunk j-1 used, compute chunk
-      // j.  Chunk 0 is complete once only the token fragments of chunks 1 ..
-      // D-2 are outstanding; from chunk 1 on the loads of every chunk were
-      // issued together.
+      // j, and after the last chunk form the outputs.  Chunk 0 is complete
+      // once only the token fragments of chunks 1 .. D-2 are outstanding;
+      // from chunk 1 on the loads of every chunk were issued together.
       auto iteration = [&](int j, auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;  // j % D
         if constexpr (u == 0) {
@@ -219,6 +276,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
         issue(j + D - 1, st[(u + D - 1) % D]);
         order_point();
         compute(st[u]);
+        if (j == nj - 1) finish();
       };
       int j0 = 0;
       for (; j0 + D <= nj; j0 += D) {
@@ -246,56 +304,9 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int e, int q, int
         }
         static_cast<uint32_t*>(a.out)[0] = x;
       }
-
-      // fixed-order sum of the 4 waves' partials, one token sub-tile at a
-      // time; wave w finishes row tile w.  The bias is unpacked only here
-      // (hoisted to the top, its unpacking would wait for its load before
-      // the first weight load went out).
-      uint32_t bx = biasq.x, by = biasq.y;
-      hold(bx);
-      hold(by);
-#pragma unroll
-      for (int nt = 0; nt < NA; ++nt) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt][nt];
-        __syncthreads();
-        const int j = tg + nt * 16 + r16;
-        if (j < n_e && r0 < a.R) {
-          f32x4_t sum;
-          if constexpr (I8) {
-            // exact int32 sums of the 4 waves -> fp32, times the row's and
-            // the token's scales (the prefill tile's int8 epilogue)
-            typedef int i32x4_t __attribute__((ext_vector_type(4)));
-            i32x4_t is = __builtin_bit_cast(i32x4_t, red[0][wave][lane]);
-            is += __builtin_bit_cast(i32x4_t, red[1][wave][lane]);
-            is += __builtin_bit_cast(i32x4_t, red[2][wave][lane]);
-            is += __builtin_bit_cast(i32x4_t, red[3][wave][lane]);
-            const float4 rs = *reinterpret_cast<const float4*>(a.row_scale + int64_t(e) * a.R + r0);
-            const int p = row_start + j;
-            const float ts = a.tok_scale[PHASE == 0 ? a.sorted_tok[p] : p];
-            sum = f32x4_t{float(is[0]) * rs.x * ts, float(is[1]) * rs.y * ts, float(is[2]) * rs.z * ts,
-                          float(is[3]) * rs.w * ts};
-          } else {
-            sum = red[0][wave][lane];
-            sum += red[1][wave][lane];
-            sum += red[2][wave][lane];
-            sum += red[3][wave][lane];
-          }
-          const float v0 = sum[0] * a.acc_scale + __uint_as_float(bx << 16);
-          const float v1 = sum[1] * a.acc_scale + __uint_as_float(bx & 0xFFFF0000u);
-          const float v2 = sum[2] * a.acc_scale + __uint_as_float(by << 16);
-          const float v3 = sum[3] * a.acc_scale + __uint_as_float(by & 0xFFFF0000u);
-          if (PHASE == 1 && a.cmb_out) {
-            // Y rows for the folded combine: read by another workgroup
-            const rsrc_t ys = make_rsrc(a.out, uint32_t(a.n_slots) * uint32_t(a.R) * 2u);
-            buf_store_dev_b64(ys, uint32_t((int64_t(row_start + j) * a.R + r0) * 2),
-                              make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
-          } else {
-            store_rows_biased<ACT, PHASE>(a, r0, row_start + j, v0, v1, v2, v3);
-          }
-        }
-        __syncthreads();
-      }
+      // a wave with no chunks (K of at most 3 chunks) still takes its part
+      // in the sum (its partials are zero)
+      if (nj == 0) finish();
     };
     if (MAXNA == 1 || nt_active == 1)
       pass(IC<1>{});

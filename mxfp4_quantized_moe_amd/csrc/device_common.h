@@ -144,6 +144,15 @@ __device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t voff, uint32
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+// Buffer-to-LDS form of a 16-byte load: lane i's 16 bytes land at lds_dst +
+// 16 i (1 KB per wave), with no registers held while it is in flight; it
+// counts in vmcnt like any other load.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, const uint8_t* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_dst), 16, off, 0, 0, 0);
+}
+
 // ------------------------------------------- device-scope hand-off
 //
 // Rows that one workgroup hands to another workgroup of the same launch

@@ -251,11 +251,6 @@ constexpr int kPrefillRT = kPrefillRows / 128;      // row tiles of 16 per row g
 constexpr int kPrefillStages = MXMOE_PREFILL_STAGES;
 constexpr int kPrefillThreads = 512;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, const uint8_t* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_dst), 16, off, 0, 0, 0);
-}
 
 template <int ACT, int PHASE, bool TILED>
 __global__ __launch_bounds__(kPrefillThreads) void gemm_prefill_kernel(GemmArgs a) {
@@ -1090,8 +1085,8 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_tiled_kernel(GemmArgs a) {
   const int4 rec = a.active[1 + slot];
   hold_uniform(rec);
   if (rec.z == 0) return;
-  __shared__ f32x4_t red[kDecodeTileLds / 16];
-  decode_tile<ACT, PHASE, MAXNA>(a, rec.x, blockIdx.x, rec.y, rec.z, red);
+  __shared__ __align__(16) uint8_t lds[kDecodeTileLds];
+  decode_tile<ACT, PHASE, MAXNA>(a, rec.x, blockIdx.x, rec.y, rec.z, lds);
   if (PHASE == 1 && a.cmb_out) {
     __shared__ int last;
     wait_vmcnt<0>();  // this wave's Y stores have reached the point of coherence
