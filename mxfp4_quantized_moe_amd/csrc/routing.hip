@@ -514,10 +514,10 @@ __device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_l
 // expert e and finds the k best keys with the merge network of topk_keys,
 // in registers; the softmax follows topk_softmax_terms over them.  After
 // one barrier, wave 0 makes the grouping permute_block makes, for at most
-// 16 * 8 slots: per-expert counts over the slots' ids in LDS, a wave scan
-// for the offsets, the active-slot records and one prefill tile per active
-// expert (an expert sees at most 16 tokens), then each slot's stable
-// position from the earlier slots of its expert.
+// 16 * 8 slots: per-expert counts of the slots' ids (LDS atomics), a wave
+// scan for the offsets, the active-slot records and one prefill tile per
+// active expert (an expert sees at most 16 tokens), then each slot's
+// stable position from ballots over the ids.
 template <int KM>
 __device__ __forceinline__ void small_batch_topk(const RouteArgs& a, const float* part, int t, int lane, int* sids) {
   const float* pt = part + 4 * t;
@@ -545,17 +545,20 @@ __device__ __forceinline__ void small_batch_topk(const RouteArgs& a, const float
 
 __device__ void finish_small_batch(const RouteArgs& a, const PermuteArgs& pa, const float* part) {
   __shared__ int sids[kRouteTokens * MAX_TOPK_DEV];
+  __shared__ int cnt[64];
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   const int E = a.E, k = a.top_k, T = a.T, N = T * k;
+  if (t == 0) cnt[lane] = 0;
   if (t < T) {  // uniform per wave
     if (k <= 4) small_batch_topk<4>(a, part, t, lane, sids);
     else small_batch_topk<MAX_TOPK_DEV>(a, part, t, lane, sids);
   }
   __syncthreads();
   if (t != 0) return;  // the rest is wave 0's, with no further barrier
-  int c = 0;
-  if (lane < E)
-    for (int s = 0; s < N; ++s) c += sids[s] == lane;
+  // per-expert counts (integer LDS atomics, order free; this wave's LDS
+  // operations complete in program order)
+  for (int s = lane; s < N; s += 64) atomicAdd(&cnt[sids[s]], 1);
+  const int c = lane < E ? cnt[lane] : 0;
   int tot;
   const int off = wave_excl_scan(c, lane, &tot);
   const uint64_t act = __ballot(c > 0);
@@ -579,19 +582,30 @@ __device__ void finish_small_batch(const RouteArgs& a, const PermuteArgs& pa, co
     if (pa.offsets_out) pa.offsets_out[E] = tot;
   }
   for (int i = atot + lane; i < min(E, N); i += 64) pa.active[1 + i] = make_int4(0, 0, 0, 0);
-  // stable positions: slot s goes after the earlier slots of its expert,
-  // from that expert's offset (lane e's prefix, taken across lanes)
+  // stable positions, 64 slots at a time in slot order: a slot's rank
+  // among the lanes holding the same expert (six ballots over the id bits,
+  // E <= 64) plus the slots of that expert placed before, from its offset
+  if (lane < E) cnt[lane] = 0;  // slots of each expert placed so far
   for (int base = 0; base < N; base += 64) {
     const int s = base + lane;
-    const int e = s < N ? sids[s] : 0;
+    const bool valid = s < N;
+    const int e = valid ? sids[s] : 0;
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+      const uint64_t bm = __ballot((e >> b) & 1);
+      m &= ((e >> b) & 1) ? bm : ~bm;
+    }
+    const int r = __popcll(m & lt);
     const int o = __shfl(off, e);
-    if (s < N) {
-      int r = 0;
-      for (int s2 = 0; s2 < s; ++s2) r += sids[s2] == e;
-      const int p = o + r;
+    const int before = cnt[e];
+    if (valid) {
+      const int p = o + before + r;
       pa.sorted[p] = s;
       pa.sorted_tok[p] = s / k;
       pa.pos[s] = p;
+      // the highest of the expert's lanes moves its count on
+      if ((m >> lane) == 1ull) cnt[e] = before + __popcll(m);
     }
   }
 }

@@ -291,6 +291,32 @@ def test_decode_two_subtile_passes(dev, fp8):
     check_layer(case, res, **kw)
 
 
+@pytest.mark.parametrize("seed, E, k, T, fp8, bias", [
+    (122, 16, 8, 16, False, 0.01),   # 128 slots: positions ranked over two 64-slot rounds
+    (126, 8, 8, 16, False, 3.0),     # every expert in every token: each expert's slots span both rounds
+    (127, 64, 8, 16, False, 3.0),    # E = 64: all six id bits of the ballot ranking
+    (124, 32, 4, 16, True, 0.01),    # FP8: the x codes written by the one router workgroup
+    (120, 32, 4, 17, False, 0.01),   # one token past the one-workgroup batch: router + grouping launches
+])
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_small_batch_grouping(dev, seed, E, k, T, fp8, bias, layout):
+    """Batches of at most 16 tokens (E <= 64) are routed and grouped by the
+    router's one workgroup: per-expert counts by LDS atomics and stable
+    positions from ballots over the expert ids, 64 slots per round.
+    Routing, grouping and the layer against the oracle, up to 128 slots and
+    one token past that batch size."""
+    case = W.small_case(seed, E, 128, 96, k, T, act_dtype="bf16", fp8=fp8, router_bias_std=bias)
+    kw = {}
+    if fp8:
+        s_x, s_h = O.calibrate_fp8(case.layer, case.x_calib, "bf16")
+        kw = dict(x_scale=s_x, h_scale=s_h)
+    note(f"{case.name} {layout} {'fp8' if fp8 else 'bf16'}")
+    res, _, _ = run_gpu(case, dev, layout=layout, want_route=not fp8, **kw)
+    if not fp8:
+        check_perm(case, res["route"])
+    check_layer(case, res, **kw)
+
+
 def test_empty_batch_is_noop(dev):
     import torch
     import mxfp4_quantized_moe_amd as mx
