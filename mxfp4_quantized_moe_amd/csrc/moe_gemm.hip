@@ -1066,11 +1066,10 @@ __device__ void combine_group(const GemmArgs& a, int q) {
 // signals its row group once its Y rows are stored; the last of the
 // group's rec.w workgroups forms the output rows.
 // Batches up to this many tokens run the decode tile with one 16-token
-// sub-tile per pass (157 registers instead of 185 for bf16 tokens: three
-// workgroups per CU instead of two); an expert with more than 16 tokens
-// then takes one pass over its weights per 16 (sweep knob; 64 measured 8%
-// faster than 16 on the 20b T = 64 batch, whose experts see 8 tokens on
-// average).
+// sub-tile per pass (150 registers instead of 166 for bf16 tokens); an
+// expert with more than 16 tokens then takes one pass over its weights per
+// 16 (sweep knob; 64 measured 8% faster than 16 on the 20b T = 64 batch,
+// whose experts see 8 tokens on average).
 #ifndef MXMOE_DECODE_ONE_SUBTILE
 #define MXMOE_DECODE_ONE_SUBTILE 64
 #endif
