@@ -48,9 +48,12 @@ PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp8_TFLOPs": 5000.0, "int8_T
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EV_EVERY = 4  # timed steps between two recordings of the dominant stage's events
 GRAPH_STEPS = 20  # forwards captured per HIP graph in the graph launch mode
+# the GEMM and codec kernels and what decides their work items (the grouping
+# writes the token tiles and item records the GEMMs read)
 KERNEL_SOURCES = ["mxfp4_quantized_moe_amd/csrc/moe_gemm.hip", "mxfp4_quantized_moe_amd/csrc/codec.hip",
                   "mxfp4_quantized_moe_amd/csrc/device_common.h", "mxfp4_quantized_moe_amd/csrc/gemm_common.h",
-                  "mxfp4_quantized_moe_amd/csrc/decode_tile.h"]
+                  "mxfp4_quantized_moe_amd/csrc/decode_tile.h", "mxfp4_quantized_moe_amd/csrc/routing.hip",
+                  "mxfp4_quantized_moe_amd/csrc/xcd_split.h", "mxfp4_quantized_moe_amd/csrc/launch.h"]
 
 
 def kernel_source_hash() -> str:

@@ -358,8 +358,10 @@ __device__ void permute_block(const PermuteArgs& a) {
   for (int e = tid; e < E; e += kPermThreads) {
     const int c = cnt[e];
     const int t0 = toff[e];
-    for (int j = 0; j * kPrefillTokens < c; ++j)
-      a.tiles[t0 + j] = make_int4(e, off[e] + j * kPrefillTokens, min(kPrefillTokens, c - j * kPrefillTokens), 0);
+    for (int j = 0; j * kPrefillTokens < c; ++j) {
+      const int2 tt = token_tile(c, j);
+      a.tiles[t0 + j] = make_int4(e, off[e] + tt.x, tt.y, 0);
+    }
   }
   write_item_records(a, cnt, 0, E, true);
 
@@ -495,8 +497,8 @@ __device__ void write_item_records(const PermuteArgs& a, const int* cnt, int e_l
       const int st = local / nt, q = local - st * nt;
       int x = 0;
       while (x < 7 && item >= bxp[x + 1]) ++x;
-      rec[8 * (item - bxp[x]) + x] =
-          make_int4(lo, s_cp[lo] + q * kPrefillTokens, min(kPrefillTokens, cnt[lo] - q * kPrefillTokens), st);
+      const int2 tt = token_tile(cnt[lo], q);
+      rec[8 * (item - bxp[x]) + x] = make_int4(lo, s_cp[lo] + tt.x, tt.y, st);
     }
     // list counters of a persistent launch: past the first item of each of
     // its workgroups
@@ -730,8 +732,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_by_expert_kernel(Permute
     if (a.offsets_out) a.offsets_out[me] = off_me;
     if (c_me > 0) a.active[1 + s_act] = make_int4(me, off_me, c_me, s_atot);
   }
-  for (int j = tid; j * kPrefillTokens < c_me; j += kPermThreads)
-    a.tiles[toff_me + j] = make_int4(me, off_me + j * kPrefillTokens, min(kPrefillTokens, c_me - j * kPrefillTokens), 0);
+  for (int j = tid; j * kPrefillTokens < c_me; j += kPermThreads) {
+    const int2 tt = token_tile(c_me, j);
+    a.tiles[toff_me + j] = make_int4(me, off_me + tt.x, tt.y, 0);
+  }
 
   write_item_records(a, cnt, me, me + 1, me == 0);
 
@@ -880,7 +884,10 @@ __global__ __launch_bounds__(256) void linear_setup_kernel(int T, int32_t* offse
     tile_off[0] = 0;
     tile_off[1] = ntiles;
   }
-  if (i < ntiles) tiles[i] = make_int4(0, i * kPrefillTokens, min(kPrefillTokens, T - i * kPrefillTokens), 0);
+  if (i < ntiles) {
+    const int2 tt = token_tile(T, i);
+    tiles[i] = make_int4(0, tt.x, tt.y, 0);
+  }
   if (zero_bias && i < N) {
     if (zero_bias_bytes == 2)
       static_cast<uint16_t*>(zero_bias)[i] = 0;
@@ -927,7 +934,8 @@ __global__ __launch_bounds__(256) void dense_group_kernel(DenseGroupArgs a) {
   }
   if (i < int64_t(E) * ntiles) {
     const int e = int(i / ntiles), q = int(i % ntiles);
-    a.tiles[i] = make_int4(e, e * T + q * kPrefillTokens, min(kPrefillTokens, T - q * kPrefillTokens), 0);
+    const int2 tt = token_tile(T, q);
+    a.tiles[i] = make_int4(e, e * T + tt.x, tt.y, 0);
   }
 }
 

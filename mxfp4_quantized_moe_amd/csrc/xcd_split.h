@@ -19,6 +19,20 @@
 
 namespace mxmoe {
 
+// Token tile q of a group of c sorted rows (an expert's tokens): {first
+// row within the group, rows}.  The group's ceil(c / kPrefillTokens) tiles
+// share its ceil(c / 16) sub-tiles of 16 rows as evenly as they go (the
+// first tiles one sub-tile more), so the tiles of one expert take about
+// equally long and stream each weight stripe side by side, where a full
+// tile followed by a short remainder would drift apart.
+__host__ __device__ __forceinline__ int2 token_tile(int c, int q) {
+  const int nt = (c + kPrefillTokens - 1) / kPrefillTokens, ns = (c + 15) >> 4;
+  const int base = ns / nt, extra = ns - base * nt;  // at most 8 sub-tiles per tile
+  const int first = 16 * (q * base + (q < extra ? q : extra));
+  const int rows = 16 * (base + (q < extra ? 1 : 0));
+  return make_int2(first, rows < c - first ? rows : c - first);
+}
+
 // Per-stripe cost of an expert with cnt tokens: kTileCost per token tile
 // plus ceil(cnt / 16) sub-tiles (its tiles are full but the last).
 __device__ __forceinline__ int expert_stripe_cost(int cnt) {

@@ -40,7 +40,7 @@ def as_f64(a, act):
     (1, 1, 64, 32, "bf16", True),       # one token: decode-shaped kernel
     (2, 7, 96, 64, "bf16", False),      # K/32 = 3: a partial 128-K chunk, no bias
     (3, 40, 2880, 544, "bf16", True),   # > 16 tokens: prefill tiles, N = 2 stripes + a ragged third
-    (4, 300, 160, 96, "bf16", True),    # ragged token tiles (128, 128, 44)
+    (4, 300, 160, 96, "bf16", True),    # ragged token tiles (112, 96 and 92 rows)
     (5, 13, 128, 96, "f32", True),      # fp32 activations
     (6, 130, 64, 64, "f32", False),     # fp32, more than 64 tokens (token groups)
 ])
