@@ -34,7 +34,7 @@ __host__ __device__ __forceinline__ int2 token_tile(int c, int q) {
 }
 
 // Per-stripe cost of an expert with cnt tokens: kTileCost per token tile
-// plus ceil(cnt / 16) sub-tiles (its tiles are full but the last).
+// plus its ceil(cnt / 16) sub-tiles.
 __device__ __forceinline__ int expert_stripe_cost(int cnt) {
   return kTileCost * ((cnt + kPrefillTokens - 1) / kPrefillTokens) + ((cnt + 15) >> 4);
 }
@@ -48,7 +48,9 @@ __device__ __forceinline__ void xcd_bounds(const int* woff, const int* toff, int
   // Lane xx <= 8 finds the first item of XCD xx: the first whose work
   // prefix reaches xx/8 of the total.  The prefix of item (expert j,
   // stripe s, tile q) is woff[j] * nstripes + s * (woff[j+1] - woff[j])
-  // + q * (kTileCost + 8): tiles before an expert's last are full.
+  // + P(q), P the cost of the expert's tiles before q: its first `extra`
+  // tiles cost kTileCost + base + 1, the others kTileCost + base
+  // (token_tile's even split of its sub-tiles).
   int bnd = nvalid;
   const int64_t W = int64_t(woff[E]) * nstripes;
   const int64_t target = (W * lane + 7) / 8;
@@ -66,9 +68,13 @@ __device__ __forceinline__ void xcd_bounds(const int* woff, const int* toff, int
     const int64_t rem = target - int64_t(woff[lo]) * nstripes;
     const int st = int(rem / gc);
     const int r2 = int(rem - int64_t(st) * gc);
-    // past the last tile's start, the next stripe's (or expert's) first
-    // item follows: index st * nt + nt
-    const int q = min((r2 + kTileCost + 7) / (kTileCost + 8), nt);
+    // the first tile q with P(q) >= r2; past the last tile's start, the
+    // next stripe's (or expert's) first item follows: index st * nt + nt
+    const int nsub = gc - kTileCost * nt, base = nsub / nt, extra = nsub - base * nt;
+    const int big = kTileCost + base + 1;  // cost of each of the first `extra` tiles
+    const int q = min(r2 <= extra * big ? (r2 + big - 1) / big
+                                        : extra + (r2 - extra * big + big - 2) / (big - 1),
+                      nt);
     bnd = toff[lo] * nstripes + st * nt + q;
   }
   // No XCD may own more than G items: clamp forward, then backward from

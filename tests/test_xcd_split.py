@@ -5,6 +5,8 @@ The kernel (gemm_prefill_tiled_kernel) orders items (expert, row stripe,
 token tile), gives XCD x a contiguous range whose estimated work (a fixed
 cost per item plus its active 16-token sub-tiles) is about an eighth of the
 total, and clamps every range to the G workgroups the grid holds per XCD.
+An expert's token tiles share its 16-token sub-tiles evenly (the first
+ones one more).
 This file restates that integer arithmetic and checks what the kernel's
 correctness rests on: the ranges partition the items exactly, none exceeds
 G, every lookup stays inside the tile table, and on skewed routings the
@@ -20,6 +22,14 @@ TILE_COST = 4     # the kernel's fixed cost per item, in 16-token sub-tiles
 
 def cdiv(a, b):
     return -(-a // b)
+
+
+def token_tile(c, q):
+    """(first row, rows) of token tile q of an expert with c tokens."""
+    nt, nsub = cdiv(c, TOKENS), cdiv(c, 16)
+    base, extra = divmod(nsub, nt)
+    first = 16 * (q * base + min(q, extra))
+    return first, min(16 * (base + (1 if q < extra else 0)), c - first)
 
 
 def weighted_bounds(cnt, R, c0):
@@ -47,11 +57,26 @@ def weighted_bounds(cnt, R, c0):
             rem = target - int(woff[j]) * ns
             st, r2 = rem // gc, rem % gc
             assert 0 <= st < ns
-            b = int(toff[j]) * ns + st * nt + min((r2 + c0 + 7) // (c0 + 8), nt)
+            b = int(toff[j]) * ns + st * nt + first_tile_at(r2, gc, nt, c0)
         else:
             b = nvalid
         bnd.append(b)
     return bnd, G, nvalid, ns, toff
+
+
+def first_tile_at(r2, gc, nt, c0):
+    """First token tile q of an expert whose cost prefix reaches r2 (nt if
+    none): the expert's gc - c0 * nt sub-tiles are split evenly over its nt
+    tiles, the first `extra` taking one more."""
+    nsub = gc - c0 * nt
+    base, extra = divmod(nsub, nt)
+    costs = [c0 + base + (1 if q < extra else 0) for q in range(nt)]
+    p = 0
+    for q in range(nt):
+        if p >= r2:
+            return q
+        p += costs[q]
+    return nt
 
 
 def upper(arr, v, E, ns):
@@ -89,7 +114,7 @@ def split(cnt, R, c0):
             local = item - int(toff[j]) * ns
             stripe, tile = local // nt, int(toff[j]) + local % nt
             assert 0 <= stripe < ns and toff[j] <= tile < toff[j + 1]
-            ntok = min(TOKENS, cnt[j] - TOKENS * (tile - int(toff[j])))
+            ntok = token_tile(cnt[j], tile - int(toff[j]))[1]
             assert ntok > 0
             seen[item] += 1
             work[x] += c0 + cdiv(ntok, 16)
@@ -117,6 +142,19 @@ def test_ranges_partition_the_items(seed):
             p = rng.dirichlet(np.full(E, 5.0))
         cnt = rng.multinomial(T * k, p).tolist()
         split(cnt, int(rng.choice([64, 96, 300, 2880, 5760])), int(rng.choice([0, 2, 4])))
+
+
+def test_token_tiles_split_evenly():
+    """An expert's tiles cover its rows in order, hold at most 128 rows,
+    and differ by at most one 16-row sub-tile (the last may be ragged)."""
+    for c in range(1, 3000):
+        nt = cdiv(c, TOKENS)
+        tiles = [token_tile(c, q) for q in range(nt)]
+        assert tiles[0][0] == 0 and sum(r for _, r in tiles) == c
+        assert all(tiles[q][0] + tiles[q][1] == tiles[q + 1][0] for q in range(nt - 1))
+        assert all(0 < r <= TOKENS for _, r in tiles)
+        subs = [cdiv(r, 16) for _, r in tiles]
+        assert sum(subs) == cdiv(c, 16) and max(subs) - min(subs) <= 1
 
 
 def test_single_token_and_empty_experts():
